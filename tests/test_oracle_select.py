@@ -1,0 +1,211 @@
+"""Pins for the oracle's pooling, scoring, budget rule and top-k selection.
+
+Each check ties the oracle to something other than itself: a hand-worked table,
+an algebraic identity, a brute-force search over subsets, or a planted signal
+whose selection is forced by margin.
+"""
+
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from head_heterogeneous_block_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- pooling
+
+
+def test_pool_identical_rows_and_short_tail():
+    rng = np.random.default_rng(0)
+    row = rng.standard_normal(8)
+    x = np.tile(row, (10, 1))  # 10 identical rows, block 4 -> blocks of 4, 4, 2
+    p = O.pool_blocks(x, 4)
+    assert p.shape == (3, 8)
+    np.testing.assert_allclose(p, np.tile(row, (3, 1)), rtol=0, atol=1e-15)
+    y = rng.standard_normal((10, 8))
+    p = O.pool_blocks(y, 4)
+    np.testing.assert_allclose(p[2], np.mean(y[8:10], axis=0), rtol=1e-15)
+    np.testing.assert_allclose(O.pool_blocks(y, 10)[0], np.mean(y, axis=0), rtol=1e-15)
+    np.testing.assert_array_equal(O.pool_blocks(y, 1), y)
+
+
+def test_pool_linear_and_shift():
+    rng = np.random.default_rng(1)
+    x, y = rng.standard_normal((2, 3, 64, 16))
+    a, b = 1.7, -0.3
+    np.testing.assert_allclose(O.pool_blocks(a * x + b * y, 16),
+                               a * O.pool_blocks(x, 16) + b * O.pool_blocks(y, 16), atol=1e-13)
+    c = rng.standard_normal(16)
+    np.testing.assert_allclose(O.pool_blocks(x + c, 16), O.pool_blocks(x, 16) + c, atol=1e-13)
+
+
+def test_bf16_widening_exact():
+    vals = np.array([1.0, -2.5, 3.140625, 0.0, -0.0, 65280.0], dtype=np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    np.testing.assert_array_equal(O.to_f64(bits), vals.astype(np.float64))
+    t = torch.tensor([0.1, -7.3, 1e-3], dtype=torch.float32).to(torch.bfloat16)
+    np.testing.assert_array_equal(O.to_f64(W.to_numpy(t)), t.float().double().numpy())
+
+
+# ---------------------------------------------------------------- scores
+
+
+def test_block_scores_equal_block_mean_of_dense_logits():
+    """<mean q, mean k> = mean over the block pair of <q_i, k_j> (bilinearity):
+    the pooled score is the block average of the dense logit matrix."""
+    rng = np.random.default_rng(2)
+    b, hq, hkv, S, D, B = 1, 4, 2, 96, 8, 32
+    q = rng.standard_normal((b, hq, S, D)).astype(np.float32)
+    k = rng.standard_normal((b, hkv, S, D)).astype(np.float32)
+    s = O.prefill_block_scores(q, k, B)
+    nb = S // B
+    for h in range(hq):
+        dense = (q[0, h].astype(np.float64) @ k[0, h // 2].astype(np.float64).T) / math.sqrt(D)
+        for m in range(nb):
+            for n in range(nb):
+                ref = dense[m * B:(m + 1) * B, n * B:(n + 1) * B].mean()
+                if n <= m:
+                    assert abs(s[0, h, m, n] - ref) < 1e-12
+                else:
+                    assert s[0, h, m, n] == -np.inf
+
+
+# ---------------------------------------------------------------- budget rule
+
+
+def test_budget_rule_golden_table():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "budget_rule.txt")) if l.strip() and l[0] != "#"]
+    assert len(rows) >= 10
+    for n, mb, r, want in ([int(x) for x in row] for row in rows):
+        assert O.budget_blocks(n, mb, r) == want, (n, mb, r)
+
+
+def test_budget_rule_exact_rational_ceiling():
+    rng = np.random.default_rng(3)
+    for _ in range(2000):
+        n = int(rng.integers(1, 5000))
+        r = int(rng.integers(0, 65537))
+        mb = int(rng.integers(0, 40))
+        c = math.ceil(Fraction(r * n, 65536))
+        assert O.budget_blocks(n, mb, r) == min(n, max(mb, c))
+
+
+# ---------------------------------------------------------------- top-k
+
+
+def _max_sum_selection(scores, k, F):
+    """Brute force: among all subsets of the non-forced blocks of size k-|F|,
+    the one with the largest score sum (unique when scores are distinct)."""
+    rest = [i for i in range(len(scores)) if i not in F]
+    best, arg = None, None
+    for comb in itertools.combinations(rest, k - len(F)):
+        v = sum(scores[i] for i in comb)
+        if best is None or v > best:
+            best, arg = v, comb
+    return sorted(list(F) + list(arg))
+
+
+def test_select_row_matches_subset_brute_force():
+    rng = np.random.default_rng(4)
+    for _ in range(300):
+        n = int(rng.integers(1, 11))
+        ns, nl = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        F = O.forced_blocks(n, ns, nl)
+        k = int(rng.integers(len(F), n + 1))
+        s = rng.standard_normal(n)
+        got = O.select_row(s, k, ns, nl)
+        assert got == _max_sum_selection(s, k, F)
+        assert got == sorted(set(got)) and len(got) == k and set(F) <= set(got)
+
+
+def test_select_row_ties_lowest_index_and_signed_zero():
+    assert O.select_row([0.0] * 10, 5, 1, 1) == [0, 1, 2, 3, 9]
+    assert O.select_row([0.5, -0.0, 0.0, 0.0, -1.0, 2.0], 4, 1, 0) == [0, 1, 2, 5]
+    assert O.select_row([3.0, 1.0, 1.0, 2.0, 1.0], 3, 0, 0) == [0, 1, 3]
+
+
+def test_select_row_edge_budgets():
+    s = np.arange(12.0)
+    assert O.select_row(s, 2, 1, 1) == [0, 11]  # k == |F|
+    assert O.select_row(s, 12, 1, 1) == list(range(12))  # k == n
+    assert O.select_row([1.0], 1, 1, 1) == [0]  # row 0: sink == diagonal
+    with pytest.raises(ValueError):
+        O.select_row(s, 1, 1, 1)
+
+
+def test_amplified_plants_are_selected():
+    """With a strong planted direction every causal hot block outranks the noise,
+    so a budget that has room for them must keep all of them."""
+    spec = W.CONFIGS[0].with_(hot_k=8.0, hot_q=1.0, counts=(6, 6, 6, 6))
+    inp = W.make_prefill(spec, 7)
+    q, k = W.to_numpy(inp.q), W.to_numpy(inp.k)
+    idx, cnt = O.select_blocks_prefill(q, k, inp.budget, spec.block)
+    checked = 0
+    for h in range(spec.n_q_heads):
+        for m in range(spec.n_blocks):
+            hot = [int(n) for n in inp.hot[0, h] if n < m]
+            if cnt[0, h, m] >= 2 + len(hot) and hot:
+                assert set(hot) <= set(idx[0, h, m, : cnt[0, h, m]].tolist()), (h, m)
+                checked += 1
+    assert checked > 20
+
+
+def test_select_prefill_invariants_and_counts():
+    spec = W.CONFIGS[1].with_(seq_len=4096)
+    inp = W.make_prefill(spec, 11)
+    q, k = W.to_numpy(inp.q), W.to_numpy(inp.k)
+    idx, cnt = O.select_blocks_prefill(q, k, inp.budget, spec.block)
+    nb = spec.n_blocks
+    for h in range(spec.n_q_heads):
+        for m in range(nb):
+            c = int(cnt[0, h, m])
+            assert c == O.budget_blocks(m + 1, inp.budget["min_blocks"][h], inp.budget["ratio_q16"][h])
+            row = idx[0, h, m]
+            sel = row[:c]
+            assert np.all(np.diff(sel) > 0) and sel[0] == 0 and sel[-1] == m
+            assert np.all(row[c:] == -1)
+
+
+def test_config0_loads_from_selection():
+    spec = W.CONFIGS[0]
+    inp = W.make_prefill(spec, W.default_seed(0))
+    idx, cnt = O.select_blocks_prefill(W.to_numpy(inp.q), W.to_numpy(inp.k), inp.budget, spec.block)
+    assert cnt.reshape(4, -1).sum(1).tolist() == [31, 58, 81, 100]
+    # algorithmic flops: 4*D per visible pair, diagonal blocks half (+B/2)
+    assert O.attended_flops_prefill(idx, cnt, 1024, 64, 64) == 250_085_376
+
+
+# ---------------------------------------------------------------- decode select
+
+
+def test_decode_streaming_heads_fixed_and_retrieval_plants():
+    spec = W.CONFIGS[4].with_(batch=2, kv_len=8192, n_streaming=3, tok_lo=256, tok_hi=1024,
+                              stream_local=16, hot_k=6.0, hot_q=8.0)
+    inp = W.make_decode(spec, 5)
+    q, k = W.to_numpy(inp.q), W.to_numpy(inp.k)
+    idx, cnt = O.decode_select(q, k, inp.budget)
+    bud = inp.budget
+    for bi in range(spec.batch):
+        for h in range(spec.n_q_heads):
+            g = int(bud["granularity"][h])
+            nc = spec.kv_len // g
+            sel = idx[bi, h, : cnt[bi, h]].tolist()
+            if bud["streaming"][h]:
+                assert sel == list(range(4)) + list(range(nc - 16, nc))
+            else:
+                assert len(sel) == bud["min_blocks"][h]
+                assert sel[0] == 0 and sel[-1] == nc - 1
+                hot = set(inp.hot[bi, h].tolist())
+                picked = set(sel) - {0, nc - 1}
+                if len(picked) >= len(hot):
+                    assert hot <= picked
+                else:  # room for fewer than the planted blocks: all picks are planted
+                    assert picked <= hot
