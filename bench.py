@@ -1,0 +1,306 @@
+"""Benchmark: 128K block-sparse prefill layer + 128K batched decode step on one MI355X.
+
+One step = the whole hot path once:
+  prefill (Llama-3.1-8B-shaped layer, 32 query / 8 KV heads, head_dim 128,
+  131072 tokens, block 128, per-head budgets with mean 6.25%):
+    pool Q and K -> block scores -> per-head top-k (sa_select_blocks)
+    -> LPT-ordered persistent block-sparse flash attention (sa_sparse_attn_prefill)
+  decode (16 sequences x 131072-token KV cache, 12 streaming + 20 retrieval heads):
+    scores against the cached pooled keys -> top-k (sa_select_blocks)
+    -> union-of-group split-KV attention + combine (sa_sparse_attn_decode)
+The greedy longest-load-first schedule depends only on the budgets, so it is
+computed once on the host before timing (it is offline in the method), as is
+the pooled-key cache of the decode KV cache.
+
+Prints one JSON line.  `value` is the prefill milliseconds per layer (the
+headline of the metric); attended TFLOP/s, decode GB/s and their roofline
+fractions are reported beside it.  `roofline` covers the dominant kernel (the
+prefill attention), timed with HIP events on the stream it runs on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill-config", type=int, default=2)
+    ap.add_argument("--decode-config", type=int, default=4)
+    ap.add_argument("--variant", type=int, default=0, help="prefill kernel_variant (0 default, 2, 4)")
+    ap.add_argument("--bins-per-cu", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
+    return ap.parse_args()
+
+
+def timed(fn, stream, reps):
+    """Median / mean milliseconds of fn() with events on `stream`."""
+    import torch
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b))
+    ts.sort()
+    return ts[len(ts) // 2], sum(ts) / len(ts), ts
+
+
+def traffic_from_profiles(kernel_src: str):
+    """HBM bytes per launch of the prefill attention kernel from the committed
+    rocprofv3 counter summary, or None if absent or taken on other kernel code."""
+    path = os.path.join(ROOT, "profiles", "prefill_attention_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != h:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline_prefill(inp, block_idx, block_cnt, budget_head0):
+    """The fp64 oracle on a bounded sample of the prefill workload, scaled to ms
+    per layer: selection for one query head (every row), attention for 32 tiles
+    of that head; selection scaled by the head count, attention by attended pairs."""
+    import numpy as np
+    import oracle as O
+    from head_heterogeneous_block_amd import metrics as M
+    from head_heterogeneous_block_amd import workloads as W
+    spec = inp.spec
+    G = spec.group
+    q = W.to_numpy(inp.q[:, [0]])
+    k = W.to_numpy(inp.k[:, [0]])
+    v = W.to_numpy(inp.v[:, [0]])
+    t0 = time.perf_counter()
+    O.select_blocks_prefill(q, k, budget_head0, spec.block)
+    t_sel = time.perf_counter() - t0
+    nb = spec.n_blocks
+    ms = np.linspace(0, nb - 1, 32).astype(int)
+    sub_idx = block_idx[:, [0]]
+    sub_cnt = block_cnt[:, [0]]
+    t0 = time.perf_counter()
+    O.attention_prefill_gather(q, k, v, sub_idx, sub_cnt, spec.block, tiles=[(0, 0, int(m)) for m in ms])
+    t_att = time.perf_counter() - t0
+    mask = np.zeros_like(sub_cnt)
+    mask[0, 0, ms] = sub_cnt[0, 0, ms]
+    pairs_sample = M.prefill_pairs(sub_idx, mask, spec.seq_len, spec.block)
+    pairs_all = M.prefill_pairs(block_idx, block_cnt, spec.seq_len, spec.block)
+    total_s = t_sel * spec.n_q_heads + t_att * pairs_all / pairs_sample
+    return total_s * 1e3, t_sel + t_att
+
+
+def cpu_baseline_decode(inp, block_idx, block_cnt):
+    """The oracle decode step for one sequence, scaled by the batch size."""
+    import oracle as O
+    from head_heterogeneous_block_amd import workloads as W
+    q = W.to_numpy(inp.q[[0]])
+    k = W.to_numpy(inp.k[[0]])
+    v = W.to_numpy(inp.v[[0]])
+    t0 = time.perf_counter()
+    O.decode_select(q, k, inp.budget)
+    O.decode_attention(q, k, v, block_idx[[0]], block_cnt[[0]], inp.budget["granularity"])
+    dt = time.perf_counter() - t0
+    return dt * inp.spec.batch * 1e3, dt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the block-sparse path has no "
+              "multi-GPU leg in this build", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from head_heterogeneous_block_amd import metrics as M
+    from head_heterogeneous_block_amd import sparse_attn as SA
+    from head_heterogeneous_block_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {}
+
+    # ---------------------------------------------------------------- prefill
+    pspec = W.CONFIGS[args.prefill_config]
+    t0 = time.time()
+    pin = W.make_prefill(pspec, W.default_seed(args.prefill_config), device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] prefill inputs {pspec.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    n_bins = n_cu * args.bins_per_cu
+    t0 = time.perf_counter()
+    plan = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, kernel_variant=args.variant)
+    lpt_ms = (time.perf_counter() - t0) * 1e3
+    o = torch.empty_like(pin.q)
+    sel = lambda: plan.select(pin.q, pin.k)  # noqa: E731
+    att = lambda: plan.attend(pin.q, pin.k, pin.v, o)  # noqa: E731
+
+    # ---------------------------------------------------------------- decode
+    dspec = W.CONFIGS[args.decode_config]
+    t0 = time.time()
+    din = W.make_decode(dspec, W.default_seed(args.decode_config), device=dev)
+    dplan = SA.DecodePlan(din.q, din.k, din.v, din.budget)
+    dplan.pool(din.k)
+    do = torch.empty_like(din.q)
+    torch.cuda.synchronize()
+    print(f"[bench] decode inputs {dspec.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dsel = lambda: dplan.select(din.q, din.k)  # noqa: E731
+    datt = lambda: dplan.attend(din.q, din.k, din.v, do)  # noqa: E731
+
+    def step():
+        if args.only in ("prefill", "all"):
+            sel()
+            att()
+        if args.only in ("decode", "all"):
+            dsel()
+            datt()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing: barrier (single rank) + synchronize on both sides
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    print(f"[bench] {args.steps} timed steps, {wall_ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    reps = max(args.steps, 5)
+    res = {}
+    if args.only in ("prefill", "all"):
+        res["sel_ms"] = timed(sel, stream, reps)[0]
+        att_med, att_mean, _ = timed(att, stream, reps)
+        res["att_ms"] = att_med
+        res["att_mean_ms"] = att_mean
+    if args.only in ("decode", "all"):
+        res["dsel_ms"] = timed(dsel, stream, reps)[0]
+        res["datt_ms"] = timed(datt, stream, reps)[0]
+        res["dstep_ms"] = timed(lambda: (dsel(), datt()), stream, reps)[0]
+
+    bidx = plan.block_idx.cpu().numpy()
+    bcnt = plan.block_cnt.cpu().numpy()
+    flops = M.prefill_flops(bidx, bcnt, pspec.seq_len, pspec.block, pspec.head_dim)
+    dbidx = dplan.block_idx.cpu().numpy()
+    dbcnt = dplan.block_cnt.cpu().numpy()
+    nc = [-(-dspec.kv_len // int(g)) for g in din.budget["granularity"]]
+    scoring = [int(dplan.counts[h]) > len(range(min(int(din.budget["n_sink"][h]), nc[h]))) +
+               min(int(din.budget["n_local"][h]), nc[h]) and int(dplan.counts[h]) < nc[h]
+               for h in range(dspec.n_q_heads)]
+    dbytes = M.decode_bytes(dbidx, dbcnt, din.budget["granularity"], dspec.n_q_heads, dspec.n_kv_heads,
+                            dspec.kv_len, dspec.head_dim, 2, scoring)
+
+    prefill_ms = res.get("sel_ms", 0.0) + res.get("att_ms", 0.0)
+    tflops = flops / (res["att_mean_ms"] * 1e-3) / 1e12 if "att_ms" in res else None
+    kernel_src = os.path.join(ROOT, "head_heterogeneous_block_amd", "csrc", "sa_prefill.hip")
+    traffic = traffic_from_profiles(kernel_src)
+    roofline = {
+        "bound": "mfma",
+        "achieved": tflops,
+        "peak": M.PEAK_BF16_FLOPS / 1e12,
+        "unit": "TFLOP/s",
+        "frac": tflops / (M.PEAK_BF16_FLOPS / 1e12) if tflops else None,
+        "traffic": traffic,
+        "kernel": "prefill_kernel (sa_sparse_attn_prefill)",
+        "flops_per_launch": flops,
+        "avg_launch_ms": res.get("att_mean_ms"),
+    }
+    dgbps = dbytes["total"] / (res["dstep_ms"] * 1e-3) / 1e9 if "dstep_ms" in res else None
+    kv_gbps = dbytes["kv"] / (res["datt_ms"] * 1e-3) / 1e9 if "datt_ms" in res else None
+
+    ablation = {}
+    if not args.no_ablation and args.only in ("prefill", "all"):
+        nat = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=0, kernel_variant=args.variant)
+        nat.block_idx.copy_(plan.block_idx)
+        nat.block_cnt.copy_(plan.block_cnt)
+        ablation["natural_order_grid_ms"] = timed(lambda: nat.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+        # persistent bins in natural (contiguous) order: tiles split evenly by count
+        n_t = plan.counts.size
+        offs = np.linspace(0, n_t, n_bins + 1).astype(np.int32)
+        cont = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=0, kernel_variant=args.variant)
+        cont.block_idx = plan.block_idx
+        cont.block_cnt = plan.block_cnt
+        cont.bin_offsets = torch.from_numpy(offs).to(dev)
+        cont.items_by_bin = torch.arange(n_t, dtype=torch.int32, device=dev)
+        cont.n_bins = n_bins
+        ablation["contiguous_bins_ms"] = timed(lambda: cont.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+        ablation["lpt_bins_ms"] = res["att_ms"]
+        loads = plan.counts.reshape(-1).astype(np.int64)
+        cont_load = np.add.reduceat(loads, offs[:-1]) if n_t else loads
+        ablation["lpt_makespan_over_mean"] = float(plan.bin_load.max() / plan.bin_load.mean())
+        ablation["contiguous_makespan_over_mean"] = float(cont_load.max() / cont_load.mean())
+
+    cpu = None
+    cpu_dec = None
+    if not args.no_cpu_baseline and args.only in ("prefill", "all"):
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # noqa: BLE001
+            cores = len(os.sched_getaffinity(0))
+        bud0 = {k2: np.asarray(v2)[[0]] for k2, v2 in pin.budget.items()}
+        cpu_ms, spent = cpu_baseline_prefill(pin, bidx, bcnt, bud0)
+        cpu = {"value": cpu_ms, "unit": "ms/layer", "cores": int(cores), "kind": "oracle",
+               "sample": f"fp64 oracle on {pspec.name}: selection of query head 0 (all {pspec.n_blocks} rows) "
+                         f"scaled by {pspec.n_q_heads} heads, attention of 32 tiles of head 0 scaled by "
+                         f"attended pairs; {spent:.1f} s of CPU work"}
+        if args.only == "all":
+            dms, dspent = cpu_baseline_decode(din, dbidx, dbcnt)
+            cpu_dec = {"value": dms, "unit": "ms/step", "sample": f"sequence 0 of {dspec.batch}, scaled; "
+                                                                   f"{dspent:.1f} s"}
+
+    out = {
+        "metric": "128K prefill ms/layer + attended TFLOP/s (%MFMA peak); decode KV GB/s (%HBM)",
+        "value": prefill_ms,
+        "unit": "ms/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian Q/K/V with planted hot blocks)",
+        "config": {"workload": f"prefill {pspec.name} (S={pspec.seq_len}, Hq={pspec.n_q_heads}, "
+                               f"Hkv={pspec.n_kv_heads}, D={pspec.head_dim}, block={pspec.block}) + decode "
+                               f"{dspec.name} (batch={dspec.batch}, L={dspec.kv_len})",
+                   "global_batch": 1, "seq_len": pspec.seq_len, "parallelism": "single GPU",
+                   "lpt_bins": n_bins, "kernel_variant": args.variant},
+        "prefill": {"select_ms": res.get("sel_ms"), "attention_ms": res.get("att_ms"),
+                    "attended_tflops": tflops, "attended_flops": flops,
+                    "mfma_frac": roofline["frac"], "lpt_host_ms": lpt_ms},
+        "decode": {"select_ms": res.get("dsel_ms"), "attention_ms": res.get("datt_ms"),
+                   "step_ms": res.get("dstep_ms"), "bytes": dbytes, "step_gbps": dgbps,
+                   "hbm_frac": dgbps / (M.PEAK_HBM_BYTES / 1e9) if dgbps else None,
+                   "kv_gbps_attention_kernel": kv_gbps},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "cpu_baseline_decode": cpu_dec,
+        "ablation": ablation,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

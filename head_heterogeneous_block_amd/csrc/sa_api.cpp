@@ -1,0 +1,688 @@
+// C ABI of libsparse_attn.so: argument validation, workspace layout, the
+// greedy longest-load-first scheduler (host) and kernel launches.
+//
+// Every entry point validates all of its arguments before the first launch;
+// on error it returns a negative sa_status and records a message readable with
+// sa_last_error() on the same thread.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <queue>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/sparse_attn.h"
+#include "sa_device.hpp"
+#include "sa_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+sa_status fail(sa_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+sa_status ok() {
+  g_err.clear();
+  return SA_OK;
+}
+
+sa_status hip_fail(hipError_t e, const char* what) {
+  return fail(SA_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+sa_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    int n = 0;
+    if (hipGetDeviceCount(&n) != hipSuccess || n == 0) return fail(SA_ERR_NO_DEVICE, "no HIP device visible");
+    return hip_fail(e, "hipGetDevice");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_NO_DEVICE, "device index %d out of range", dev);
+  int s = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (s == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    s = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(s, std::memory_order_relaxed);
+    if (s == 2) return fail(SA_ERR_ARCH, "device %d is %s, the kernels are built for gfx950", dev, prop.gcnArchName);
+  }
+  if (s == 2) return fail(SA_ERR_ARCH, "device %d is not gfx950", dev);
+  return SA_OK;
+}
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int elem_size(int dtype) { return dtype == SA_BF16 ? 2 : 4; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_prefill(const sa_attn_desc* d) { return d->q_len != 1 || d->kv_len == 1; }
+
+sa_status check_desc(const sa_attn_desc* d, bool prefill) {
+  if (!d) return fail(SA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1)
+    return fail(SA_ERR_INVALID_ARG, "batch/heads must be >= 1 (got %d, %d, %d)", d->batch, d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads % d->n_kv_heads)
+    return fail(SA_ERR_INVALID_ARG, "n_q_heads %d not a multiple of n_kv_heads %d", d->n_q_heads, d->n_kv_heads);
+  if (d->n_q_heads > SA_MAX_HEADS) return fail(SA_ERR_UNSUPPORTED, "n_q_heads > %d", SA_MAX_HEADS);
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(SA_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", d->head_dim);
+  if (d->dtype != SA_BF16 && d->dtype != SA_F32) return fail(SA_ERR_INVALID_ARG, "dtype %d", d->dtype);
+  if (d->kv_len < 1) return fail(SA_ERR_INVALID_ARG, "kv_len %d", d->kv_len);
+  if (!(d->softmax_scale >= 0.f) || std::isinf(d->softmax_scale))
+    return fail(SA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
+  if (d->kernel_variant != 0 && d->kernel_variant != 2 && d->kernel_variant != 4)
+    return fail(SA_ERR_INVALID_ARG, "kernel_variant %d (0, 2 or 4)", d->kernel_variant);
+  if (d->kernel_variant == 4 && (d->dtype != SA_BF16 || d->block_size != 128))
+    return fail(SA_ERR_UNSUPPORTED, "kernel_variant 4 needs bf16 and block_size 128");
+  if (prefill) {
+    if (d->q_len != d->kv_len) return fail(SA_ERR_INVALID_ARG, "prefill needs q_len == kv_len");
+    if (d->block_size != 64 && d->block_size != 128)
+      return fail(SA_ERR_UNSUPPORTED, "block_size %d (64 or 128)", d->block_size);
+    if (d->dtype == SA_F32 && d->block_size != 64) return fail(SA_ERR_UNSUPPORTED, "fp32 prefill needs block_size 64");
+    if (cdiv(d->q_len, d->block_size) > 8192) return fail(SA_ERR_UNSUPPORTED, "more than 8192 blocks per row");
+  } else {
+    if (d->q_len != 1) return fail(SA_ERR_INVALID_ARG, "decode needs q_len == 1");
+    if (d->kv_len > (1 << 24) * 16) return fail(SA_ERR_UNSUPPORTED, "kv_len too large");
+  }
+  const int es = elem_size(d->dtype);
+  const int64_t* st[4] = {d->q_stride, d->k_stride, d->v_stride, d->o_stride};
+  for (int t = 0; t < 4; ++t) {
+    for (int i = 0; i < 3; ++i) {
+      if (st[t][i] < 0) return fail(SA_ERR_INVALID_ARG, "negative stride");
+      if (!prefill && (t == 0 || t == 3) && i == 2) continue;
+      if ((st[t][i] * es) % 16) return fail(SA_ERR_INVALID_ARG, "strides must be multiples of 16 bytes");
+    }
+    if (prefill || t == 1 || t == 2)
+      if (st[t][2] < d->head_dim) return fail(SA_ERR_INVALID_ARG, "token stride < head_dim");
+  }
+  return SA_OK;
+}
+
+sa_status check_budgets(const sa_attn_desc* d, const sa_head_budget* b, bool prefill) {
+  if (!b) return fail(SA_ERR_INVALID_ARG, "budgets is NULL");
+  for (int h = 0; h < d->n_q_heads; ++h) {
+    const sa_head_budget& x = b[h];
+    if (x.min_blocks < 1) return fail(SA_ERR_INVALID_ARG, "head %d: min_blocks must be >= 1", h);
+    if (x.n_sink < 0 || x.n_local < 0 || x.n_sink > 32767 || x.n_local > 32767)
+      return fail(SA_ERR_INVALID_ARG, "head %d: bad n_sink/n_local", h);
+    if (x.n_sink + x.n_local > x.min_blocks)
+      return fail(SA_ERR_INVALID_ARG, "head %d: n_sink + n_local (%d) exceeds min_blocks %d", h, x.n_sink + x.n_local,
+                  x.min_blocks);
+    if (x.ratio_q16 > 65536u) return fail(SA_ERR_INVALID_ARG, "head %d: ratio_q16 > 65536", h);
+    if (!prefill) {
+      const int g = x.granularity;
+      if (g != 16 && g != 32 && g != 64 && g != 128)
+        return fail(SA_ERR_UNSUPPORTED, "head %d: granularity %d (16, 32, 64 or 128)", h, g);
+    }
+  }
+  return SA_OK;
+}
+
+sa::HeadTable make_table(const sa_attn_desc* d, const sa_head_budget* b, bool prefill) {
+  sa::HeadTable t;
+  std::memset(&t, 0, sizeof t);
+  for (int h = 0; h < d->n_q_heads; ++h) {
+    t.min_blocks[h] = b[h].min_blocks;
+    t.ratio_q16[h] = b[h].ratio_q16;
+    t.n_sink[h] = int16_t(b[h].n_sink);
+    t.n_local[h] = int16_t(b[h].n_local);
+    t.gran[h] = int16_t(prefill ? d->block_size : b[h].granularity);
+  }
+  return t;
+}
+
+int forced_count(int n, int ns, int nl) {
+  ns = std::min(ns, n);
+  const int lo = std::max(ns, n - nl);
+  return ns + (n - lo);
+}
+
+int decode_count(const sa_attn_desc* d, const sa_head_budget& b) {
+  const int nc = int(cdiv(d->kv_len, b.granularity));
+  return sa::budget_blocks(nc, b.min_blocks, b.ratio_q16);
+}
+
+bool decode_scores_head(const sa_attn_desc* d, const sa_head_budget& b) {
+  const int nc = int(cdiv(d->kv_len, b.granularity));
+  const int k = sa::budget_blocks(nc, b.min_blocks, b.ratio_q16);
+  return k > forced_count(nc, b.n_sink, b.n_local) && k < nc;
+}
+
+// distinct granularities of the scoring heads, ascending
+std::vector<int> decode_pools(const sa_attn_desc* d, const sa_head_budget* b) {
+  std::vector<int> g;
+  for (int h = 0; h < d->n_q_heads; ++h)
+    if (decode_scores_head(d, b[h])) g.push_back(b[h].granularity);
+  std::sort(g.begin(), g.end());
+  g.erase(std::unique(g.begin(), g.end()), g.end());
+  return g;
+}
+
+size_t pooled_elems(const sa_attn_desc* d, int g) {
+  return size_t(d->batch) * d->n_kv_heads * cdiv(d->kv_len, g) * d->head_dim;
+}
+
+// ---- workspace layouts
+struct PrefillSelectWs {
+  size_t qpool, kpool, scores, total;
+};
+PrefillSelectWs prefill_select_ws(const sa_attn_desc* d) {
+  const size_t nb = cdiv(d->q_len, d->block_size);
+  PrefillSelectWs w;
+  w.qpool = 0;
+  w.kpool = w.qpool + align256(size_t(d->batch) * d->n_q_heads * nb * d->head_dim * 4);
+  w.scores = w.kpool + align256(size_t(d->batch) * d->n_kv_heads * nb * d->head_dim * 4);
+  w.total = w.scores + align256(size_t(d->batch) * d->n_q_heads * nb * nb * 4);
+  return w;
+}
+
+struct DecodeSelectWs {
+  size_t pooled, scores, total;
+  int nc_max;
+};
+DecodeSelectWs decode_select_ws(const sa_attn_desc* d, const sa_head_budget* b, bool need_pool) {
+  DecodeSelectWs w;
+  w.nc_max = 1;
+  for (int h = 0; h < d->n_q_heads; ++h)
+    if (decode_scores_head(d, b[h])) w.nc_max = std::max<int>(w.nc_max, int(cdiv(d->kv_len, b[h].granularity)));
+  w.pooled = 0;
+  size_t pooled = 0;
+  if (need_pool)
+    for (int g : decode_pools(d, b)) pooled += pooled_elems(d, g) * 4;
+  w.scores = align256(pooled);
+  w.total = w.scores + align256(size_t(d->batch) * d->n_q_heads * w.nc_max * 4);
+  return w;
+}
+
+constexpr int kChunkAtoms = 32;
+
+struct DecodeAttnWs {
+  size_t atoms, n_union, part_o, part_ml, total;
+  int max_union, n_chunks;
+};
+DecodeAttnWs decode_attn_ws(const sa_attn_desc* d, const sa_head_budget* b) {
+  const int G = d->n_q_heads / d->n_kv_heads;
+  const int64_t n_atoms = cdiv(d->kv_len, sa::kAtom);
+  int64_t mu = 1;
+  for (int j = 0; j < d->n_kv_heads; ++j) {
+    int64_t s = 0;
+    for (int gi = 0; gi < G; ++gi) {
+      const sa_head_budget& x = b[j * G + gi];
+      s += int64_t(decode_count(d, x)) * (x.granularity / sa::kAtom);
+    }
+    mu = std::max(mu, std::min(s, n_atoms));
+  }
+  DecodeAttnWs w;
+  w.max_union = int(mu);
+  w.n_chunks = int(cdiv(mu, kChunkAtoms));
+  const size_t bk = size_t(d->batch) * d->n_kv_heads;
+  w.atoms = 0;
+  w.n_union = align256(bk * w.max_union * 4);
+  w.part_o = w.n_union + align256(bk * 4);
+  w.part_ml = w.part_o + align256(bk * w.n_chunks * G * d->head_dim * 4);
+  w.total = w.part_ml + align256(bk * w.n_chunks * G * 2 * 4);
+  return w;
+}
+
+float scale_of(const sa_attn_desc* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt(float(d->head_dim));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sa_version(void) { return 10000; }
+
+const char* sa_last_error(void) { return g_err.c_str(); }
+
+sa_status sa_lpt_schedule(const int64_t* loads, int32_t n_items, int32_t n_bins, int32_t* bin_of_item,
+                          int32_t* bin_offsets, int32_t* items_by_bin, int64_t* bin_load) {
+  if (n_items < 0) return fail(SA_ERR_INVALID_ARG, "n_items < 0");
+  if (n_bins < 1) return fail(SA_ERR_INVALID_ARG, "n_bins must be >= 1");
+  if (n_items > 0 && (!loads || !bin_of_item || !items_by_bin)) return fail(SA_ERR_INVALID_ARG, "NULL array");
+  if (!bin_offsets) return fail(SA_ERR_INVALID_ARG, "bin_offsets is NULL");
+  for (int32_t i = 0; i < n_items; ++i)
+    if (loads[i] < 0) return fail(SA_ERR_INVALID_ARG, "load of item %d is negative", i);
+  // items by load, largest first; equal loads keep ascending item order
+  std::vector<int32_t> order(n_items);
+  for (int32_t i = 0; i < n_items; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return loads[a] > loads[b]; });
+  // least-loaded bin first; equal loads: lower bin index
+  using Entry = std::pair<int64_t, int32_t>;
+  std::priority_queue<Entry, std::vector<Entry>, std::greater<Entry>> heap;
+  for (int32_t b = 0; b < n_bins; ++b) heap.push({0, b});
+  std::vector<int32_t> count(n_bins, 0);
+  std::vector<int64_t> load(n_bins, 0);
+  for (int32_t i : order) {
+    Entry e = heap.top();
+    heap.pop();
+    bin_of_item[i] = e.second;
+    count[e.second] += 1;
+    load[e.second] = e.first + loads[i];
+    heap.push({load[e.second], e.second});
+  }
+  bin_offsets[0] = 0;
+  for (int32_t b = 0; b < n_bins; ++b) bin_offsets[b + 1] = bin_offsets[b] + count[b];
+  std::vector<int32_t> fill(bin_offsets, bin_offsets + n_bins);
+  for (int32_t i : order) items_by_bin[fill[bin_of_item[i]]++] = i;  // assignment order
+  if (bin_load)
+    for (int32_t b = 0; b < n_bins; ++b) bin_load[b] = load[b];
+  return ok();
+}
+
+sa_status sa_prefill_block_counts(const sa_attn_desc* desc, const sa_head_budget* budgets, int32_t* counts,
+                                  int32_t* kmax) {
+  sa_status s = check_desc(desc, true);
+  if (s) return s;
+  if ((s = check_budgets(desc, budgets, true))) return s;
+  const int nb = int(cdiv(desc->q_len, desc->block_size));
+  int km = 0;
+  for (int b = 0; b < desc->batch; ++b)
+    for (int h = 0; h < desc->n_q_heads; ++h)
+      for (int m = 0; m < nb; ++m) {
+        const int k = sa::budget_blocks(m + 1, budgets[h].min_blocks, budgets[h].ratio_q16);
+        if (counts) counts[((int64_t)b * desc->n_q_heads + h) * nb + m] = k;
+        km = std::max(km, k);
+      }
+  if (kmax) *kmax = km;
+  return ok();
+}
+
+sa_status sa_decode_block_counts(const sa_attn_desc* desc, const sa_head_budget* budgets, int32_t* counts,
+                                 int32_t* kmax) {
+  sa_status s = check_desc(desc, false);
+  if (s) return s;
+  if ((s = check_budgets(desc, budgets, false))) return s;
+  int km = 0;
+  for (int h = 0; h < desc->n_q_heads; ++h) {
+    const int k = decode_count(desc, budgets[h]);
+    if (counts) counts[h] = k;
+    km = std::max(km, k);
+  }
+  if (kmax) *kmax = km;
+  return ok();
+}
+
+size_t sa_decode_pooled_size(const sa_attn_desc* desc, const sa_head_budget* budgets) {
+  if (check_desc(desc, false) || check_budgets(desc, budgets, false)) return 0;
+  size_t n = 0;
+  for (int g : decode_pools(desc, budgets)) n += pooled_elems(desc, g) * 4;
+  return n;
+}
+
+static sa_status pool_decode_into(const sa_attn_desc* d, const sa_head_budget* b, const void* k, float* out,
+                                  hipStream_t st) {
+  size_t off = 0;
+  for (int g : decode_pools(d, b)) {
+    sa::PoolParams pp;
+    pp.x = k;
+    pp.s0 = d->k_stride[0];
+    pp.s1 = d->k_stride[1];
+    pp.s2 = d->k_stride[2];
+    pp.out = out + off;
+    pp.heads = d->n_kv_heads;
+    pp.T = d->kv_len;
+    pp.g = g;
+    pp.nb = int(cdiv(d->kv_len, g));
+    pp.blocks_per_wg = std::max(1, 256 / g);
+    hipError_t e = sa::launch_pool(pp, d->dtype, d->head_dim, d->batch, st);
+    if (e != hipSuccess) return hip_fail(e, "pool kernel launch");
+    off += pooled_elems(d, g);
+  }
+  return SA_OK;
+}
+
+sa_status sa_pool_keys_decode(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* k,
+                              float* k_pooled, void* stream) {
+  sa_status s = check_desc(desc, false);
+  if (s) return s;
+  if ((s = check_budgets(desc, budgets, false))) return s;
+  if (!k || !k_pooled) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(k) || !aligned16(k_pooled)) return fail(SA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if ((s = check_device())) return s;
+  if ((s = pool_decode_into(desc, budgets, k, k_pooled, (hipStream_t)stream))) return s;
+  return ok();
+}
+
+size_t sa_select_workspace_size(const sa_attn_desc* desc, const sa_head_budget* budgets, int32_t kmax) {
+  (void)kmax;
+  if (!desc) return 0;
+  if (is_prefill(desc)) {
+    if (check_desc(desc, true)) return 0;
+    return prefill_select_ws(desc).total;
+  }
+  if (check_desc(desc, false) || check_budgets(desc, budgets, false)) return 0;
+  return decode_select_ws(desc, budgets, true).total;
+}
+
+sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* q, const void* k,
+                           const float* k_pooled, int32_t* block_idx, int32_t* block_cnt, int32_t kmax,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!desc) return fail(SA_ERR_INVALID_ARG, "desc is NULL");
+  const bool prefill = is_prefill(desc);
+  sa_status s = check_desc(desc, prefill);
+  if (s) return s;
+  if ((s = check_budgets(desc, budgets, prefill))) return s;
+  if (!q || !k || !block_idx || !block_cnt) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || (k_pooled && !aligned16(k_pooled)))
+    return fail(SA_ERR_INVALID_ARG, "q, k and k_pooled must be 16-byte aligned");
+  int32_t need = 0;
+  if (prefill) {
+    if (k_pooled) return fail(SA_ERR_INVALID_ARG, "k_pooled must be NULL for prefill");
+    sa_prefill_block_counts(desc, budgets, nullptr, &need);
+  } else {
+    sa_decode_block_counts(desc, budgets, nullptr, &need);
+  }
+  if (kmax < need) return fail(SA_ERR_INVALID_ARG, "kmax %d < largest block count %d", kmax, need);
+  const size_t ws_need = prefill ? prefill_select_ws(desc).total : decode_select_ws(desc, budgets, !k_pooled).total;
+  if (!workspace || workspace_bytes < ws_need)
+    return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws_need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(SA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if ((s = check_device())) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  const float scale = scale_of(desc);
+  const int D = desc->head_dim;
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  hipError_t e;
+  sa::TopkParams tp;
+  std::memset(&tp, 0, sizeof tp);
+  tp.idx = block_idx;
+  tp.cnt = block_cnt;
+  tp.kmax = kmax;
+  tp.Hq = desc->n_q_heads;
+  tp.heads = make_table(desc, budgets, prefill);
+  if (prefill) {
+    const PrefillSelectWs w = prefill_select_ws(desc);
+    const int nb = int(cdiv(desc->q_len, desc->block_size));
+    float* qp = reinterpret_cast<float*>(ws + w.qpool);
+    float* kp = reinterpret_cast<float*>(ws + w.kpool);
+    float* sc = reinterpret_cast<float*>(ws + w.scores);
+    sa::PoolParams pp;
+    pp.g = desc->block_size;
+    pp.nb = nb;
+    pp.T = desc->q_len;
+    pp.blocks_per_wg = 1;
+    pp.x = q;
+    pp.s0 = desc->q_stride[0];
+    pp.s1 = desc->q_stride[1];
+    pp.s2 = desc->q_stride[2];
+    pp.out = qp;
+    pp.heads = desc->n_q_heads;
+    if ((e = sa::launch_pool(pp, desc->dtype, D, desc->batch, st)) != hipSuccess) return hip_fail(e, "pool Q");
+    pp.x = k;
+    pp.s0 = desc->k_stride[0];
+    pp.s1 = desc->k_stride[1];
+    pp.s2 = desc->k_stride[2];
+    pp.out = kp;
+    pp.heads = desc->n_kv_heads;
+    if ((e = sa::launch_pool(pp, desc->dtype, D, desc->batch, st)) != hipSuccess) return hip_fail(e, "pool K");
+    sa::PrefillScoreParams sp;
+    sp.qp = qp;
+    sp.kp = kp;
+    sp.s = sc;
+    sp.Hq = desc->n_q_heads;
+    sp.G = G;
+    sp.NB = nb;
+    sp.scale = scale;
+    if ((e = sa::launch_prefill_scores(sp, D, desc->batch, st)) != hipSuccess) return hip_fail(e, "block scores");
+    tp.s = sc;
+    tp.s_row = nb;
+    tp.rows = desc->batch * desc->n_q_heads * nb;
+    tp.mode = 0;
+    tp.NB = nb;
+    if ((e = sa::launch_topk(tp, nb, st)) != hipSuccess) return hip_fail(e, "top-k");
+    return ok();
+  }
+  // decode
+  const DecodeSelectWs w = decode_select_ws(desc, budgets, !k_pooled);
+  const float* pooled = k_pooled;
+  if (!pooled) {
+    if ((s = pool_decode_into(desc, budgets, k, reinterpret_cast<float*>(ws + w.pooled), st))) return s;
+    pooled = reinterpret_cast<const float*>(ws + w.pooled);
+  }
+  float* sc = reinterpret_cast<float*>(ws + w.scores);
+  const std::vector<int> pools = decode_pools(desc, budgets);
+  if (pools.size() > 4) return fail(SA_ERR_UNSUPPORTED, "more than 4 granularities");
+  sa::DecodeScoreParams dp;
+  std::memset(&dp, 0, sizeof dp);
+  dp.q = q;
+  dp.qs0 = desc->q_stride[0];
+  dp.qs1 = desc->q_stride[1];
+  dp.pooled = pooled;
+  {
+    int64_t off = 0;
+    for (size_t i = 0; i < pools.size(); ++i) {
+      dp.pool_off[i] = off;
+      dp.pool_nc[i] = int(cdiv(desc->kv_len, pools[i]));
+      off += int64_t(pooled_elems(desc, pools[i]));
+    }
+  }
+  dp.s = sc;
+  dp.nc_max = w.nc_max;
+  dp.Hq = desc->n_q_heads;
+  dp.Hkv = desc->n_kv_heads;
+  dp.rows_per_wg = 256;
+  dp.scale = scale;
+  // jobs: (KV head, granularity) -> the scoring heads, at most 8 per job
+  std::vector<sa::DecodeScoreJob> jobs;
+  for (int j = 0; j < desc->n_kv_heads; ++j)
+    for (size_t pi = 0; pi < pools.size(); ++pi) {
+      sa::DecodeScoreJob job;
+      std::memset(&job, 0, sizeof job);
+      job.kvh = j;
+      job.pool = int(pi);
+      for (int gi = 0; gi < G; ++gi) {
+        const int h = j * G + gi;
+        if (decode_scores_head(desc, budgets[h]) && budgets[h].granularity == pools[pi]) {
+          if (job.n_heads == 8) {
+            jobs.push_back(job);
+            job.n_heads = 0;
+          }
+          job.heads[job.n_heads++] = h;
+        }
+      }
+      if (job.n_heads) jobs.push_back(job);
+    }
+  for (size_t j0 = 0; j0 < jobs.size(); j0 += sa::kMaxScoreJobs) {
+    const size_t nj = std::min<size_t>(sa::kMaxScoreJobs, jobs.size() - j0);
+    dp.n_jobs = int(nj);
+    for (size_t i = 0; i < nj; ++i) dp.jobs[i] = jobs[j0 + i];
+    if ((e = sa::launch_decode_scores(dp, desc->dtype, D, desc->batch, st)) != hipSuccess)
+      return hip_fail(e, "decode scores");
+  }
+  tp.s = sc;
+  tp.s_row = w.nc_max;
+  tp.rows = desc->batch * desc->n_q_heads;
+  tp.mode = 1;
+  tp.kv_len = desc->kv_len;
+  if ((e = sa::launch_topk(tp, w.nc_max, st)) != hipSuccess) return hip_fail(e, "decode top-k");
+  return ok();
+}
+
+size_t sa_prefill_workspace_size(const sa_attn_desc* desc, int32_t kmax, int32_t n_bins) {
+  (void)desc;
+  (void)kmax;
+  (void)n_bins;
+  return 0;
+}
+
+sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
+                                 const int32_t* bin_offsets, const int32_t* items_by_bin, int32_t n_bins,
+                                 int32_t out_f32, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  sa_status s = check_desc(desc, true);
+  if (s) return s;
+  if (!q || !k || !v || !o || !block_idx || !block_cnt) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(SA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
+  if (kmax < 1) return fail(SA_ERR_INVALID_ARG, "kmax must be >= 1");
+  if ((bin_offsets == nullptr) != (items_by_bin == nullptr))
+    return fail(SA_ERR_INVALID_ARG, "bin_offsets and items_by_bin must both be given or both NULL");
+  if (bin_offsets && n_bins < 1) return fail(SA_ERR_INVALID_ARG, "n_bins must be >= 1");
+  const int64_t nb = cdiv(desc->q_len, desc->block_size);
+  const int64_t n_tiles = int64_t(desc->batch) * desc->n_q_heads * nb;
+  if (n_tiles > (1ll << 30)) return fail(SA_ERR_UNSUPPORTED, "too many tiles");
+  {
+    const int64_t es = elem_size(desc->dtype);
+    if (int64_t(desc->kv_len) * desc->k_stride[2] * es >= (1ll << 31) ||
+        int64_t(desc->kv_len) * desc->v_stride[2] * es >= (1ll << 31))
+      return fail(SA_ERR_UNSUPPORTED, "one (batch, KV head) slice of K or V must span < 2 GiB");
+  }
+  if ((s = check_device())) return s;
+  sa::PrefillParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.qs0 = desc->q_stride[0];
+  p.qs1 = desc->q_stride[1];
+  p.qs2 = desc->q_stride[2];
+  p.ks0 = desc->k_stride[0];
+  p.ks1 = desc->k_stride[1];
+  p.ks2 = desc->k_stride[2];
+  p.vs0 = desc->v_stride[0];
+  p.vs1 = desc->v_stride[1];
+  p.vs2 = desc->v_stride[2];
+  p.os0 = desc->o_stride[0];
+  p.os1 = desc->o_stride[1];
+  p.os2 = desc->o_stride[2];
+  p.block_idx = block_idx;
+  p.block_cnt = block_cnt;
+  p.kmax = kmax;
+  p.bin_offsets = bin_offsets;
+  p.items_by_bin = items_by_bin;
+  p.Hq = desc->n_q_heads;
+  p.G = desc->n_q_heads / desc->n_kv_heads;
+  p.S = desc->q_len;
+  p.NB = int(nb);
+  p.n_tiles = int(n_tiles);
+  p.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+  p.out_f32 = out_f32 ? 1 : 0;
+  const int grid = bin_offsets ? n_bins : int(n_tiles);
+  // default: 4 waves x 32 queries (two waves per SIMD) where built, else 2 x B/2
+  const bool four = desc->dtype == SA_BF16 && desc->block_size == 128;
+  const int waves = desc->kernel_variant != 0 ? desc->kernel_variant : (four ? 4 : 2);
+  hipError_t e =
+      sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, waves, grid, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
+  return ok();
+}
+
+size_t sa_decode_workspace_size(const sa_attn_desc* desc, const sa_head_budget* budgets, int32_t kmax) {
+  (void)kmax;
+  if (check_desc(desc, false) || check_budgets(desc, budgets, false)) return 0;
+  return decode_attn_ws(desc, budgets).total;
+}
+
+sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* q,
+                                const void* k, const void* v, void* o, float* lse, const int32_t* block_idx,
+                                const int32_t* block_cnt, int32_t kmax, int32_t out_f32, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  sa_status s = check_desc(desc, false);
+  if (s) return s;
+  if ((s = check_budgets(desc, budgets, false))) return s;
+  if (!q || !k || !v || !o || !block_idx || !block_cnt) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(k) || !aligned16(v)) return fail(SA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  const int G = desc->n_q_heads / desc->n_kv_heads;
+  if (G > 8) return fail(SA_ERR_UNSUPPORTED, "GQA group size %d > 8", G);
+  int32_t need = 0;
+  sa_decode_block_counts(desc, budgets, nullptr, &need);
+  if (kmax < need) return fail(SA_ERR_INVALID_ARG, "kmax %d < largest block count %d", kmax, need);
+  const DecodeAttnWs w = decode_attn_ws(desc, budgets);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", w.total, workspace_bytes);
+  if (!aligned16(workspace)) return fail(SA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const int64_t n_atoms = cdiv(desc->kv_len, sa::kAtom);
+  if (int64_t(G) * cdiv(n_atoms, 32) * 4 > 64 * 1024) return fail(SA_ERR_UNSUPPORTED, "kv_len too long for the plan");
+  if ((s = check_device())) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  uint32_t* atoms = reinterpret_cast<uint32_t*>(ws + w.atoms);
+  int32_t* n_union = reinterpret_cast<int32_t*>(ws + w.n_union);
+  float* part_o = reinterpret_cast<float*>(ws + w.part_o);
+  float* part_ml = reinterpret_cast<float*>(ws + w.part_ml);
+  hipError_t e;
+  sa::DecodePlanParams pp;
+  pp.block_idx = block_idx;
+  pp.block_cnt = block_cnt;
+  pp.kmax = kmax;
+  pp.Hq = desc->n_q_heads;
+  pp.Hkv = desc->n_kv_heads;
+  pp.G = G;
+  pp.kv_len = desc->kv_len;
+  pp.n_atoms = int(n_atoms);
+  pp.max_union = w.max_union;
+  pp.atoms = atoms;
+  pp.n_union = n_union;
+  pp.heads = make_table(desc, budgets, false);
+  if ((e = sa::launch_decode_plan(pp, desc->batch, st)) != hipSuccess) return hip_fail(e, "decode plan");
+  sa::DecodeAttnParams ap;
+  ap.q = q;
+  ap.qs0 = desc->q_stride[0];
+  ap.qs1 = desc->q_stride[1];
+  ap.k = k;
+  ap.v = v;
+  ap.ks0 = desc->k_stride[0];
+  ap.ks1 = desc->k_stride[1];
+  ap.ks2 = desc->k_stride[2];
+  ap.vs0 = desc->v_stride[0];
+  ap.vs1 = desc->v_stride[1];
+  ap.vs2 = desc->v_stride[2];
+  ap.atoms = atoms;
+  ap.n_union = n_union;
+  ap.max_union = w.max_union;
+  ap.chunk_atoms = kChunkAtoms;
+  ap.n_chunks = w.n_chunks;
+  ap.Hq = desc->n_q_heads;
+  ap.Hkv = desc->n_kv_heads;
+  ap.G = G;
+  ap.kv_len = desc->kv_len;
+  ap.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+  ap.part_o = part_o;
+  ap.part_ml = part_ml;
+  if ((e = sa::launch_decode_attn(ap, desc->dtype, desc->head_dim, desc->batch, st)) != hipSuccess)
+    return hip_fail(e, "decode attention");
+  sa::DecodeCombineParams cp;
+  cp.part_o = part_o;
+  cp.part_ml = part_ml;
+  cp.n_union = n_union;
+  cp.chunk_atoms = kChunkAtoms;
+  cp.n_chunks = w.n_chunks;
+  cp.Hq = desc->n_q_heads;
+  cp.Hkv = desc->n_kv_heads;
+  cp.G = G;
+  cp.o = o;
+  cp.os0 = desc->o_stride[0];
+  cp.os1 = desc->o_stride[1];
+  cp.lse = lse;
+  cp.out_f32 = out_f32 ? 1 : 0;
+  if ((e = sa::launch_decode_combine(cp, desc->dtype, desc->head_dim, desc->batch, st)) != hipSuccess)
+    return hip_fail(e, "decode combine");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Launch interfaces of the gfx950 kernels (host side).  Only sa_api.cpp calls
+// these, after validating every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kMaxHeads = 128;
+
+// Per-head budget parameters, passed by value in kernel arguments.
+struct HeadTable {
+  int32_t min_blocks[kMaxHeads];
+  uint32_t ratio_q16[kMaxHeads];
+  int16_t n_sink[kMaxHeads];
+  int16_t n_local[kMaxHeads];
+  int16_t gran[kMaxHeads];
+};
+
+// ---------------------------------------------------------------- pooling
+struct PoolParams {
+  const void* x;         // [batch][heads][T][D] (strided)
+  int64_t s0, s1, s2;    // strides in elements
+  float* out;            // [batch][heads][nb][D] fp32, contiguous
+  int heads, T, g, nb, blocks_per_wg;
+};
+hipError_t launch_pool(const PoolParams& p, int dtype, int D, int batch, hipStream_t stream);
+
+// ---------------------------------------------------------------- prefill selection
+struct PrefillScoreParams {
+  const float* qp;  // [batch*Hq][NB][D]
+  const float* kp;  // [batch*Hkv][NB][D]
+  float* s;         // [batch*Hq][NB][NB]
+  int Hq, G, NB;
+  float scale;
+};
+hipError_t launch_prefill_scores(const PrefillScoreParams& p, int D, int batch, hipStream_t stream);
+
+struct TopkParams {
+  const float* s;       // scores; row r at s + r * s_row
+  int64_t s_row;
+  int32_t* idx;         // out: row r at idx + r * kmax
+  int32_t* cnt;         // out: [rows]
+  int kmax;
+  int rows;
+  int mode;             // 0: prefill rows (bh, m): candidates m+1; 1: decode rows (b, h)
+  int Hq, NB;           // prefill: rows = batch*Hq*NB
+  int kv_len;           // decode
+  HeadTable heads;
+};
+hipError_t launch_topk(const TopkParams& p, int max_cand, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode selection
+struct DecodeScoreJob {
+  int kvh;        // KV head
+  int pool;       // index of the pooled array (granularity class)
+  int n_heads;
+  int heads[8];
+};
+constexpr int kMaxScoreJobs = 48;
+struct DecodeScoreParams {
+  const void* q;          // [batch][Hq][D]
+  int64_t qs0, qs1;
+  const float* pooled;    // concatenated pooled arrays
+  int64_t pool_off[4];    // element offset of each pooled array
+  int pool_nc[4];         // blocks per head of each pooled array
+  float* s;               // [batch][Hq][nc_max]
+  int nc_max, Hq, Hkv, n_jobs, rows_per_wg;
+  float scale;
+  DecodeScoreJob jobs[kMaxScoreJobs];
+};
+hipError_t launch_decode_scores(const DecodeScoreParams& p, int dtype, int D, int batch, hipStream_t stream);
+
+// ---------------------------------------------------------------- prefill attention
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
+  const int32_t* block_idx;
+  const int32_t* block_cnt;
+  int kmax;
+  const int32_t* bin_offsets;   // nullable
+  const int32_t* items_by_bin;
+  int Hq, G, S, NB, n_tiles;
+  float scale_log2;
+  int out_f32;
+};
+// waves: workgroup size in waves (2 or 4); the tile's B queries are split over them
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int waves, int grid, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode attention
+// Union of the selected 16-token atoms of the query heads of one KV group.
+constexpr int kAtom = 16;
+struct DecodePlanParams {
+  const int32_t* block_idx;  // [batch][Hq][kmax]
+  const int32_t* block_cnt;  // [batch][Hq]
+  int kmax, Hq, Hkv, G, kv_len, n_atoms;  // n_atoms = ceil(kv_len / 16)
+  int max_union;             // capacity of the atom list per (b, kvh)
+  uint32_t* atoms;           // out: [batch][Hkv][max_union]: atom index | head mask << 24
+  int32_t* n_union;          // out: [batch][Hkv]
+  HeadTable heads;
+};
+hipError_t launch_decode_plan(const DecodePlanParams& p, int batch, hipStream_t stream);
+
+struct DecodeAttnParams {
+  const void* q;
+  int64_t qs0, qs1;
+  const void* k;
+  const void* v;
+  int64_t ks0, ks1, ks2, vs0, vs1, vs2;
+  const uint32_t* atoms;
+  const int32_t* n_union;
+  int max_union, chunk_atoms, n_chunks;  // chunks per (b, kvh)
+  int Hq, Hkv, G, kv_len;
+  float scale_log2;
+  float* part_o;    // [batch][Hkv][n_chunks][G][D]
+  float* part_ml;   // [batch][Hkv][n_chunks][G][2]  (max in log2 domain, sum)
+};
+hipError_t launch_decode_attn(const DecodeAttnParams& p, int dtype, int D, int batch, hipStream_t stream);
+
+struct DecodeCombineParams {
+  const float* part_o;
+  const float* part_ml;
+  const int32_t* n_union;
+  int chunk_atoms, n_chunks, Hq, Hkv, G;
+  void* o;
+  int64_t os0, os1;
+  float* lse;
+  int out_f32;
+};
+hipError_t launch_decode_combine(const DecodeCombineParams& p, int dtype, int D, int batch, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,376 @@
+// Block selection kernels for gfx950: mean pooling, block scores and the exact
+// per-row top-k with forced sink/local blocks.
+//
+//  * pooling: the Index step of "Unifying Sparse Attention with Hierarchical
+//    Memory for Scalable Long-Context LLM Serving" (Spin), Spanish summary
+//    §2.A, at block granularity ("Fluxion", Italian summary, Intuizioni
+//    Chiave 2): the mean of the rows of every block, accumulated in fp32.
+//  * scoring + top-k: the Select step (same passage) with per-head budgets
+//    ("S-HPLB ...", Italian summary §2.A, Chinese summary §2.1) and a top-k
+//    token budget per head (same pages §1).
+//
+// Top-k is exact: scores become order-preserving 32-bit keys; the k'-th largest
+// key is found by a 32-step bitwise search over block-wide counts; blocks with a
+// larger key, and the first (lowest-index) ties, are kept.  Candidates are
+// scanned in index order, so the output comes out ascending with no sort.
+
+#include "sa_device.hpp"
+#include "sa_kernels.hpp"
+
+namespace sa {
+
+namespace {
+
+// ---------------------------------------------------------------- pooling
+// One workgroup (256 threads) pools `blocks_per_wg` consecutive blocks of one
+// (batch, head).  Each thread owns one 16-byte column chunk and a strided set
+// of rows; row groups are combined through LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
+  constexpr int kE = 16 / int(sizeof(T));  // elements per chunk
+  constexpr int kCh = D / kE;              // chunks per row
+  constexpr int kRG = 256 / kCh;           // row groups
+  __shared__ float part[kRG][D + 1];
+  const int tid = threadIdx.x;
+  const int ch = tid % kCh, rg = tid / kCh;
+  const int h = blockIdx.y, bi = blockIdx.z;
+  const char* base = reinterpret_cast<const char*>(p.x) + (bi * p.s0 + h * p.s1) * (int64_t)sizeof(T);
+  const int64_t rs = p.s2 * (int64_t)sizeof(T);
+  for (int bb = 0; bb < p.blocks_per_wg; ++bb) {
+    const int n = blockIdx.x * p.blocks_per_wg + bb;
+    if (n >= p.nb) break;
+    const int lo = n * p.g;
+    const int cnt = min(p.g, p.T - lo);
+    float acc[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+    for (int r = rg; r < cnt; r += kRG) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(base + (int64_t)(lo + r) * rs + ch * 16);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16_lo(w[e]);
+          acc[2 * e + 1] += bf16_hi(w[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kE; ++e) part[rg][ch * kE + e] = acc[e];
+    __syncthreads();
+    for (int d = tid; d < D; d += 256) {
+      float s = 0.f;
+#pragma unroll 8
+      for (int r = 0; r < kRG; ++r) s += part[r][d];
+      p.out[(((int64_t)bi * p.heads + h) * p.nb + n) * D + d] = s / float(cnt);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- prefill block scores
+// s[bh][m][n] = scale * <Qbar[bh][m], Kbar[bkv][n]> for the causal 64x64 tiles.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_scores_kernel(PrefillScoreParams p) {
+  constexpr int kT = 64;
+  constexpr int kDC = 32;  // d columns staged per pass
+  __shared__ float qs[kT][kDC + 1];
+  __shared__ float ks[kT][kDC + 1];
+  const int n0 = blockIdx.x * kT, m0 = blockIdx.y * kT;
+  if (n0 > m0 + kT - 1) return;  // entirely above the diagonal
+  const int bh = blockIdx.z;
+  const int bi = bh / p.Hq, h = bh % p.Hq;
+  const int bkv = bi * (p.Hq / p.G) + h / p.G;
+  const float* qp = p.qp + (int64_t)bh * p.NB * D;
+  const float* kp = p.kp + (int64_t)bkv * p.NB * D;
+  const int tid = threadIdx.x;
+  const int tm = tid / 16, tn = tid % 16;
+  float acc[4][4] = {};
+  for (int d0 = 0; d0 < D; d0 += kDC) {
+    for (int i = tid; i < kT * kDC / 4; i += 256) {
+      const int r = i / (kDC / 4), c = (i % (kDC / 4)) * 4;
+      f32x4 a = (m0 + r < p.NB) ? *reinterpret_cast<const f32x4*>(qp + (int64_t)(m0 + r) * D + d0 + c) : f32x4{};
+      f32x4 b = (n0 + r < p.NB) ? *reinterpret_cast<const f32x4*>(kp + (int64_t)(n0 + r) * D + d0 + c) : f32x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qs[r][c + e] = a[e];
+        ks[r][c + e] = b[e];
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int d = 0; d < kDC; ++d) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = qs[tm + 16 * i][d];
+        b[i] = ks[tn + 16 * i][d];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* srow = p.s + (int64_t)bh * p.NB * p.NB;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + tm + 16 * i;
+    if (m >= p.NB) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tn + 16 * j;
+      if (n <= m) srow[(int64_t)m * p.NB + n] = acc[i][j] * p.scale;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- top-k
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* red) {
+  x = wave_sum_u32(x);
+  if constexpr (NT == 64) {
+    return x;
+  } else {
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = x;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) t += red[i];
+    return t;
+  }
+}
+
+// Exclusive prefix (in thread order) of a per-thread flag; returns the total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_prefix(bool flag, uint32_t& before, uint32_t* red) {
+  const uint64_t b = __ballot(flag);
+  const uint32_t in_wave = lanes_below(b);
+  const uint32_t wave_tot = __popcll(b);
+  if constexpr (NT == 64) {
+    before = in_wave;
+    return wave_tot;
+  } else {
+    const int w = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[w] = wave_tot;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      off += (i < w) ? red[i] : 0u;
+      tot += red[i];
+    }
+    before = off + in_wave;
+    return tot;
+  }
+}
+
+template <int NT, int CPT>
+__global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
+  __shared__ uint32_t red[NT / 64 > 0 ? NT / 64 : 1];
+  const int row = blockIdx.x;
+  if (row >= p.rows) return;
+  const int tid = threadIdx.x;
+  int h, n_cand;
+  if (p.mode == 0) {
+    const int m = row % p.NB;
+    h = (row / p.NB) % p.Hq;
+    n_cand = m + 1;
+  } else {
+    h = row % p.Hq;
+    const int g = p.heads.gran[h];
+    n_cand = (p.kv_len + g - 1) / g;
+  }
+  const int k = budget_blocks(n_cand, p.heads.min_blocks[h], p.heads.ratio_q16[h]);
+  const int ns = min<int>(p.heads.n_sink[h], n_cand);
+  // forced: [0, ns) U [nl_lo, n_cand), the two ranges made disjoint
+  const int nl_lo = max(ns, n_cand - p.heads.n_local[h]);
+  const int n_forced = ns + (n_cand - nl_lo);
+  const int kk = k - n_forced;  // to pick among the others
+  int32_t* out = p.idx + (int64_t)row * p.kmax;
+  if (tid == 0) p.cnt[row] = k;
+  for (int i = k + tid; i < p.kmax; i += NT) out[i] = -1;
+
+  auto forced = [&](int n) { return n < ns || n >= nl_lo; };
+
+  if (kk <= 0 || k == n_cand) {
+    // nothing to rank: the forced set (k == |F|) or every candidate (k == n)
+    if (k == n_cand) {
+      for (int n = tid; n < n_cand; n += NT) out[n] = n;
+    } else {
+      for (int n = tid; n < n_cand; n += NT) {
+        if (n < ns) out[n] = n;
+        else if (n >= nl_lo) out[ns + (n - nl_lo)] = n;
+      }
+    }
+    return;
+  }
+
+  const float* srow = p.s + (int64_t)row * p.s_row;
+  uint32_t key[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int n = c * NT + tid;
+    key[c] = (n < n_cand && !forced(n)) ? ordered_key(srow[n]) : 0u;
+  }
+  // largest T with count(key >= T) >= kk, i.e. the kk-th largest key
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) c += key[i] >= cand ? 1u : 0u;
+    c = block_sum<NT>(c, red);
+    if (c >= (uint32_t)kk) {
+      T = cand;
+      if (c == (uint32_t)kk) break;  // exactly kk keys >= T: no tie to resolve
+    }
+  }
+  uint32_t gt = 0;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) gt += key[i] > T ? 1u : 0u;
+  gt = block_sum<NT>(gt, red);
+  const uint32_t ties_wanted = (uint32_t)kk - gt;
+  uint32_t pos = 0, ties_seen = 0;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    if (c * NT >= n_cand) break;
+    const int n = c * NT + tid;
+    const bool valid = n < n_cand;
+    const bool is_tie = valid && !forced(n) && key[c] == T;
+    uint32_t tie_before;
+    const uint32_t tie_tot = block_prefix<NT>(is_tie, tie_before, red);
+    const bool take = valid && (forced(n) || key[c] > T || (is_tie && ties_seen + tie_before < ties_wanted));
+    uint32_t before;
+    const uint32_t tot = block_prefix<NT>(take, before, red);
+    if (take) out[pos + before] = n;
+    pos += tot;
+    ties_seen += tie_tot;
+  }
+}
+
+// ---------------------------------------------------------------- decode scores
+// One workgroup scores rows_per_wg pooled blocks of one (batch, KV head,
+// granularity) against every scoring query head of that group and granularity.
+// 8 lanes share a pooled row (D/8 floats each); partial dots meet by xor-shuffle.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_scores_kernel(DecodeScoreParams p) {
+  constexpr int kLanes = 8;
+  constexpr int kPer = D / kLanes;  // floats per lane
+  const DecodeScoreJob& job = p.jobs[blockIdx.y];
+  const int bi = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int sub = tid % kLanes;
+  const int rloc = tid / kLanes;  // 32 rows per pass
+  const int nc = p.pool_nc[job.pool];
+  const float* kp = p.pooled + p.pool_off[job.pool] + ((int64_t)bi * p.Hkv + job.kvh) * nc * D;
+  float qv[8][kPer];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i >= job.n_heads) break;
+    const char* qrow = reinterpret_cast<const char*>(p.q) +
+                       (bi * p.qs0 + job.heads[i] * p.qs1) * (int64_t)sizeof(T);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int d = sub * kPer + e;
+      if constexpr (sizeof(T) == 2)
+        qv[i][e] = bf16_to_f32(reinterpret_cast<const bf16_t*>(qrow)[d]);
+      else
+        qv[i][e] = reinterpret_cast<const float*>(qrow)[d];
+    }
+  }
+  const int r0 = blockIdx.x * p.rows_per_wg;
+  const int r1 = min(nc, r0 + p.rows_per_wg);
+  // the 8 lanes of a row always take the same trip count, so the xor-shuffles
+  // below stay inside active lane groups
+  for (int r = r0 + rloc; r < r1; r += 256 / kLanes) {
+    float kv[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; e += 4) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(kp + (int64_t)r * D + sub * kPer + e);
+      kv[e] = w[0];
+      kv[e + 1] = w[1];
+      kv[e + 2] = w[2];
+      kv[e + 3] = w[3];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i >= job.n_heads) break;
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc = fmaf(qv[i][e], kv[e], acc);
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      acc += __shfl_xor(acc, 4, 64);
+      if (sub == 0) p.s[((int64_t)bi * p.Hq + job.heads[i]) * p.nc_max + r] = acc * p.scale;
+    }
+  }
+}
+
+template <int NT, int CPT>
+hipError_t topk_launch(const TopkParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL((topk_kernel<NT, CPT>), dim3(p.rows), dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pool(const PoolParams& p, int dtype, int D, int batch, hipStream_t stream) {
+  dim3 grid((p.nb + p.blocks_per_wg - 1) / p.blocks_per_wg, p.heads, batch);
+  if (dtype == 0 && D == 128) hipLaunchKernelGGL((pool_kernel<bf16_t, 128>), grid, dim3(256), 0, stream, p);
+  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((pool_kernel<bf16_t, 64>), grid, dim3(256), 0, stream, p);
+  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((pool_kernel<float, 128>), grid, dim3(256), 0, stream, p);
+  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((pool_kernel<float, 64>), grid, dim3(256), 0, stream, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_scores(const PrefillScoreParams& p, int D, int batch, hipStream_t stream) {
+  const int t = (p.NB + 63) / 64;
+  dim3 grid(t, t, batch * p.Hq);
+  if (D == 128) hipLaunchKernelGGL((prefill_scores_kernel<128>), grid, dim3(256), 0, stream, p);
+  else if (D == 64) hipLaunchKernelGGL((prefill_scores_kernel<64>), grid, dim3(256), 0, stream, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkParams& p, int max_cand, hipStream_t stream) {
+  if (p.mode == 0) {
+    if (max_cand <= 64) return topk_launch<64, 1>(p, stream);
+    if (max_cand <= 128) return topk_launch<64, 2>(p, stream);
+    if (max_cand <= 256) return topk_launch<64, 4>(p, stream);
+    if (max_cand <= 512) return topk_launch<64, 8>(p, stream);
+    if (max_cand <= 1024) return topk_launch<64, 16>(p, stream);
+    if (max_cand <= 2048) return topk_launch<64, 32>(p, stream);
+    if (max_cand <= 4096) return topk_launch<256, 16>(p, stream);
+    if (max_cand <= 8192) return topk_launch<256, 32>(p, stream);
+  } else {
+    if (max_cand <= 256) return topk_launch<256, 1>(p, stream);
+    if (max_cand <= 1024) return topk_launch<256, 4>(p, stream);
+    if (max_cand <= 2048) return topk_launch<256, 8>(p, stream);
+    if (max_cand <= 4096) return topk_launch<256, 16>(p, stream);
+    if (max_cand <= 8192) return topk_launch<256, 32>(p, stream);
+    if (max_cand <= 16384) return topk_launch<256, 64>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_scores(const DecodeScoreParams& p, int dtype, int D, int batch, hipStream_t stream) {
+  int max_nc = 0;
+  for (int i = 0; i < 4; ++i) max_nc = max(max_nc, p.pool_nc[i]);
+  dim3 grid((max_nc + p.rows_per_wg - 1) / p.rows_per_wg, p.n_jobs, batch);
+  if (dtype == 0 && D == 128) hipLaunchKernelGGL((decode_scores_kernel<bf16_t, 128>), grid, dim3(256), 0, stream, p);
+  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((decode_scores_kernel<bf16_t, 64>), grid, dim3(256), 0, stream, p);
+  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((decode_scores_kernel<float, 128>), grid, dim3(256), 0, stream, p);
+  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((decode_scores_kernel<float, 64>), grid, dim3(256), 0, stream, p);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace sa

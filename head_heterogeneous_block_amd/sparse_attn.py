@@ -1,0 +1,315 @@
+"""ctypes binding of libsparse_attn.so (argument marshalling only).
+
+Each function has the name of the C entry point it calls and does no compute of
+its own: it turns torch tensors into device pointers, shapes into an
+``sa_attn_desc``, per-head budgets into ``sa_head_budget[]``, and passes the
+current HIP stream.  Every step of the method runs in the library's kernels.
+Importing this module fails loudly if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "or `python head_heterogeneous_block_amd/build.py`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP, SA_ERR_NO_DEVICE, SA_ERR_ARCH = \
+    0, -1, -2, -3, -4, -5, -6
+SA_BF16, SA_F32 = 0, 1
+MAX_HEADS = 128
+
+EXPORTED = [
+    "sa_version", "sa_last_error", "sa_lpt_schedule", "sa_prefill_block_counts", "sa_decode_block_counts",
+    "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
+    "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_decode_workspace_size", "sa_sparse_attn_decode",
+]
+
+
+class SaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sparse_attn status {status}: {msg}")
+        self.status = status
+
+
+class sa_attn_desc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("q_len", ctypes.c_int32), ("kv_len", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("kernel_variant", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3), ("v_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class sa_head_budget(ctypes.Structure):
+    _fields_ = [("min_blocks", ctypes.c_int32), ("ratio_q16", ctypes.c_uint32), ("n_sink", ctypes.c_int32),
+                ("n_local", ctypes.c_int32), ("granularity", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_descp = ctypes.POINTER(sa_attn_desc)
+_budp = ctypes.POINTER(sa_head_budget)
+
+_SIG = {
+    "sa_version": (ctypes.c_int32, []),
+    "sa_last_error": (ctypes.c_char_p, []),
+    "sa_lpt_schedule": (ctypes.c_int32, [_i64p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
+    "sa_prefill_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
+    "sa_decode_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
+    "sa_decode_pooled_size": (ctypes.c_size_t, [_descp, _budp]),
+    "sa_pool_keys_decode": (ctypes.c_int32, [_descp, _budp, _P, _P, _P]),
+    "sa_select_workspace_size": (ctypes.c_size_t, [_descp, _budp, ctypes.c_int32]),
+    "sa_select_blocks": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t,
+                                          _P]),
+    "sa_prefill_workspace_size": (ctypes.c_size_t, [_descp, ctypes.c_int32, ctypes.c_int32]),
+    "sa_sparse_attn_prefill": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+                                                ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+    "sa_decode_workspace_size": (ctypes.c_size_t, [_descp, _budp, ctypes.c_int32]),
+    "sa_sparse_attn_decode": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                               ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+}
+for _name, (_res, _args) in _SIG.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def _check(status: int) -> None:
+    if status != SA_OK:
+        raise SaError(status, _lib.sa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    if t.is_cuda:
+        return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    return None
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float32:
+        return SA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def make_budgets(budget: dict) -> ctypes.Array:
+    """``sa_head_budget[H]`` from a dict of per-head integer arrays
+    (min_blocks, ratio_q16, n_sink, n_local, granularity)."""
+    H = len(budget["min_blocks"])
+    arr = (sa_head_budget * H)()
+    for h in range(H):
+        arr[h].min_blocks = int(budget["min_blocks"][h])
+        arr[h].ratio_q16 = int(budget["ratio_q16"][h])
+        arr[h].n_sink = int(budget["n_sink"][h])
+        arr[h].n_local = int(budget["n_local"][h])
+        arr[h].granularity = int(budget["granularity"][h]) if "granularity" in budget else 0
+    return arr
+
+
+def make_prefill_desc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor], block: int,
+                      scale: float = 0.0, kernel_variant: int = 0) -> sa_attn_desc:
+    """Descriptor for q/o ``[b, Hq, S, D]`` and k/v ``[b, Hkv, S, D]`` (any strides
+    with a contiguous last axis)."""
+    b, hq, S, D = q.shape
+    d = sa_attn_desc()
+    d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim = b, hq, k.shape[1], D
+    d.q_len, d.kv_len, d.block_size, d.dtype = S, k.shape[2], block, _dtype_code(q)
+    d.softmax_scale, d.kernel_variant = scale, kernel_variant
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o if o is not None else q)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: last axis must be contiguous")
+        getattr(d, name)[:] = [t.stride(0), t.stride(1), t.stride(2)]
+    return d
+
+
+def make_decode_desc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optional[torch.Tensor],
+                     scale: float = 0.0) -> sa_attn_desc:
+    """Descriptor for q/o ``[b, Hq, D]`` and the KV cache k/v ``[b, Hkv, L, D]``."""
+    b, hq, D = q.shape
+    d = sa_attn_desc()
+    d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim = b, hq, k.shape[1], D
+    d.q_len, d.kv_len, d.block_size, d.dtype = 1, k.shape[2], 0, _dtype_code(q)
+    d.softmax_scale = scale
+    oo = o if o is not None else q
+    d.q_stride[:] = [q.stride(0), q.stride(1), 0]
+    d.o_stride[:] = [oo.stride(0), oo.stride(1), 0]
+    d.k_stride[:] = [k.stride(0), k.stride(1), k.stride(2)]
+    d.v_stride[:] = [v.stride(0), v.stride(1), v.stride(2)]
+    return d
+
+
+# ---------------------------------------------------------------- host calls
+
+
+def sa_version() -> int:
+    return int(_lib.sa_version())
+
+
+def sa_lpt_schedule(loads: Sequence[int], n_bins: int):
+    """Greedy longest-load-first placement (host).  Returns numpy
+    ``(bin_of_item, bin_offsets, items_by_bin, bin_load)``."""
+    ld = np.ascontiguousarray(np.asarray(loads, dtype=np.int64))
+    n = ld.size
+    bin_of = np.empty(n, np.int32)
+    off = np.empty(n_bins + 1 if n_bins > 0 else 1, np.int32)
+    items = np.empty(n, np.int32)
+    bl = np.empty(max(n_bins, 1), np.int64)
+    _check(_lib.sa_lpt_schedule(ld.ctypes.data_as(_i64p), n, n_bins, bin_of.ctypes.data_as(_i32p),
+                                off.ctypes.data_as(_i32p), items.ctypes.data_as(_i32p), bl.ctypes.data_as(_i64p)))
+    return bin_of, off, items, bl
+
+
+def sa_prefill_block_counts(desc: sa_attn_desc, budgets) -> tuple[np.ndarray, int]:
+    nb = -(-desc.q_len // desc.block_size)
+    counts = np.empty((desc.batch, desc.n_q_heads, nb), np.int32)
+    kmax = ctypes.c_int32(0)
+    _check(_lib.sa_prefill_block_counts(ctypes.byref(desc), budgets, counts.ctypes.data_as(_i32p),
+                                        ctypes.byref(kmax)))
+    return counts, int(kmax.value)
+
+
+def sa_decode_block_counts(desc: sa_attn_desc, budgets) -> tuple[np.ndarray, int]:
+    counts = np.empty(desc.n_q_heads, np.int32)
+    kmax = ctypes.c_int32(0)
+    _check(_lib.sa_decode_block_counts(ctypes.byref(desc), budgets, counts.ctypes.data_as(_i32p),
+                                       ctypes.byref(kmax)))
+    return counts, int(kmax.value)
+
+
+def sa_select_workspace_size(desc: sa_attn_desc, budgets, kmax: int) -> int:
+    return int(_lib.sa_select_workspace_size(ctypes.byref(desc), budgets, kmax))
+
+
+def sa_prefill_workspace_size(desc: sa_attn_desc, kmax: int, n_bins: int) -> int:
+    return int(_lib.sa_prefill_workspace_size(ctypes.byref(desc), kmax, n_bins))
+
+
+def sa_decode_workspace_size(desc: sa_attn_desc, budgets, kmax: int) -> int:
+    return int(_lib.sa_decode_workspace_size(ctypes.byref(desc), budgets, kmax))
+
+
+def sa_decode_pooled_size(desc: sa_attn_desc, budgets) -> int:
+    return int(_lib.sa_decode_pooled_size(ctypes.byref(desc), budgets))
+
+
+# ---------------------------------------------------------------- device calls
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def sa_pool_keys_decode(desc: sa_attn_desc, budgets, k: torch.Tensor, k_pooled: torch.Tensor) -> None:
+    _check(_lib.sa_pool_keys_decode(ctypes.byref(desc), budgets, _ptr(k), _ptr(k_pooled), _stream(k)))
+
+
+def sa_select_blocks(desc: sa_attn_desc, budgets, q: torch.Tensor, k: torch.Tensor,
+                     k_pooled: Optional[torch.Tensor], block_idx: torch.Tensor, block_cnt: torch.Tensor,
+                     kmax: int, workspace: torch.Tensor) -> None:
+    _check(_lib.sa_select_blocks(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(k_pooled), _ptr(block_idx),
+                                 _ptr(block_cnt), kmax, _ptr(workspace), workspace.numel(), _stream(q)))
+
+
+def sa_sparse_attn_prefill(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
+                           bin_offsets=None, items_by_bin=None, n_bins: int = 0, out_f32: bool = False,
+                           workspace: Optional[torch.Tensor] = None) -> None:
+    ws = workspace
+    _check(_lib.sa_sparse_attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       _ptr(block_idx), _ptr(block_cnt), kmax, _ptr(bin_offsets),
+                                       _ptr(items_by_bin), n_bins, 1 if out_f32 else 0, _ptr(ws),
+                                       0 if ws is None else ws.numel(), _stream(q)))
+
+
+def sa_sparse_attn_decode(desc: sa_attn_desc, budgets, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
+                          workspace: torch.Tensor, out_f32: bool = False) -> None:
+    _check(_lib.sa_sparse_attn_decode(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      _ptr(block_idx), _ptr(block_cnt), kmax, 1 if out_f32 else 0, _ptr(workspace),
+                                      workspace.numel(), _stream(q)))
+
+
+# ---------------------------------------------------------------- conveniences
+# (allocation + the calls above, in order; still no compute outside the library)
+
+
+class PrefillPlan:
+    """Everything a prefill layer needs that depends only on shapes and budgets:
+    descriptor, per-head budgets, block counts (LPT loads), kmax and the LPT
+    schedule over ``n_bins`` persistent workgroups (uploaded to the device)."""
+
+    def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
+                 kernel_variant: int = 0):
+        self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
+        self.budgets = make_budgets(budget)
+        self.counts, self.kmax = sa_prefill_block_counts(self.desc, self.budgets)
+        self.block = block
+        self.n_bins = n_bins
+        self.out_f32 = out_f32
+        dev = q.device
+        self.nb = -(-q.shape[2] // block)
+        self.block_idx = torch.empty((q.shape[0], q.shape[1], self.nb, self.kmax), dtype=torch.int32, device=dev)
+        self.block_cnt = torch.empty((q.shape[0], q.shape[1], self.nb), dtype=torch.int32, device=dev)
+        self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
+        if n_bins > 0:
+            _, off, items, load = sa_lpt_schedule(self.counts.reshape(-1), n_bins)
+            self.bin_load = load
+            self.bin_offsets = torch.from_numpy(off).to(dev)
+            self.items_by_bin = torch.from_numpy(items).to(dev)
+        else:
+            self.bin_load = None
+            self.bin_offsets = self.items_by_bin = None
+
+    def select(self, q, k) -> None:
+        sa_select_blocks(self.desc, self.budgets, q, k, None, self.block_idx, self.block_cnt, self.kmax,
+                         self.select_ws)
+
+    def attend(self, q, k, v, o, lse=None) -> None:
+        sa_sparse_attn_prefill(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
+                               self.bin_offsets, self.items_by_bin, self.n_bins, self.out_f32)
+
+
+class DecodePlan:
+    """Descriptor, budgets, kmax, index buffers and workspaces for one decode
+    shape; ``pool`` builds the pooled-key cache once per KV cache."""
+
+    def __init__(self, q, k, v, budget: dict, out_f32: bool = False):
+        self.desc = make_decode_desc(q, k, v, q)
+        self.budgets = make_budgets(budget)
+        self.counts, self.kmax = sa_decode_block_counts(self.desc, self.budgets)
+        self.out_f32 = out_f32
+        dev = q.device
+        self.block_idx = torch.empty((q.shape[0], q.shape[1], self.kmax), dtype=torch.int32, device=dev)
+        self.block_cnt = torch.empty((q.shape[0], q.shape[1]), dtype=torch.int32, device=dev)
+        self.k_pooled = torch.empty(max(sa_decode_pooled_size(self.desc, self.budgets) // 4, 4),
+                                    dtype=torch.float32, device=dev)
+        self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
+        self.attn_ws = _workspace(sa_decode_workspace_size(self.desc, self.budgets, self.kmax), dev)
+
+    def pool(self, k) -> None:
+        sa_pool_keys_decode(self.desc, self.budgets, k, self.k_pooled)
+
+    def select(self, q, k) -> None:
+        sa_select_blocks(self.desc, self.budgets, q, k, self.k_pooled, self.block_idx, self.block_cnt, self.kmax,
+                         self.select_ws)
+
+    def attend(self, q, k, v, o, lse=None) -> None:
+        sa_sparse_attn_decode(self.desc, self.budgets, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
+                              self.attn_ws, self.out_f32)

@@ -1,0 +1,213 @@
+/*
+ * sparse_attn.h -- C ABI of the per-head heterogeneous block-sparse attention
+ * library for AMD MI355X (gfx950).  libsparse_attn.so exports exactly the
+ * functions declared here.
+ *
+ * The operations (gist.science technical summaries):
+ *   - select_blocks: mean-pool keys (and query blocks) into blocks, score every
+ *     (head, query block) against the pooled keys and keep a per-head budget of
+ *     top-scoring key blocks, sink and local blocks always kept.  Per-head
+ *     budgets: "S-HPLB: Efficient LLM Attention Serving via Sparsity-Aware Head
+ *     Parallelism Load Balance", Italian summary §2.A and Chinese summary §2.1;
+ *     top-k sparse attention: same pages §1; block granularity and
+ *     streaming/retrieval heads: "Fluxion", Italian summary, Intuizioni Chiave
+ *     1-2; Index/Select operations: "Unifying Sparse Attention with
+ *     Hierarchical Memory for Scalable Long-Context LLM Serving" (Spin),
+ *     Spanish summary §2.A.
+ *   - lpt_schedule: greedy longest-load-first placement of work items on bins
+ *     (S-HPLB, Italian summary §2.B, Chinese summary §2.2).  On one GPU the
+ *     items are (head, query-block) tiles and the bins are the persistent
+ *     workgroups of the prefill kernel.
+ *   - sparse_attn_prefill / sparse_attn_decode: exact softmax attention of every
+ *     query over the keys of its selected blocks only (causal for prefill), with
+ *     grouped-query (GQA) heads sharing one KV head ("Fluxion", Componenti di
+ *     Sistema: GQA handled at KV-group level).
+ *
+ * Conventions
+ *   - "[dev]" pointers are HIP device memory owned by the caller; "[host]"
+ *     pointers are host memory owned by the caller.  The library never
+ *     allocates or frees caller-visible memory; scratch space is the caller's
+ *     workspace, sized by the *_workspace_size functions.
+ *   - Tensors are addressed as base + b*stride[0] + h*stride[1] + t*stride[2] + d
+ *     (strides in elements; the head_dim axis is contiguous).
+ *   - GQA: query head h reads KV head h / (n_q_heads / n_kv_heads).
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns after enqueueing.  Faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - Every function validates all arguments before enqueueing anything: on
+ *     error nothing is launched, a negative sa_status is returned and
+ *     sa_last_error() describes it.
+ *   - Thread safety: calls are reentrant; the error text is per thread.  Calls
+ *     that share a workspace must be ordered on one stream.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sa_status;
+enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = -1, /* bad shape, pointer, budget or size */
+  SA_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim, block, dtype, limits) */
+  SA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than *_workspace_size */
+  SA_ERR_HIP = -4,         /* a HIP runtime call failed (name in sa_last_error) */
+  SA_ERR_NO_DEVICE = -5,   /* no HIP device visible */
+  SA_ERR_ARCH = -6         /* current device is not gfx950 */
+};
+
+enum { SA_BF16 = 0, SA_F32 = 1 };
+
+#define SA_MAX_HEADS 128
+
+/* Shape of one attention call.
+ *   prefill: q_len == kv_len (causal self-attention, both start at token 0);
+ *            block_size is the query/key block (64 or 128).
+ *   decode:  q_len == 1; the query is the token at position kv_len-1 and sees
+ *            all kv_len cached tokens; block_size is ignored (each head has its
+ *            own granularity in sa_head_budget).
+ * head_dim: 64 or 128.  dtype: SA_BF16 or SA_F32 for Q/K/V.
+ * softmax_scale: 0 means 1/sqrt(head_dim).  kernel_variant: see the field.
+ * Strides: prefill q/o [batch][n_q_heads][q_len][head_dim], k/v
+ * [batch][n_kv_heads][kv_len][head_dim]; decode q/o use stride[2] unused
+ * ([batch][n_q_heads][head_dim]). */
+typedef struct {
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  int32_t q_len, kv_len;
+  int32_t block_size;
+  int32_t dtype;
+  float softmax_scale;
+  int32_t kernel_variant; /* prefill attention workgroup shape: 0 = default,
+                             2 = 2 waves x B/2 queries, 4 = 4 waves x B/4 queries
+                             (bf16, block 128 only); results are identical */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+} sa_attn_desc;
+
+/* Budget of one query head (one entry per query head, [host]).
+ * A row with n candidate blocks keeps
+ *   k = min(n, max(min_blocks, ceil(ratio_q16 * n / 65536)))
+ * blocks (exact integer arithmetic): the first n_sink and last n_local
+ * candidates always, the rest by descending score, ties to the lower block
+ * index.  Candidates: prefill row m sees blocks 0..m; a decode head sees
+ * ceil(kv_len / granularity) blocks.  Requires 1 <= min_blocks and
+ * n_sink + n_local <= min_blocks.  granularity: decode tokens per block
+ * (16, 32, 64 or 128; ignored in prefill). */
+typedef struct {
+  int32_t min_blocks;
+  uint32_t ratio_q16;
+  int32_t n_sink, n_local;
+  int32_t granularity;
+} sa_head_budget;
+
+int32_t sa_version(void);
+/* Text of the last error on the calling thread ("" if none).  Valid until the
+ * next call on this thread. */
+const char* sa_last_error(void);
+
+/* ---------------------------------------------------------------- host-only */
+
+/* Greedy longest-load-first placement (host, synchronous, O(n log n + n log
+ * n_bins)).  Items are taken by load, largest first, ties to the lower item
+ * index; each goes to the bin with the least load so far, ties to the lower
+ * bin index.
+ *   loads[n_items]           [host] non-negative
+ *   bin_of_item[n_items]     [host] out: bin of each item
+ *   bin_offsets[n_bins+1]    [host] out: CSR offsets into items_by_bin
+ *   items_by_bin[n_items]    [host] out: items of bin b, in assignment order,
+ *                            at [bin_offsets[b], bin_offsets[b+1])
+ *   bin_load[n_bins]         [host] out: total load per bin (may be NULL)
+ * n_items >= 0, n_bins >= 1; a negative load is SA_ERR_INVALID_ARG. */
+sa_status sa_lpt_schedule(const int64_t* loads, int32_t n_items, int32_t n_bins,
+                          int32_t* bin_of_item, int32_t* bin_offsets, int32_t* items_by_bin,
+                          int64_t* bin_load);
+
+/* Blocks kept per prefill row, from the budget rule alone (no data needed):
+ * counts[b][h][m] for m < ceil(q_len/block_size) ([host] out, int32), and the
+ * maximum over all rows in *kmax ([host] out, may be NULL).  These are the
+ * item loads for sa_lpt_schedule (item = (b*n_q_heads + h)*n_blocks + m). */
+sa_status sa_prefill_block_counts(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                                  int32_t* counts, int32_t* kmax);
+
+/* Blocks kept per decode head (counts[h], [host] out) and their maximum. */
+sa_status sa_decode_block_counts(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                                 int32_t* counts, int32_t* kmax);
+
+/* ---------------------------------------------------------------- selection */
+
+/* Bytes of fp32 pooled keys the decode selection reads: one array
+ * [batch][n_kv_heads][ceil(kv_len/g)][head_dim] per distinct granularity g of
+ * the heads that score (heads whose budget exceeds their forced blocks),
+ * concatenated in ascending g. */
+size_t sa_decode_pooled_size(const sa_attn_desc* desc, const sa_head_budget* budgets);
+
+/* Build the decode pooled-key cache described above from k [dev] into
+ * k_pooled [dev] (mean of each block's key rows in fp32; a short last block is
+ * averaged over the rows it has). */
+sa_status sa_pool_keys_decode(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                              const void* k, float* k_pooled, void* stream);
+
+size_t sa_select_workspace_size(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                                int32_t kmax);
+
+/* Top-k block selection.
+ * prefill (q_len == kv_len): pools Q and K into fp32 block means (workspace),
+ *   scores s[h][m][n] = scale * <Qbar[h][m], Kbar[h/G][n]> for n <= m, selects.
+ *   k_pooled must be NULL.
+ * decode (q_len == 1): scores s[h][n] = scale * <q[h], Kbar_g[h/G][n]> against
+ *   the pooled-key cache k_pooled [dev] from sa_pool_keys_decode (NULL: pool
+ *   from k into the workspace first).
+ * Outputs [dev]: block_idx int32, prefill [batch][n_q_heads][n_blocks][kmax],
+ * decode [batch][n_q_heads][kmax]: the kept blocks in ascending order, -1
+ * padded; block_cnt int32 [batch][n_q_heads][n_blocks] (prefill) or
+ * [batch][n_q_heads] (decode).  kmax must be >= the largest count
+ * (sa_*_block_counts). */
+sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                           const void* q, const void* k, const float* k_pooled,
+                           int32_t* block_idx, int32_t* block_cnt, int32_t kmax,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- attention */
+
+size_t sa_prefill_workspace_size(const sa_attn_desc* desc, int32_t kmax, int32_t n_bins);
+
+/* Causal block-sparse prefill attention.  Row t of query block m of head h
+ * attends to keys t' <= t of the blocks block_idx[b][h][m][0..block_cnt-1] of
+ * KV head h/G: o = softmax(scale * q k^T) v over those keys.
+ *   q, k, v [dev] dtype desc->dtype; o [dev] fp32 if out_f32 else desc->dtype;
+ *   lse [dev] fp32 [batch][n_q_heads][q_len] natural-log sum-exp (may be NULL).
+ *   Schedule: bin_offsets [dev] (n_bins+1) and items_by_bin [dev] from
+ *   sa_lpt_schedule over the tiles item = (b*n_q_heads + h)*n_blocks + m; one
+ *   persistent workgroup walks each bin.  NULL schedule = one workgroup per tile
+ *   in natural order (n_bins ignored).  Every tile must appear exactly once. */
+sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k,
+                                 const void* v, void* o, float* lse, const int32_t* block_idx,
+                                 const int32_t* block_cnt, int32_t kmax,
+                                 const int32_t* bin_offsets, const int32_t* items_by_bin,
+                                 int32_t n_bins, int32_t out_f32, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+size_t sa_decode_workspace_size(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                                int32_t kmax);
+
+/* Block-sparse decode attention: the query of head h attends to the tokens of
+ * its selected blocks (granularity budgets[h].granularity) of KV head h/G.  The
+ * KV tokens of a group are read once for all its query heads (union of their
+ * selections, per-head masks).  q [dev] [batch][n_q_heads][head_dim]; k, v
+ * [dev] cache; o [dev] like q (fp32 if out_f32); lse [dev] fp32
+ * [batch][n_q_heads] (may be NULL). */
+sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                                const void* q, const void* k, const void* v, void* o,
+                                float* lse, const int32_t* block_idx, const int32_t* block_cnt,
+                                int32_t kmax, int32_t out_f32, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,166 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library loads, exports every function include/sparse_attn.h declares, and
+its host-only entry points agree with the oracle: the greedy longest-load-first
+schedule bit for bit, the per-row block counts of the budget rule exactly.
+Argument validation returns error codes before anything touches a device.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle as O
+from head_heterogeneous_block_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SA = pytest.importorskip("head_heterogeneous_block_amd.sparse_attn", reason="library not built")
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "sparse_attn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = _header_functions()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(SA.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(SA.EXPORTED) == names
+
+
+def test_version_and_error_text():
+    assert SA.sa_version() >= 10000
+    with pytest.raises(SA.SaError) as e:
+        SA.sa_lpt_schedule([1, 2], 0)
+    assert e.value.status == SA.SA_ERR_INVALID_ARG and "n_bins" in str(e.value)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_lpt_matches_oracle_bit_exact(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(0, 3000))
+    bins = int(rng.integers(1, 700))
+    loads = rng.integers(0, 50, size=n) if seed % 2 else np.exp(rng.uniform(0, 6, n)).astype(np.int64)
+    got = SA.sa_lpt_schedule(loads, bins)
+    ref = O.lpt_schedule(loads.tolist(), bins)
+    for g, r in zip(got, ref):
+        np.testing.assert_array_equal(g, r)
+
+
+def test_lpt_golden_and_negative_load():
+    _, off, items, load = SA.sa_lpt_schedule([31, 58, 81, 100], 2)
+    assert items.tolist() == [3, 0, 2, 1] and off.tolist() == [0, 2, 4] and load.tolist() == [131, 139]
+    with pytest.raises(SA.SaError):
+        SA.sa_lpt_schedule([3, -1], 2)
+
+
+def test_lpt_on_config_tile_loads():
+    """The tile loads of the 32K Llama-shaped workload scheduled onto 512 bins:
+    identical to the oracle, and the makespan within one item of the mean."""
+    spec = W.CONFIGS[1]
+    bud = W.prefill_budgets(spec, W.default_seed(1))
+    import torch
+    q = torch.empty((1, spec.n_q_heads, spec.seq_len, spec.head_dim), dtype=torch.bfloat16, device="meta")
+    k = torch.empty((1, spec.n_kv_heads, spec.seq_len, spec.head_dim), dtype=torch.bfloat16, device="meta")
+    desc = SA.make_prefill_desc(q, k, k, q, spec.block)
+    counts, kmax = SA.sa_prefill_block_counts(desc, SA.make_budgets(bud))
+    loads = counts.reshape(-1)
+    got = SA.sa_lpt_schedule(loads, 512)
+    ref = O.lpt_schedule(loads.tolist(), 512)
+    for g, r in zip(got, ref):
+        np.testing.assert_array_equal(g, r)
+    assert got[3].max() <= loads.sum() / 512 + loads.max()
+
+
+def test_block_counts_match_budget_rule():
+    import torch
+    for spec, seed in ((W.CONFIGS[0], 1000), (W.CONFIGS[2].with_(seq_len=8192 + 64), 7), (W.CONFIGS[3], 1003)):
+        bud = W.prefill_budgets(spec, seed)
+        q = torch.empty((1, spec.n_q_heads, spec.seq_len, spec.head_dim), device="meta",
+                        dtype=torch.float32 if spec.dtype == "f32" else torch.bfloat16)
+        k = torch.empty((1, spec.n_kv_heads, spec.seq_len, spec.head_dim), device="meta", dtype=q.dtype)
+        desc = SA.make_prefill_desc(q, k, k, q, spec.block)
+        counts, kmax = SA.sa_prefill_block_counts(desc, SA.make_budgets(bud))
+        for h in range(spec.n_q_heads):
+            ref = [O.budget_blocks(m + 1, bud["min_blocks"][h], bud["ratio_q16"][h]) for m in range(spec.n_blocks)]
+            assert counts[0, h].tolist() == ref
+        assert kmax == counts.max()
+    dspec = W.CONFIGS[4]
+    bud = W.decode_budgets(dspec, 1004)
+    q = torch.empty((dspec.batch, dspec.n_q_heads, dspec.head_dim), dtype=torch.bfloat16, device="meta")
+    k = torch.empty((dspec.batch, dspec.n_kv_heads, dspec.kv_len, dspec.head_dim), dtype=torch.bfloat16,
+                    device="meta")
+    desc = SA.make_decode_desc(q, k, k, q)
+    counts, kmax = SA.sa_decode_block_counts(desc, SA.make_budgets(bud))
+    for h in range(dspec.n_q_heads):
+        nc = -(-dspec.kv_len // int(bud["granularity"][h]))
+        assert counts[h] == O.budget_blocks(nc, bud["min_blocks"][h], bud["ratio_q16"][h])
+
+
+def _desc(**kw):
+    import torch
+    q = torch.empty((1, 4, 1024, 64), dtype=torch.bfloat16, device="meta")
+    k = torch.empty((1, 2, 1024, 64), dtype=torch.bfloat16, device="meta")
+    d = SA.make_prefill_desc(q, k, k, q, 64)
+    for key, val in kw.items():
+        setattr(d, key, val)
+    return d
+
+
+def _bud(**kw):
+    b = {"min_blocks": [2] * 4, "ratio_q16": [4096] * 4, "n_sink": [1] * 4, "n_local": [1] * 4,
+         "granularity": [64] * 4}
+    b.update(kw)
+    return SA.make_budgets(b)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), SA.SA_ERR_UNSUPPORTED),
+    (dict(n_kv_heads=3), SA.SA_ERR_INVALID_ARG),
+    (dict(block_size=32), SA.SA_ERR_UNSUPPORTED),
+    (dict(kv_len=512), SA.SA_ERR_INVALID_ARG),
+    (dict(dtype=7), SA.SA_ERR_INVALID_ARG),
+    (dict(kernel_variant=3), SA.SA_ERR_INVALID_ARG),
+    (dict(batch=0), SA.SA_ERR_INVALID_ARG),
+])
+def test_invalid_descriptors_rejected(kw, code):
+    with pytest.raises(SA.SaError) as e:
+        SA.sa_prefill_block_counts(_desc(**kw), _bud())
+    assert e.value.status == code
+
+
+@pytest.mark.parametrize("kw", [dict(min_blocks=[1] * 4), dict(n_sink=[-1] * 4), dict(ratio_q16=[70000] * 4),
+                                dict(min_blocks=[0] * 4, n_sink=[0] * 4, n_local=[0] * 4)])
+def test_invalid_budgets_rejected(kw):
+    with pytest.raises(SA.SaError) as e:
+        SA.sa_prefill_block_counts(_desc(), _bud(**kw))
+    assert e.value.status == SA.SA_ERR_INVALID_ARG
+
+
+def test_device_calls_fail_cleanly_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    d = _desc()
+    b = _bud()
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation and the device check come first
+    lib = SA._lib
+    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 64, fake, 1 << 30, None)
+    assert st in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
+    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 1, fake, 1 << 30, None)
+    assert st == SA.SA_ERR_INVALID_ARG  # kmax below the largest count, caught before the device check
+    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 64, fake, 16, None)
+    assert st == SA.SA_ERR_WORKSPACE
+    st = lib.sa_sparse_attn_prefill(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 16, None, None, 0, 0,
+                                    None, 0, None)
+    assert st in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
+    st = lib.sa_sparse_attn_prefill(ctypes.byref(d), ctypes.c_void_p(3), fake, fake, fake, None, fake, fake, 16,
+                                    None, None, 0, 0, None, 0, None)
+    assert st == SA.SA_ERR_INVALID_ARG  # misaligned q

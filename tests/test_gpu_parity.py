@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Bars: block indices bit-exact on every pinned row (score gap > 1e-4 relative,
+ties to the lowest index), valid on near-tie rows; LPT schedules bit-exact;
+attention max-abs error <= 1e-5 for fp32 inputs and <= 1e-2 for bf16 inputs
+(fp32 output), bf16 output within 1e-2 + half a bf16 ulp of the oracle value.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from head_heterogeneous_block_amd import workloads as W
+
+from gpu_helpers import (bf16_half_ulp, check_prefill_selection, check_row, max_abs, prefill_gpu, to_host)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from head_heterogeneous_block_amd import sparse_attn as SA  # noqa: E402  (fails loudly if not built)
+
+DEV = "cuda:0"
+TOL_F32 = 1e-5
+TOL_BF16 = 1e-2
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _bud_sub(budget, heads):
+    return {k: np.asarray(v)[heads] for k, v in budget.items()}
+
+
+# ---------------------------------------------------------------- prefill, all rows
+
+
+@pytest.mark.parametrize("schedule", ["natural", "lpt"])
+def test_prefill_config0_fp32_all_rows(schedule):
+    spec = W.CONFIGS[0]
+    inp = W.make_prefill(spec, W.default_seed(0), device=DEV)
+    _say("case: config0 fp32", schedule)
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=8 if schedule == "lpt" else 0)
+    q, k, v = to_host(inp)
+    oidx, ocnt, scores = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, return_scores=True)
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    pinned, exempt = check_prefill_selection(gidx, gcnt, oidx, ocnt, scores, inp.budget)
+    _say("pinned", pinned, "exempt", exempt)
+    assert pinned >= 0.9 * (pinned + exempt)
+    ro, rl = O.attention_prefill_gather(q, k, v, gidx, gcnt, spec.block)
+    err = max_abs(o.cpu().numpy(), ro)
+    lerr = max_abs(lse.cpu().numpy(), rl)
+    _say("max abs err o", err, "lse", lerr)
+    assert err <= TOL_F32 and lerr <= TOL_F32
+    if schedule == "lpt":
+        ref = O.lpt_schedule(plan.counts.reshape(-1).tolist(), 8)
+        np.testing.assert_array_equal(plan.bin_offsets.cpu().numpy(), ref[1])
+        np.testing.assert_array_equal(plan.items_by_bin.cpu().numpy(), ref[2])
+
+
+PREFILL_SHAPES = [
+    # name, overrides
+    ("llama-2k", dict(seq_len=2048, n_q_heads=8, n_kv_heads=2)),
+    ("llama-ragged", dict(seq_len=2000, n_q_heads=8, n_kv_heads=2)),
+    ("d64-b128", dict(seq_len=1536, n_q_heads=4, n_kv_heads=1, head_dim=64)),
+    ("b64", dict(seq_len=1500, n_q_heads=4, n_kv_heads=2, block=64)),
+    ("one-block", dict(seq_len=100, n_q_heads=2, n_kv_heads=1)),
+]
+
+
+@pytest.mark.parametrize("name,over", PREFILL_SHAPES, ids=[s[0] for s in PREFILL_SHAPES])
+@pytest.mark.parametrize("variant", [0, 2])
+def test_prefill_bf16_all_rows(name, over, variant):
+    spec = W.CONFIGS[1].with_(**over)
+    if variant == 2 and spec.block != 128:
+        pytest.skip("variant applies to block 128")
+    inp = W.make_prefill(spec, 77, device=DEV)
+    _say("case:", name, "variant", variant)
+    idx, cnt, o, lse, plan = prefill_gpu(inp, kernel_variant=variant)
+    q, k, v = to_host(inp)
+    oidx, ocnt, scores = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, return_scores=True)
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    pinned, exempt = check_prefill_selection(gidx, gcnt, oidx, ocnt, scores, inp.budget)
+    _say("pinned", pinned, "exempt", exempt)
+    ro, rl = O.attention_prefill_gather(q, k, v, gidx, gcnt, spec.block)
+    err = max_abs(o.cpu().numpy(), ro)
+    lerr = max_abs(lse.cpu().numpy(), rl)
+    _say("max abs err o", err, "lse", lerr)
+    assert err <= TOL_BF16 and lerr <= TOL_BF16
+
+
+def test_prefill_bf16_output_and_determinism():
+    spec = W.CONFIGS[1].with_(seq_len=2048 + 128, n_q_heads=8, n_kv_heads=2)
+    inp = W.make_prefill(spec, 5, device=DEV)
+    idx, cnt, o16, _, plan = prefill_gpu(inp, out_f32=False, with_lse=False)
+    q, k, v = to_host(inp)
+    ro, _ = O.attention_prefill_gather(q, k, v, idx.cpu().numpy(), cnt.cpu().numpy(), spec.block)
+    got = o16.float().cpu().numpy()
+    bound = TOL_BF16 + bf16_half_ulp(ro)
+    assert np.all(np.abs(got - ro) <= bound)
+    _, _, o16b, _, _ = prefill_gpu(inp, out_f32=False, with_lse=False)
+    assert torch.equal(o16, o16b), "two runs differ"
+
+
+def test_prefill_schedules_and_variants_bitwise_equal():
+    """Every tile is computed by one workgroup with the same arithmetic whatever
+    the schedule or workgroup shape: outputs must be identical bit for bit."""
+    spec = W.CONFIGS[1].with_(seq_len=4096, n_q_heads=8, n_kv_heads=2)
+    inp = W.make_prefill(spec, 9, device=DEV)
+    outs = []
+    for n_bins, var in ((0, 0), (64, 0), (512, 0), (0, 2), (97, 2)):
+        _say("schedule", n_bins, "variant", var)
+        _, _, o, lse, _ = prefill_gpu(inp, n_bins=n_bins, kernel_variant=var)
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+
+
+# ---------------------------------------------------------------- prefill, full sizes
+
+
+@pytest.mark.parametrize("which", [1, 2, 3])
+def test_prefill_full_size_sampled(which):
+    spec = W.CONFIGS[which]
+    _say("case: full config", which, spec.name)
+    inp = W.make_prefill(spec, W.default_seed(which), device=DEV)
+    n_bins = 512
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins)
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    np.testing.assert_array_equal(gcnt, plan.counts)
+    G = spec.group
+    nb = spec.n_blocks
+    heads = [0, spec.n_q_heads // 2 + 1, spec.n_q_heads - 1]
+    q, k, v = W.to_numpy(inp.q[:, heads]), None, None
+    kv_heads = [h // G for h in heads]
+    k = W.to_numpy(inp.k[:, kv_heads])
+    vv = W.to_numpy(inp.v[:, kv_heads])
+    # selection of the sampled heads, every row (each head paired with its own KV head)
+    for i, h in enumerate(heads):
+        sub = _bud_sub(inp.budget, [h])
+        oidx, ocnt, sc = O.select_blocks_prefill(q[:, [i]], k[:, [i]], sub, spec.block, kmax=plan.kmax,
+                                                 return_scores=True)
+        pinned, exempt = check_prefill_selection(gidx[:, [h]], gcnt[:, [h]], oidx, ocnt, sc, sub)
+        _say("head", h, "pinned", pinned, "exempt", exempt)
+        assert pinned >= 0.9 * (pinned + exempt)
+    # attention on sampled tiles, oracle over the GPU's block lists
+    rng = np.random.default_rng(which)
+    ms = sorted(set([0, 1, nb - 1] + rng.integers(0, nb, 5).tolist()))
+    tiles = [(0, i, m) for i in range(len(heads)) for m in ms]
+    sub_idx = gidx[:, heads]
+    sub_cnt = gcnt[:, heads]
+    ro, rl = O.attention_prefill_gather(q, k, vv, sub_idx, sub_cnt, spec.block, tiles=tiles)
+    og = o[:, heads].cpu().numpy()
+    lg = lse[:, heads].cpu().numpy()
+    worst = 0.0
+    for (bi, i, m) in tiles:
+        rows = slice(m * spec.block, min(spec.seq_len, (m + 1) * spec.block))
+        worst = max(worst, max_abs(og[bi, i, rows], ro[bi, i, rows]), max_abs(lg[bi, i, rows], rl[bi, i, rows]))
+    _say("max abs err over", len(tiles), "tiles:", worst)
+    assert worst <= TOL_BF16
+    assert torch.isfinite(o).all()
+
+
+# ---------------------------------------------------------------- decode
+
+
+def _decode_gpu(inp, out_f32=True):
+    q, k, v = inp.q, inp.k, inp.v
+    plan = SA.DecodePlan(q, k, v, inp.budget, out_f32=out_f32)
+    o = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    plan.pool(k)
+    plan.select(q, k)
+    plan.attend(q, k, v, o, lse)
+    torch.cuda.synchronize()
+    return plan, o, lse
+
+
+def _check_decode(inp, plan, o, lse, seqs):
+    spec = inp.spec
+    gidx, gcnt = plan.block_idx.cpu().numpy(), plan.block_cnt.cpu().numpy()
+    np.testing.assert_array_equal(gcnt, np.broadcast_to(plan.counts, gcnt.shape))
+    q = W.to_numpy(inp.q[seqs])
+    k = W.to_numpy(inp.k[seqs])
+    v = W.to_numpy(inp.v[seqs])
+    oidx, ocnt, sc = O.decode_select(q, k, inp.budget, kmax=plan.kmax, return_scores=True)
+    pinned = exempt = 0
+    for i, bi in enumerate(seqs):
+        for h in range(spec.n_q_heads):
+            g = int(inp.budget["granularity"][h])
+            nc = -(-spec.kv_len // g)
+            c = int(ocnt[i, h])
+            assert int(gcnt[bi, h]) == c
+            F = O.forced_blocks(nc, int(inp.budget["n_sink"][h]), int(inp.budget["n_local"][h]))
+            if check_row(gidx[bi, h, :c], oidx[i, h, :c], sc[i, h], c, F):
+                pinned += 1
+            else:
+                exempt += 1
+    _say("decode pinned", pinned, "exempt", exempt)
+    ro, rl = O.decode_attention(q, k, v, gidx[seqs], gcnt[seqs], inp.budget["granularity"])
+    err = max_abs(o[seqs].cpu().numpy(), ro)
+    lerr = max_abs(lse[seqs].cpu().numpy(), rl)
+    _say("decode max abs err o", err, "lse", lerr)
+    assert err <= TOL_BF16 and lerr <= TOL_BF16
+
+
+@pytest.mark.parametrize("L", [8192, 8192 + 40, 1000])
+def test_decode_reduced_all(L):
+    spec = W.CONFIGS[4].with_(batch=3, kv_len=L, tok_lo=256, tok_hi=2048, stream_local=16)
+    _say("case: decode L", L)
+    inp = W.make_decode(spec, 31, device=DEV)
+    plan, o, lse = _decode_gpu(inp)
+    _check_decode(inp, plan, o, lse, list(range(spec.batch)))
+
+
+def test_decode_gqa8_fp32():
+    spec = W.CONFIGS[4].with_(dtype="f32", batch=2, n_q_heads=16, n_kv_heads=2, kv_len=4096, tok_lo=256,
+                              tok_hi=1024, stream_local=8, n_streaming=4)
+    inp = W.make_decode(spec, 32, device=DEV)
+    plan, o, lse = _decode_gpu(inp)
+    _check_decode(inp, plan, o, lse, [0, 1])
+
+
+def test_decode_full_size_sampled():
+    spec = W.CONFIGS[4]
+    _say("case: full decode config")
+    inp = W.make_decode(spec, W.default_seed(4), device=DEV)
+    plan, o, lse = _decode_gpu(inp)
+    _check_decode(inp, plan, o, lse, [0, 9])
+    assert torch.isfinite(o).all()
+    # determinism: a second step is bitwise identical
+    o2 = torch.empty_like(o)
+    plan.select(inp.q, inp.k)
+    plan.attend(inp.q, inp.k, inp.v, o2)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
