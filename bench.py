@@ -39,7 +39,6 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--prefill-config", type=int, default=2)
     ap.add_argument("--decode-config", type=int, default=4)
-    ap.add_argument("--variant", type=int, default=0, help="prefill kernel_variant (0 default, 2, 4)")
     ap.add_argument("--bins-per-cu", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
@@ -148,7 +147,7 @@ def main():
     print(f"[bench] prefill inputs {pspec.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     n_bins = n_cu * args.bins_per_cu
     t0 = time.perf_counter()
-    plan = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, kernel_variant=args.variant)
+    plan = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins)
     lpt_ms = (time.perf_counter() - t0) * 1e3
     o = torch.empty_like(pin.q)
     sel = lambda: plan.select(pin.q, pin.k)  # noqa: E731
@@ -156,15 +155,16 @@ def main():
 
     # ---------------------------------------------------------------- decode
     dspec = W.CONFIGS[args.decode_config]
-    t0 = time.time()
-    din = W.make_decode(dspec, W.default_seed(args.decode_config), device=dev)
-    dplan = SA.DecodePlan(din.q, din.k, din.v, din.budget)
-    dplan.pool(din.k)
-    do = torch.empty_like(din.q)
-    torch.cuda.synchronize()
-    print(f"[bench] decode inputs {dspec.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    dsel = lambda: dplan.select(din.q, din.k)  # noqa: E731
-    datt = lambda: dplan.attend(din.q, din.k, din.v, do)  # noqa: E731
+    if args.only in ("decode", "all"):
+        t0 = time.time()
+        din = W.make_decode(dspec, W.default_seed(args.decode_config), device=dev)
+        dplan = SA.DecodePlan(din.q, din.k, din.v, din.budget)
+        dplan.pool(din.k)
+        do = torch.empty_like(din.q)
+        torch.cuda.synchronize()
+        print(f"[bench] decode inputs {dspec.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+        dsel = lambda: dplan.select(din.q, din.k)  # noqa: E731
+        datt = lambda: dplan.attend(din.q, din.k, din.v, do)  # noqa: E731
 
     def step():
         if args.only in ("prefill", "all"):
@@ -201,14 +201,16 @@ def main():
     bidx = plan.block_idx.cpu().numpy()
     bcnt = plan.block_cnt.cpu().numpy()
     flops = M.prefill_flops(bidx, bcnt, pspec.seq_len, pspec.block, pspec.head_dim)
-    dbidx = dplan.block_idx.cpu().numpy()
-    dbcnt = dplan.block_cnt.cpu().numpy()
-    nc = [-(-dspec.kv_len // int(g)) for g in din.budget["granularity"]]
-    scoring = [int(dplan.counts[h]) > len(range(min(int(din.budget["n_sink"][h]), nc[h]))) +
-               min(int(din.budget["n_local"][h]), nc[h]) and int(dplan.counts[h]) < nc[h]
-               for h in range(dspec.n_q_heads)]
-    dbytes = M.decode_bytes(dbidx, dbcnt, din.budget["granularity"], dspec.n_q_heads, dspec.n_kv_heads,
-                            dspec.kv_len, dspec.head_dim, 2, scoring)
+    dbytes = {"total": 0}
+    if args.only in ("decode", "all"):
+        dbidx = dplan.block_idx.cpu().numpy()
+        dbcnt = dplan.block_cnt.cpu().numpy()
+        nc = [-(-dspec.kv_len // int(g)) for g in din.budget["granularity"]]
+        scoring = [int(dplan.counts[h]) > len(range(min(int(din.budget["n_sink"][h]), nc[h]))) +
+                   min(int(din.budget["n_local"][h]), nc[h]) and int(dplan.counts[h]) < nc[h]
+                   for h in range(dspec.n_q_heads)]
+        dbytes = M.decode_bytes(dbidx, dbcnt, din.budget["granularity"], dspec.n_q_heads, dspec.n_kv_heads,
+                                dspec.kv_len, dspec.head_dim, 2, scoring)
 
     prefill_ms = res.get("sel_ms", 0.0) + res.get("att_ms", 0.0)
     tflops = flops / (res["att_mean_ms"] * 1e-3) / 1e12 if "att_ms" in res else None
@@ -230,14 +232,14 @@ def main():
 
     ablation = {}
     if not args.no_ablation and args.only in ("prefill", "all"):
-        nat = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=0, kernel_variant=args.variant)
+        nat = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=0)
         nat.block_idx.copy_(plan.block_idx)
         nat.block_cnt.copy_(plan.block_cnt)
         ablation["natural_order_grid_ms"] = timed(lambda: nat.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
         # persistent bins in natural (contiguous) order: tiles split evenly by count
         n_t = plan.counts.size
         offs = np.linspace(0, n_t, n_bins + 1).astype(np.int32)
-        cont = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=0, kernel_variant=args.variant)
+        cont = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=0)
         cont.block_idx = plan.block_idx
         cont.block_cnt = plan.block_cnt
         cont.bin_offsets = torch.from_numpy(offs).to(dev)
@@ -286,7 +288,7 @@ def main():
                                f"Hkv={pspec.n_kv_heads}, D={pspec.head_dim}, block={pspec.block}) + decode "
                                f"{dspec.name} (batch={dspec.batch}, L={dspec.kv_len})",
                    "global_batch": 1, "seq_len": pspec.seq_len, "parallelism": "single GPU",
-                   "lpt_bins": n_bins, "kernel_variant": args.variant},
+                   "lpt_bins": n_bins},
         "prefill": {"select_ms": res.get("sel_ms"), "attention_ms": res.get("att_ms"),
                     "attended_tflops": tflops, "attended_flops": flops,
                     "mfma_frac": roofline["frac"], "lpt_host_ms": lpt_ms},

@@ -89,10 +89,7 @@ sa_status check_desc(const sa_attn_desc* d, bool prefill) {
   if (d->kv_len < 1) return fail(SA_ERR_INVALID_ARG, "kv_len %d", d->kv_len);
   if (!(d->softmax_scale >= 0.f) || std::isinf(d->softmax_scale))
     return fail(SA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-  if (d->kernel_variant != 0 && d->kernel_variant != 2 && d->kernel_variant != 4)
-    return fail(SA_ERR_INVALID_ARG, "kernel_variant %d (0, 2 or 4)", d->kernel_variant);
-  if (d->kernel_variant == 4 && (d->dtype != SA_BF16 || d->block_size != 128))
-    return fail(SA_ERR_UNSUPPORTED, "kernel_variant 4 needs bf16 and block_size 128");
+  if (d->kernel_variant != 0) return fail(SA_ERR_INVALID_ARG, "kernel_variant %d (must be 0)", d->kernel_variant);
   if (prefill) {
     if (d->q_len != d->kv_len) return fail(SA_ERR_INVALID_ARG, "prefill needs q_len == kv_len");
     if (d->block_size != 64 && d->block_size != 128)
@@ -547,8 +544,8 @@ sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const 
   if (n_tiles > (1ll << 30)) return fail(SA_ERR_UNSUPPORTED, "too many tiles");
   {
     const int64_t es = elem_size(desc->dtype);
-    if (int64_t(desc->kv_len) * desc->k_stride[2] * es >= (1ll << 31) ||
-        int64_t(desc->kv_len) * desc->v_stride[2] * es >= (1ll << 31))
+    if (int64_t(desc->kv_len + 256) * desc->k_stride[2] * es >= (1ll << 31) ||
+        int64_t(desc->kv_len + 256) * desc->v_stride[2] * es >= (1ll << 31))
       return fail(SA_ERR_UNSUPPORTED, "one (batch, KV head) slice of K or V must span < 2 GiB");
   }
   if ((s = check_device())) return s;
@@ -583,11 +580,7 @@ sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const 
   p.scale_log2 = scale_of(desc) * 1.4426950408889634f;
   p.out_f32 = out_f32 ? 1 : 0;
   const int grid = bin_offsets ? n_bins : int(n_tiles);
-  // default: 4 waves x 32 queries (two waves per SIMD) where built, else 2 x B/2
-  const bool four = desc->dtype == SA_BF16 && desc->block_size == 128;
-  const int waves = desc->kernel_variant != 0 ? desc->kernel_variant : (four ? 4 : 2);
-  hipError_t e =
-      sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, waves, grid, (hipStream_t)stream);
+  hipError_t e = sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, grid, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
   return ok();
 }

@@ -89,8 +89,8 @@ struct PrefillParams {
   float scale_log2;
   int out_f32;
 };
-// waves: workgroup size in waves (2 or 4); the tile's B queries are split over them
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int waves, int grid, hipStream_t stream);
+// workgroup of B/32 waves, 32 queries each; grid = persistent bins or tiles
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int grid, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode attention
 // Union of the selected 16-token atoms of the query heads of one KV group.

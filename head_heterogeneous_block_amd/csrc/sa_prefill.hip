@@ -11,32 +11,34 @@
 //
 // Work decomposition
 //   tile      = (batch b, query head h, query block m): B query rows.
-//   workgroup = W waves; wave w owns query rows [w*B/W, (w+1)*B/W) of the tile.
+//   workgroup = B/32 waves; wave w owns query rows [32w, 32w+32) of the tile.
 //   step      = 64 keys of one selected key block (B/64 steps per block).
-//   K and V of a step are gathered from HBM through the block-index table with
-//   buffer loads (the (batch, KV head) slice is the buffer, so rows past the
-//   end of the sequence read as zero), double-buffered in LDS (K row-major, V
-//   transposed) and XOR-swizzled so that the 16-byte LDS reads of the MFMA
-//   operands do not conflict.  While step s is computed from one stage, step
-//   s+1 is fetched: K first, V once Q K^T of step s is done.
+//   Every step's K and V rows are gathered through the block-index table with
+//   buffer loads straight into LDS (buffer_load_dwordx4 ... lds: no registers;
+//   the (batch, KV head) slice is the buffer, so rows past the sequence end
+//   read as zero).  K and V live in two-slot LDS rings; K runs one step ahead
+//   of V.  Iteration i, after one barrier, fetches K(i+2) and V(i+1), computes
+//   S(i+1) = K(i+1) Q^T on the MFMA pipe while the VALU turns S(i) into P(i),
+//   then accumulates O += P(i) V(i).
 //
-// Math per step and wave (bf16 path):
-//   S^T[key][q] = K Q^T    v_mfma_f32_32x32x16_bf16, A = K rows (LDS),
-//                          B = Q^T (registers, loaded once per tile).
-//   With S transposed every lane column is one query, so the row max and row
-//   sum of the online softmax are in-lane plus one exchange between the two
-//   half-waves.
-//   O^T[d][q] += V^T P^T   A = V^T rows (LDS), B = P^T straight from the S^T
-//                          accumulators.  For that, key rows are stored in LDS
-//                          with bits 2 and 3 of the key index swapped: the
-//                          accumulator element i of a lane then holds key
-//                          16*(i/8) + 8*half + i%8, i.e. 8 consecutive keys per
-//                          16-key chunk, which is the B-operand layout.
-//   fp32 path: v_mfma_f32_32x32x2f32 with the same layouts, P kept in fp32.
-// Softmax: scores stay unscaled; exp2(s*c - m) with c = scale*log2(e) is one
-// FMA and one v_exp_f32.  The running max m is only raised when a new score
-// exceeds it by more than 2^kLazy (then O and l are rescaled, decided per wave),
-// so p <= 2^kLazy; l and O use the same m, so the result is unchanged.
+// Math per step and wave (bf16):
+//   S^T[key][q] = K Q^T    v_mfma_f32_32x32x16_bf16, A = K rows (LDS), B = Q^T
+//                          (registers, one load per tile).  Each lane column is
+//                          one query, so the row max and row sum are in-lane
+//                          plus one exchange between the two half-waves.
+//   O^T[d][q] += V^T P^T   A = V^T fragments read with ds_read_b64_tr_b16
+//                          (V stays row-major in LDS), B = P^T straight from
+//                          the S^T accumulators: key rows are stored in LDS with
+//                          bits 2 and 3 of the key index swapped, so lane
+//                          element i of S^T holds key 16*(i/8) + 8*half + i%8,
+//                          8 consecutive keys per 16-key chunk as the B operand
+//                          wants.
+//   fp32 inputs: v_mfma_f32_32x32x2f32 with the same layouts, P kept in fp32,
+//   V^T elements read one by one.
+// Softmax: scores stay unscaled; p = exp2(s*c - m) with c = scale*log2(e) is one
+// FMA and one v_exp_f32.  The running max m is raised only when a score exceeds it by more
+// than 2^kLazy (decided per wave; O and l are then rescaled), so p <= 2^kLazy;
+// l and O share m, so the quotient is unchanged.
 
 #include "sa_device.hpp"
 #include "sa_kernels.hpp"
@@ -45,116 +47,80 @@ namespace sa {
 
 namespace {
 
-constexpr int kKS = 64;        // keys per step
-constexpr float kLazy = 8.f;   // log2 headroom before the running max is raised
+constexpr int kKS = 64;       // keys per step
+constexpr float kLazy = 8.f;  // log2 headroom before the running max is raised
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // swap bits 2 and 3 of a key index (an involution)
 __device__ __forceinline__ int perm_key(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-// 16-byte chunk swizzles
-__device__ __forceinline__ int swz_k(int row, int chunk) { return chunk ^ (row & 7); }
-__device__ __forceinline__ int swz_v(int drow, int chunk) { return chunk ^ ((drow + (drow >> 3)) & 7); }
+__device__ __forceinline__ u32x4 lds16(const char* base, int off) { return *reinterpret_cast<const u32x4*>(base + off); }
 
-__device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x4 lds16(const char* base, int byte_off) {
-  return *reinterpret_cast<const u32x4*>(base + byte_off);
-}
-template <int BYTES>
-__device__ __forceinline__ void sts(char* base, int byte_off, const uint32_t* w) {
-  if constexpr (BYTES == 16) {
-    *reinterpret_cast<u32x4*>(base + byte_off) = u32x4{w[0], w[1], w[2], w[3]};
-  } else if constexpr (BYTES == 8) {
-    *reinterpret_cast<uint2*>(base + byte_off) = uint2{w[0], w[1]};
-  } else {
-    *reinterpret_cast<uint32_t*>(base + byte_off) = w[0];
-  }
+// 16 bytes per lane from a buffer straight into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds).  The builtin only exists for the device
+// target, so the host pass of the single-source compile sees an empty body.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+#else
+  (void)r, (void)lds, (void)voff, (void)soff;
+#endif
 }
 
-template <typename T, int D, int B, int W>
+template <typename T, int D, int B>
 struct Cfg {
   static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int kThreads = 64 * W;
+  static constexpr int kW = B / 32;  // waves, 32 queries each
+  static constexpr int kThreads = 64 * kW;
   static constexpr int kE16 = 16 / int(sizeof(T));  // elements per 16 bytes
-  static constexpr int kNSub = B / kKS;             // steps per key block
-  static constexpr int kQPW = B / W;                // queries per wave
-  static constexpr int kQT = kQPW / 32;             // 32-query MFMA column tiles per wave
-  static constexpr int kDT = D / 32;                // 32-row d tiles of O^T
-  static constexpr int kKRowBytes = D * int(sizeof(T));
-  static constexpr int kKChunks = kKRowBytes / 16;  // 16-byte chunks per K row
-  static constexpr int kVRowBytes = kKS * int(sizeof(T));
-  static constexpr int kKBytes = kKS * kKRowBytes;
-  static constexpr int kVBytes = D * kVRowBytes;
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kKLoads = kKS * kKChunks / kThreads;  // 16-byte K loads per thread
-  static constexpr int kKRowsPerLoad = kThreads / kKChunks;
-  // V transpose unit: kVK keys x kE16 d (one 16-byte load per key row),
-  // written as kE16 transposed runs of kVK elements
-  static constexpr int kVKWant = kKS * D / (kE16 * kThreads);
-  static constexpr int kVK = kVKWant > kE16 ? kE16 : (kVKWant < 2 ? 2 : kVKWant);
-  static constexpr int kVUnits = (kKS / kVK) * (D / kE16);
-  static constexpr int kVUnitsPerThread = (kVUnits + kThreads - 1) / kThreads;
-  static constexpr int kVWrite = kVK * int(sizeof(T));  // bytes per transposed run
-  static constexpr int kDG = D / (2 * kE16);            // Q K^T k-groups (16 B per lane)
-  static_assert(kQT >= 1, "at least 32 queries per wave");
-  static_assert(kKLoads * kThreads == kKS * kKChunks, "K loads must divide evenly");
+  static constexpr int kNSub = B / kKS;
+  static constexpr int kDT = D / 32;  // 32-row d tiles of O^T
+  static constexpr int kRow = D * int(sizeof(T));  // bytes per K or V row
+  static constexpr int kCpr = kRow / 16;           // 16-byte chunks per row
+  static constexpr int kTile = kKS * kRow;         // bytes of one K (or V) step
+  static constexpr int kInsts = kTile / 1024;      // 1 KB direct-to-LDS wave instructions per tile
+  static constexpr int kInstsPerWave = kInsts / kW;
+  static constexpr int kDG = D / (2 * kE16);  // Q K^T k-groups of 16 bytes per lane
+  static constexpr int kLds = 4 * kTile;      // K ring (2) + V ring (2)
+  static_assert(kInsts % kW == 0, "direct loads must split evenly over the waves");
+
+  // 16-byte chunk swizzles, free of bank conflicts whether the LDS serves 128
+  // or 256 bytes per clock.  K rows (read 16 B per lane, one row per lane):
+  // the 16 rows a 256-byte cycle touches land on 16 distinct slots.  V rows
+  // (transposed 8-byte reads, 4 rows x 2 or 4 chunks per cycle): the XOR
+  // patterns {0, 6, 10, 12} differ both in chunk bits 1-2 and in bits 2-3.
+  static constexpr int kRowsPer256 = kRow >= 256 ? 1 : 256 / kRow;
+  static constexpr int kKMask = (kCpr < 16 ? kCpr : 16) - 1;
+  __device__ static int swz_k(int row) { return (row / kRowsPer256) & kKMask; }
+  __device__ static int swz_v(int row) {
+    const int x = (0xCA60 >> ((row & 3) * 4)) & 15;  // 0, 6, 10, 12
+    return x & (kCpr - 1);
+  }
 };
 
+// One 64-key step, wave-uniform (scalar registers).
 struct Step {
   int valid;
-  int item;  // index into the bin's item list
-  int tile;
+  int item;  // position in the bin's item list
   int j;     // position in the tile's block list
-  int hs;    // step within the key block
-  int cnt;   // blocks of this tile
+  int hs;    // 64-key step within the key block
   int n;     // key block index
+  int tile;  // (b * Hq + h) * NB + m
+  int m;     // query block of the tile
+  int bh;    // b * Hq + h
+  int kb;    // batch of the tile
+  int kh;    // KV head h / G
 };
 
-__device__ __forceinline__ int tile_of(const PrefillParams& p, int item) {
-  return p.items_by_bin ? p.items_by_bin[item] : item;
-}
-
-// key block j of a tile, or -1 if the table holds something outside 0..m
-__device__ __forceinline__ int block_at(const PrefillParams& p, int tile, int j) {
-  const int n = wave_uniform(p.block_idx[(int64_t)tile * p.kmax + j]);
-  return (n >= 0 && n <= tile % p.NB) ? n : -1;
-}
-
-// first step at or after (item it, block j) whose block entry is valid
-__device__ __forceinline__ void seek(const PrefillParams& p, int it, int j, int it_end, Step& s) {
-  s.valid = 0;
-  for (; it < it_end; ++it, j = 0) {
-    const int tile = wave_uniform(tile_of(p, it));
-    if (tile < 0 || tile >= p.n_tiles) continue;
-    const int cnt = min(wave_uniform(p.block_cnt[tile]), p.kmax);
-    for (; j < cnt; ++j) {
-      const int n = block_at(p, tile, j);
-      if (n >= 0) {
-        s.valid = 1;
-        s.item = it;
-        s.tile = tile;
-        s.j = j;
-        s.hs = 0;
-        s.cnt = cnt;
-        s.n = n;
-        return;
-      }
-    }
-  }
-}
-
-template <int NSUB>
-__device__ __forceinline__ void advance(const PrefillParams& p, int it_end, Step& s) {
-  if (s.hs + 1 < NSUB) {
-    s.hs += 1;
-    return;
-  }
-  seek(p, s.item, s.j + 1, it_end, s);
-}
-
-template <typename T, int D, int B, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ? 2 : 1, W == 4 ? 2 : 1))) void prefill_kernel(PrefillParams p) {
-  using C = Cfg<T, D, B, W>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::kStage];
+template <typename T, int D, int B>
+__global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
+  using C = Cfg<T, D, B>;
+  __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
+  char* const kring = smem;                 // K slots 0, 1
+  char* const vring = smem + 2 * C::kTile;  // V slots 0, 1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,326 +139,374 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(W == 4 ?
   const int NB = p.NB;
   const int S = p.S;
   const float c2 = p.scale_log2;
-
-  // ---------------------------------------------------------------- loads
-  u32x4 kreg[C::kKLoads];
-  u32x4 vreg[C::kVUnitsPerThread][C::kVK];
   const int krs = int(p.ks2 * (int64_t)sizeof(T));
   const int vrs = int(p.vs2 * (int64_t)sizeof(T));
-  const int k_voff = (tid / C::kKChunks) * krs + (tid % C::kKChunks) * 16;
 
-  auto slice = [&](int tile, const void* base, int64_t s0, int64_t s1, int rs) {
-    const int bi = tile / (p.Hq * NB);
-    const int h = (tile / NB) % p.Hq;
-    const char* b = reinterpret_cast<const char*>(base) + (bi * s0 + (h / p.G) * s1) * (int64_t)sizeof(T);
-    return __builtin_amdgcn_make_buffer_rsrc((void*)b, (short)0, S * rs, 0x00020000);
+  // ---------------------------------------------------------------- step cursor
+  // The bin's items and each tile's block list are read through per-wave
+  // register windows (lane l holds entry base + l) and picked out with
+  // readlane, so advancing a step never waits on memory.  The window of the
+  // next item's blocks is fetched while the current item runs.
+  int ibase = it_beg;
+  int iw_tile = -1, iw_cnt = 0;  // per lane: tile and block count of item ibase + lane
+  auto load_items = [&](int base) {
+    ibase = base;
+    const int it = base + lane;
+    int t = -1, c = 0;
+    if (it < it_end) {
+      t = p.items_by_bin ? p.items_by_bin[it] : it;
+      if (t >= 0 && t < p.n_tiles) c = min(p.block_cnt[t], p.kmax);
+      else t = -1;
+    }
+    iw_tile = t;
+    iw_cnt = c;
   };
-  auto load_k = [&](const Step& s) {
-    const auto rk = slice(s.tile, p.k, p.ks0, p.ks1, krs);
-    const int key0 = s.n * B + s.hs * kKS;
-#pragma unroll
-    for (int i = 0; i < C::kKLoads; ++i)
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, k_voff, (key0 + i * C::kKRowsPerLoad) * krs, 0);
+  auto load_blocks = [&](int tile, int cnt, int base) {
+    const int jj = base + lane;
+    return jj < cnt ? p.block_idx[(int64_t)tile * p.kmax + jj] : -1;
   };
-  auto load_v = [&](const Step& s) {
-    const auto rv = slice(s.tile, p.v, p.vs0, p.vs1, vrs);
-    const int key0 = s.n * B + s.hs * kKS;
-#pragma unroll
-    for (int u = 0; u < C::kVUnitsPerThread; ++u) {
-      const int unit = u * C::kThreads + tid;
-      if (unit < C::kVUnits) {
-        const int dc = unit % (D / C::kE16), kg = unit / (D / C::kE16);
-        const int voff = kg * C::kVK * vrs + dc * 16;
-#pragma unroll
-        for (int e = 0; e < C::kVK; ++e)
-          vreg[u][e] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, (key0 + e) * vrs, 0);
+  // cursor over the lookahead step (the others are copies of it)
+  int c_cnt = 0, c_wbase = 0, c_win = -1;  // blocks of the cursor's tile: window at c_wbase
+  int nx_item = -1, nx_win = -1;            // prefetched first window of item nx_item
+  Step cur;
+  cur.valid = 0;
+
+  auto item_tile = [&](int it, int& tile, int& cnt) {
+    if (it - ibase >= 64) load_items(it);
+    tile = __builtin_amdgcn_readlane(iw_tile, it - ibase);
+    cnt = __builtin_amdgcn_readlane(iw_cnt, it - ibase);
+  };
+  auto prefetch_next = [&](int it) {
+    nx_item = -1;
+    if (it >= it_end || it - ibase >= 64) return;
+    const int tile = __builtin_amdgcn_readlane(iw_tile, it - ibase);
+    const int cnt = __builtin_amdgcn_readlane(iw_cnt, it - ibase);
+    if (tile < 0) return;
+    nx_win = load_blocks(tile, cnt, 0);
+    nx_item = it;
+  };
+  // first valid block at or after position j of item `it` (moving to later items)
+  auto seek = [&](int it, int j) {
+    while (true) {
+      if (it >= it_end) {
+        cur.valid = 0;
+        return;
       }
-    }
-  };
-  auto store_k = [&](int stage) {
-    char* ks = smem + stage * C::kStage;
-#pragma unroll
-    for (int i = 0; i < C::kKLoads; ++i) {
-      const int flat = i * C::kThreads + tid;
-      const int r = flat / C::kKChunks, c = flat % C::kKChunks;
-      const int lr = perm_key(r);
-      *reinterpret_cast<u32x4*>(ks + lr * C::kKRowBytes + swz_k(lr, c) * 16) = kreg[i];
-    }
-  };
-  auto store_v = [&](int stage) {
-    char* vs = smem + stage * C::kStage + C::kKBytes;
-#pragma unroll
-    for (int u = 0; u < C::kVUnitsPerThread; ++u) {
-      const int unit = u * C::kThreads + tid;
-      if (unit < C::kVUnits) {
-        const int dc = unit % (D / C::kE16), kg = unit / (D / C::kE16);
-        const int kbyte = kg * C::kVWrite;  // byte offset of the run within a V^T row
-#pragma unroll
-        for (int e = 0; e < C::kE16; ++e) {
-          uint32_t w[4];
-          if constexpr (C::kBf16) {
-            // column e (d = 8*dc + e) of the kVK key rows, packed two keys per word
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-            for (int t = 0; t < C::kVK / 2; ++t)
-              w[t] = __builtin_amdgcn_perm(vreg[u][2 * t + 1][e >> 1], vreg[u][2 * t][e >> 1], sel);
-          } else {
-#pragma unroll
-            for (int t = 0; t < C::kVK; ++t) w[t] = vreg[u][t][e];
-          }
-          const int drow = dc * C::kE16 + e;
-          sts<C::kVWrite>(vs, drow * C::kVRowBytes + swz_v(drow, kbyte >> 4) * 16 + (kbyte & 15), w);
+      if (it != cur.item || !cur.valid) {
+        int tile, cnt;
+        item_tile(it, tile, cnt);
+        cur.item = it;
+        cur.valid = 1;
+        cur.tile = tile;
+        c_cnt = tile >= 0 ? cnt : 0;
+        c_wbase = 0;
+        if (tile >= 0) {
+          c_win = (nx_item == it) ? nx_win : load_blocks(tile, c_cnt, 0);
+          cur.m = tile % NB;
+          cur.bh = tile / NB;
+          cur.kb = cur.bh / p.Hq;
+          cur.kh = (cur.bh % p.Hq) / p.G;
+          prefetch_next(it + 1);
         }
       }
-    }
-  };
-
-  // ---------------------------------------------------------------- tile state
-  u32x4 qf[C::kQT][C::kDG];  // Q^T fragments
-  f32x16 oacc[C::kDT][C::kQT];
-  float m_run[C::kQT], l_run[C::kQT];
-
-  auto start_tile = [&](int tile) {
-    const int bi = tile / (p.Hq * NB);
-    const int h = (tile / NB) % p.Hq;
-    const int m = tile % NB;
-    const char* qb = reinterpret_cast<const char*>(p.q) + (bi * p.qs0 + h * p.qs1) * (int64_t)sizeof(T);
-#pragma unroll
-    for (int qt = 0; qt < C::kQT; ++qt) {
-      const int qrow = m * B + wave * C::kQPW + qt * 32 + col;
-      const char* rp = qb + (int64_t)qrow * p.qs2 * (int64_t)sizeof(T);
-#pragma unroll
-      for (int dg = 0; dg < C::kDG; ++dg) {
-        // bf16: lane half g holds d = 16*dg + 8*g .. +7; fp32: d = 8*dg + 4*g .. +3
-        const int d0 = dg * 2 * C::kE16 + half * C::kE16;
-        qf[qt][dg] = qrow < S ? ldg16(rp + d0 * (int)sizeof(T)) : u32x4{0u, 0u, 0u, 0u};
-      }
-      m_run[qt] = kNegInf;
-      l_run[qt] = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < C::kDT; ++dt) oacc[dt][qt] = f32x16{};
-    }
-  };
-
-  auto finish_tile = [&](int tile) {
-    const int bi = tile / (p.Hq * NB);
-    const int h = (tile / NB) % p.Hq;
-    const int m = tile % NB;
-#pragma unroll
-    for (int qt = 0; qt < C::kQT; ++qt) {
-      const float l = l_run[qt] + __shfl_xor(l_run[qt], 32, 64);
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int qrow = m * B + wave * C::kQPW + qt * 32 + col;
-      if (qrow < S) {
-        const int64_t orow = bi * p.os0 + h * p.os1 + (int64_t)qrow * p.os2;
-#pragma unroll
-        for (int dt = 0; dt < C::kDT; ++dt) {
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int d = dt * 32 + r4 * 8 + half * 4;
-            const float o0 = oacc[dt][qt][r4 * 4 + 0] * inv, o1 = oacc[dt][qt][r4 * 4 + 1] * inv;
-            const float o2 = oacc[dt][qt][r4 * 4 + 2] * inv, o3 = oacc[dt][qt][r4 * 4 + 3] * inv;
-            if (C::kBf16 && !p.out_f32) {
-              uint2 w;
-              w.x = pack_bf16x2(o0, o1);
-              w.y = pack_bf16x2(o2, o3);
-              *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.o) + orow + d) = w;
-            } else {
-              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d) = f32x4{o0, o1, o2, o3};
-            }
-          }
+      for (; j < c_cnt; ++j) {
+        if (j - c_wbase >= 64) {
+          c_wbase = j;
+          c_win = load_blocks(cur.tile, c_cnt, j);
         }
-        if (p.lse && half == 0)
-          p.lse[((int64_t)bi * p.Hq + h) * S + qrow] = l > 0.f ? (m_run[qt] + __log2f(l)) * kLn2 : kNegInf;
+        const int n = __builtin_amdgcn_readlane(c_win, j - c_wbase);
+        if (n >= 0 && n <= cur.m) {
+          cur.j = j;
+          cur.hs = 0;
+          cur.n = n;
+          return;
+        }
       }
+      ++it;
+      j = 0;
     }
   };
-
-  // ---------------------------------------------------------------- one step
-  auto compute_step = [&](const Step& s, int stage, const Step& nx) {
-    const int m = s.tile % NB;
-    const int n = s.n;
-    const int key0 = s.hs * kKS;      // first key of the step within block n
-    const int q_lo = wave * C::kQPW;  // first query of the wave within block m
-    // the whole step lies above the causal diagonal for this wave
-    if (n == m && key0 > q_lo + C::kQPW - 1) {
-      if (nx.valid) {
-        store_k(stage ^ 1);
-        load_v(nx);
-      }
+  auto advance = [&]() {
+    if (!cur.valid) return;
+    if (cur.hs + 1 < C::kNSub) {
+      cur.hs += 1;
       return;
     }
-    const bool diag = (n == m) && (key0 + kKS - 1 > q_lo);
-    const bool tail = (n * B + key0 + kKS > S);
-    const char* ks = smem + stage * C::kStage;
-    const char* vs = ks + C::kKBytes;
+    seek(cur.item, cur.j + 1);
+  };
 
-    f32x16 sacc[2][C::kQT];
+  // ---------------------------------------------------------------- direct loads
+  // Wave instruction t of a step fills LDS bytes [1024 t, 1024 t + 1024): lane i
+  // writes 16 bytes at 1024 t + 16 i, i.e. LDS row r = (1024 t + 16 i) / kRow,
+  // physical chunk cp; it fetches the global row and chunk the swizzle puts there.
+  int k_voff[C::kInstsPerWave], v_voff[C::kInstsPerWave];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+  for (int u = 0; u < C::kInstsPerWave; ++u) {
+    const int t = wave * C::kInstsPerWave + u;
+    const int byte = t * 1024 + lane * 16;
+    const int r = byte / C::kRow, cp = (byte % C::kRow) / 16;
+    k_voff[u] = perm_key(r) * krs + (cp ^ C::swz_k(r)) * 16;
+    v_voff[u] = r * vrs + (cp ^ C::swz_v(r)) * 16;
+  }
+  auto fetch = [&](const Step& s, int slot, bool k_side) {
+    const char* base = k_side
+                           ? reinterpret_cast<const char*>(p.k) + (s.kb * p.ks0 + s.kh * p.ks1) * (int64_t)sizeof(T)
+                           : reinterpret_cast<const char*>(p.v) + (s.kb * p.vs0 + s.kh * p.vs1) * (int64_t)sizeof(T);
+    const int rs = k_side ? krs : vrs;
+    const auto r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, S * rs, 0x00020000);
+    const int so = (s.n * B + s.hs * kKS) * rs;
+    char* dst = (k_side ? kring : vring) + slot * C::kTile + wave * C::kInstsPerWave * 1024;
 #pragma unroll
-      for (int qt = 0; qt < C::kQT; ++qt) sacc[kt][qt] = f32x16{};
+    for (int u = 0; u < C::kInstsPerWave; ++u) dma16(r, dst + u * 1024, k_side ? k_voff[u] : v_voff[u], so);
+  };
+  // all of this wave's direct loads have landed in LDS (vmcnt(0) only)
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-    // ---- S^T = K Q^T
+  // ---------------------------------------------------------------- tile state
+  u32x4 qf[C::kDG];  // Q^T fragments of the wave's 32 queries
+  f32x16 oacc[C::kDT];
+  float m_run = kNegInf, l_run = 0.f;
+  int t_bh = 0, t_m = 0;  // tile being accumulated
+
+  auto start_tile = [&](const Step& s) {
+    t_bh = s.bh;
+    t_m = s.m;
+    const int bi = s.bh / p.Hq, h = s.bh % p.Hq;
+    const int qrow = s.m * B + wave * 32 + col;
+    const char* rp = reinterpret_cast<const char*>(p.q) +
+                     (bi * p.qs0 + h * p.qs1 + (int64_t)qrow * p.qs2) * (int64_t)sizeof(T);
+#pragma unroll
+    for (int dg = 0; dg < C::kDG; ++dg) {
+      // bf16: lane half g holds d = 16*dg + 8*g .. +7; fp32: d = 8*dg + 4*g .. +3
+      const int d0 = dg * 2 * C::kE16 + half * C::kE16;
+      qf[dg] = qrow < S ? *reinterpret_cast<const u32x4*>(rp + d0 * (int)sizeof(T)) : u32x4{0u, 0u, 0u, 0u};
+    }
+    m_run = kNegInf;
+    l_run = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; ++dt) oacc[dt] = f32x16{};
+  };
+
+  auto finish_tile = [&]() {
+    const int bi = t_bh / p.Hq, h = t_bh % p.Hq;
+    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int qrow = t_m * B + wave * 32 + col;
+    if (qrow < S) {
+      const int64_t orow = bi * p.os0 + h * p.os1 + (int64_t)qrow * p.os2;
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; ++dt) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = dt * 32 + r4 * 8 + half * 4;
+          const float o0 = oacc[dt][r4 * 4 + 0] * inv, o1 = oacc[dt][r4 * 4 + 1] * inv;
+          const float o2 = oacc[dt][r4 * 4 + 2] * inv, o3 = oacc[dt][r4 * 4 + 3] * inv;
+          if (C::kBf16 && !p.out_f32) {
+            *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.o) + orow + d) =
+                uint2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+          } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d) = f32x4{o0, o1, o2, o3};
+          }
+        }
+      }
+      if (p.lse && half == 0)
+        p.lse[(int64_t)t_bh * S + qrow] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : kNegInf;
+    }
+  };
+
+  // does this wave see any key of step s? (the causal diagonal can hide a whole step)
+  auto visible = [&](const Step& s) { return s.valid && !(s.n == s.m && s.hs * kKS > wave * 32 + 31); };
+
+  // S^T = K Q^T of a step from K slot `slot`
+  auto qk = [&](int slot, f32x16(&sacc)[2]) {
+    const char* ks = kring + slot * C::kTile;
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
 #pragma unroll
     for (int dg = 0; dg < C::kDG; ++dg) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const int r = kt * 32 + col;
-        const u32x4 a = lds16(ks, r * C::kKRowBytes + swz_k(r, dg * 2 + half) * 16);
+        const u32x4 a = lds16(ks, r * C::kRow + ((dg * 2 + half) ^ C::swz_k(r)) * 16);
+        if constexpr (C::kBf16) {
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                             __builtin_bit_cast(bf16x8, qf[dg]), sacc[kt], 0, 0, 0);
+        } else {
 #pragma unroll
-        for (int qt = 0; qt < C::kQT; ++qt) {
-          if constexpr (C::kBf16) {
-            sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[qt][dg]), sacc[kt][qt], 0, 0, 0);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              sacc[kt][qt] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), __uint_as_float(qf[qt][dg][e]),
-                                                                  sacc[kt][qt], 0, 0, 0);
-          }
+          for (int e = 0; e < 4; ++e)
+            sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), __uint_as_float(qf[dg][e]),
+                                                            sacc[kt], 0, 0, 0);
         }
       }
     }
+  };
 
-    // K of the next step goes to the other stage now; V of the next step is
-    // fetched while the softmax and P V run
-    if (nx.valid) {
-      store_k(stage ^ 1);
-      load_v(nx);
-    }
-
-    // ---- online softmax in the log2 domain
-#pragma unroll
-    for (int qt = 0; qt < C::kQT; ++qt) {
-      if (diag || tail) {
-        const int q_in_blk = q_lo + qt * 32 + col;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kl = key0 + kt * 32 + (i >> 3) * 16 + half * 8 + (i & 7);
-            const bool masked = (diag && kl > q_in_blk) || (tail && n * B + kl >= S);
-            if (masked) sacc[kt][qt][i] = kNegInf;
-          }
-      }
-      float mx = kNegInf;
+  // softmax of a step (its scores in sacc) and O += P V from V slot `slot`
+  auto softmax_pv = [&](const Step& s, int slot, f32x16(&sacc)[2]) {
+    const int key0 = s.hs * kKS;
+    const bool diag = (s.n == s.m) && (key0 + kKS - 1 > wave * 32);
+    const bool tail = (s.n * B + key0 + kKS > S);
+    if (diag || tail) {
+      const int q_in_blk = wave * 32 + col;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][qt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-      // raise the running max only when a score gets 2^kLazy above it
-      const bool raise = mx > m_run[qt] + kLazy;
-      if (__ballot(raise) != 0) {
-        const float m_new = raise ? mx : m_run[qt];
-        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run[qt] - m_new) : 1.f;  // 0 when m_run = -inf
-        l_run[qt] *= alpha;
+        for (int i = 0; i < 16; ++i) {
+          const int kl = key0 + kt * 32 + (i >> 3) * 16 + half * 8 + (i & 7);
+          if ((diag && kl > q_in_blk) || (tail && s.n * B + kl >= S)) sacc[kt][i] = kNegInf;
+        }
+    }
+    float mx = kNegInf;
 #pragma unroll
-        for (int dt = 0; dt < C::kDT; ++dt) oacc[dt][qt] *= alpha;
-        m_run[qt] = m_new;
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kt][i], sacc[kt][i + 1]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+    const bool raise = mx > m_run + kLazy;
+    if (__ballot(raise) != 0) {
+      const float m_new = raise ? mx : m_run;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < C::kDT; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    const char* vs = vring + slot * C::kTile;
+    if constexpr (C::kBf16) {
+      // P as packed bf16 (the MFMA B operand) and its row sum
+      u32x4 pf[4];
+      float psum0 = 0.f, psum1 = 0.f;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int i = (kc & 1) * 8 + 2 * w;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][i], c2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][i + 1], c2, -m_use));
+          pf[kc][w] = pack_bf16x2(p0, p1);
+          psum0 += p0;
+          psum1 += p1;
+        }
       }
-      const float m_use = m_run[qt] == kNegInf ? 0.f : m_run[qt];
+      l_run += psum0 + psum1;
+      // O^T += V^T P^T.  A fragments by transposed LDS reads: 16-lane group G
+      // covers d = 32 dt + 16 (G % 2) + lane % 16 and keys 16 kc + 8 (G / 2) +
+      // 4 r + 0..3; source lane j of the group points at V row k0 + j / 4,
+      // columns dbase + 4 (j % 4) .. +3.
+      const int G = lane >> 4, j = lane & 15;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int dt = 0; dt < C::kDT; ++dt) {
+          const int d = dt * 32 + (G & 1) * 16 + (j & 3) * 4;
+          const int row0 = kc * 16 + (G >> 1) * 8 + (j >> 2);
+          const int row1 = row0 + 4;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(vs + row0 * C::kRow + (((d >> 3) ^ C::swz_v(row0)) << 4) + ((d & 7) << 1)));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16*)(vs + row1 * C::kRow + (((d >> 3) ^ C::swz_v(row1)) << 4) + ((d & 7) << 1)));
+          const u32x4 a = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                             __builtin_bit_cast(bf16x8, pf[kc]), oacc[dt], 0, 0, 0);
+        }
+      }
+    } else {
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][qt][i], c2, -m_use));
-          sacc[kt][qt][i] = pv;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], c2, -m_use));
+          sacc[kt][i] = pv;
           psum += pv;
         }
-      l_run[qt] += psum;
-    }
-
-    // ---- O^T += V^T P^T
+      l_run += psum;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const int kt = kc >> 1, c = kc & 1;
-      if constexpr (C::kBf16) {
-        u32x4 pf[C::kQT];
-#pragma unroll
-        for (int qt = 0; qt < C::kQT; ++qt)
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            pf[qt][w] = pack_bf16x2(sacc[kt][qt][8 * c + 2 * w], sacc[kt][qt][8 * c + 2 * w + 1]);
+      for (int kc = 0; kc < 4; ++kc) {
 #pragma unroll
         for (int dt = 0; dt < C::kDT; ++dt) {
-          const int drow = dt * 32 + col;
-          const u32x4 a = lds16(vs, drow * C::kVRowBytes + swz_v(drow, kc * 2 + half) * 16);
+          const int d = dt * 32 + col;
 #pragma unroll
-          for (int qt = 0; qt < C::kQT; ++qt)
-            oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, pf[qt]), oacc[dt][qt], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int dt = 0; dt < C::kDT; ++dt) {
-          const int drow = dt * 32 + col;
-          // keys 16*kc + 8*half .. +7: two 16-byte chunks
-          const u32x4 a0 = lds16(vs, drow * C::kVRowBytes + swz_v(drow, kc * 4 + half * 2) * 16);
-          const u32x4 a1 = lds16(vs, drow * C::kVRowBytes + swz_v(drow, kc * 4 + half * 2 + 1) * 16);
-#pragma unroll
-          for (int qt = 0; qt < C::kQT; ++qt)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              oacc[dt][qt] = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(e < 4 ? a0[e & 3] : a1[e & 3]),
-                                                                  sacc[kt][qt][8 * c + e], oacc[dt][qt], 0, 0, 0);
+          for (int e = 0; e < 8; ++e) {
+            const int row = kc * 16 + half * 8 + e;
+            const int off = row * C::kRow + (((d >> 2) ^ C::swz_v(row)) << 4) + ((d & 3) << 2);
+            const float a = *reinterpret_cast<const float*>(vs + off);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sacc[kc >> 1][(kc & 1) * 8 + e], oacc[dt], 0, 0, 0);
+          }
         }
       }
     }
   };
 
   // ---------------------------------------------------------------- walk
-  Step cur, nxt;
-  seek(p, it_beg, 0, it_end, cur);
-  if (!cur.valid) return;
-  load_k(cur);
-  load_v(cur);
-  store_k(0);
-  store_v(0);
+  // Step i's K sits in K slot i%2, its V in V slot i%2.  At the top of
+  // iteration i, S(i) is computed (if the wave sees the step) and K(i+1), V(i)
+  // were fetched during iteration i-1.
+  load_items(it_beg);
+  cur.item = -1;
+  seek(it_beg, 0);
+  Step s0 = cur;
+  if (!s0.valid) return;
+  advance();
+  Step s1 = cur;
+  advance();
+  fetch(s0, 0, true);
+  fetch(s0, 0, false);
+  if (s1.valid) fetch(s1, 1, true);
+  wait_loads();
   __syncthreads();
-  nxt = cur;
-  advance<C::kNSub>(p, it_end, nxt);
-  start_tile(cur.tile);
-  int stage = 0;
-  while (true) {
-    if (nxt.valid) load_k(nxt);
-    compute_step(cur, stage, nxt);
-    const bool tile_done = !nxt.valid || nxt.tile != cur.tile || nxt.item != cur.item;
-    if (tile_done) finish_tile(cur.tile);
-    if (nxt.valid) store_v(stage ^ 1);
+  start_tile(s0);
+  f32x16 sa[2], sb[2];
+  sb[0] = f32x16{};
+  sb[1] = f32x16{};
+  bool vis0 = visible(s0);
+  if (vis0) qk(0, sa);
+
+  // one iteration; `sc` holds S of step s0, `sn` receives S of step s1
+  auto iteration = [&](int slot, f32x16(&sc)[2], f32x16(&sn)[2]) -> bool {
+    // K(i+1) and V(i) are in LDS; every wave is done with the slots refilled here
+    wait_loads();
     __syncthreads();
-    if (!nxt.valid) break;
-    if (tile_done) start_tile(nxt.tile);
-    cur = nxt;
-    advance<C::kNSub>(p, it_end, nxt);
-    stage ^= 1;
+    if (cur.valid) fetch(cur, slot, true);  // K(i+2)
+    if (s1.valid) fetch(s1, slot ^ 1, false);  // V(i+1)
+    const bool pipe = s1.valid && s1.item == s0.item;
+    const bool vis1 = visible(s1);
+    if (pipe && vis1) qk(slot ^ 1, sn);
+    if (vis0) softmax_pv(s0, slot, sc);
+    if (!pipe) {
+      finish_tile();
+      if (!s1.valid) return false;
+      start_tile(s1);
+      if (vis1) qk(slot ^ 1, sn);
+    }
+    vis0 = vis1;
+    s0 = s1;
+    s1 = cur;
+    advance();
+    return true;
+  };
+  while (iteration(0, sa, sb) && iteration(1, sb, sa)) {
   }
 }
 
-template <typename T, int D, int B, int W>
+template <typename T, int D, int B>
 hipError_t launch_t(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<T, D, B, W>), dim3(grid), dim3(64 * W), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<T, D, B>), dim3(grid), dim3(2 * B), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int waves, int grid, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int grid, hipStream_t stream) {
   if (dtype == 0) {
-    if (waves == 2) {
-      if (D == 128 && B == 128) return launch_t<bf16_t, 128, 128, 2>(p, grid, stream);
-      if (D == 128 && B == 64) return launch_t<bf16_t, 128, 64, 2>(p, grid, stream);
-      if (D == 64 && B == 128) return launch_t<bf16_t, 64, 128, 2>(p, grid, stream);
-      if (D == 64 && B == 64) return launch_t<bf16_t, 64, 64, 2>(p, grid, stream);
-    } else if (waves == 4) {
-      if (D == 128 && B == 128) return launch_t<bf16_t, 128, 128, 4>(p, grid, stream);
-      if (D == 64 && B == 128) return launch_t<bf16_t, 64, 128, 4>(p, grid, stream);
-    }
-  } else if (waves == 2) {
-    if (D == 128 && B == 64) return launch_t<float, 128, 64, 2>(p, grid, stream);
-    if (D == 64 && B == 64) return launch_t<float, 64, 64, 2>(p, grid, stream);
+    if (D == 128 && B == 128) return launch_t<bf16_t, 128, 128>(p, grid, stream);
+    if (D == 128 && B == 64) return launch_t<bf16_t, 128, 64>(p, grid, stream);
+    if (D == 64 && B == 128) return launch_t<bf16_t, 64, 128>(p, grid, stream);
+    if (D == 64 && B == 64) return launch_t<bf16_t, 64, 64>(p, grid, stream);
+  } else {
+    if (D == 128 && B == 64) return launch_t<float, 128, 64>(p, grid, stream);
+    if (D == 64 && B == 64) return launch_t<float, 64, 64>(p, grid, stream);
   }
   return hipErrorInvalidValue;
 }

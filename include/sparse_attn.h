@@ -82,9 +82,7 @@ typedef struct {
   int32_t block_size;
   int32_t dtype;
   float softmax_scale;
-  int32_t kernel_variant; /* prefill attention workgroup shape: 0 = default,
-                             2 = 2 waves x B/2 queries, 4 = 4 waves x B/4 queries
-                             (bf16, block 128 only); results are identical */
+  int32_t kernel_variant; /* reserved for alternative kernel shapes; must be 0 */
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
 } sa_attn_desc;
 

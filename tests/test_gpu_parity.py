@@ -72,14 +72,12 @@ PREFILL_SHAPES = [
 
 
 @pytest.mark.parametrize("name,over", PREFILL_SHAPES, ids=[s[0] for s in PREFILL_SHAPES])
-@pytest.mark.parametrize("variant", [0, 2])
-def test_prefill_bf16_all_rows(name, over, variant):
+@pytest.mark.parametrize("n_bins", [0, 37])
+def test_prefill_bf16_all_rows(name, over, n_bins):
     spec = W.CONFIGS[1].with_(**over)
-    if variant == 2 and spec.block != 128:
-        pytest.skip("variant applies to block 128")
     inp = W.make_prefill(spec, 77, device=DEV)
-    _say("case:", name, "variant", variant)
-    idx, cnt, o, lse, plan = prefill_gpu(inp, kernel_variant=variant)
+    _say("case:", name, "bins", n_bins)
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins)
     q, k, v = to_host(inp)
     oidx, ocnt, scores = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, return_scores=True)
     gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
@@ -105,15 +103,15 @@ def test_prefill_bf16_output_and_determinism():
     assert torch.equal(o16, o16b), "two runs differ"
 
 
-def test_prefill_schedules_and_variants_bitwise_equal():
+def test_prefill_schedules_bitwise_equal():
     """Every tile is computed by one workgroup with the same arithmetic whatever
-    the schedule or workgroup shape: outputs must be identical bit for bit."""
+    the schedule: outputs must be identical bit for bit."""
     spec = W.CONFIGS[1].with_(seq_len=4096, n_q_heads=8, n_kv_heads=2)
     inp = W.make_prefill(spec, 9, device=DEV)
     outs = []
-    for n_bins, var in ((0, 0), (64, 0), (512, 0), (0, 2), (97, 2)):
-        _say("schedule", n_bins, "variant", var)
-        _, _, o, lse, _ = prefill_gpu(inp, n_bins=n_bins, kernel_variant=var)
+    for n_bins in (0, 1, 64, 512, 97):
+        _say("schedule", n_bins)
+        _, _, o, lse, _ = prefill_gpu(inp, n_bins=n_bins)
         outs.append((o, lse))
     for o, lse in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
