@@ -28,6 +28,9 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # inputs are finite: lets v_max/v_max3 take MFMA results without a
+    # canonicalizing v_max per value (infinities, used as -inf masks, are kept)
+    "-fno-honor-nans",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -314,9 +314,6 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     }
   };
 
-  // does this wave see any key of step s? (the causal diagonal can hide a whole step)
-  auto visible = [&](const Step& s) { return s.valid && !(s.n == s.m && s.hs * kKS > wave * 32 + 31); };
-
   // S^T = K Q^T of a step from K slot `slot`
   auto qk = [&](int slot, f32x16(&sacc)[2]) {
     const char* ks = kring + slot * C::kTile;
@@ -341,55 +338,56 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     }
   };
 
-  // softmax of a step (its scores in sacc) and O += P V from V slot `slot`
-  auto softmax_pv = [&](const Step& s, int slot, f32x16(&sacc)[2]) {
+  // Masking of a step's scores in place (causal diagonal, sequence tail, or a
+  // step this wave cannot see at all).
+  auto apply_mask = [&](const Step& s, f32x16(&sacc)[2]) {
     const int key0 = s.hs * kKS;
-    const bool diag = (s.n == s.m) && (key0 + kKS - 1 > wave * 32);
-    const bool tail = (s.n * B + key0 + kKS > S);
-    if (diag || tail) {
-      const int q_in_blk = wave * 32 + col;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kl = key0 + kt * 32 + (i >> 3) * 16 + half * 8 + (i & 7);
-          if ((diag && kl > q_in_blk) || (tail && s.n * B + kl >= S)) sacc[kt][i] = kNegInf;
-        }
-    }
-    float mx = kNegInf;
+    const bool diag = s.n == s.m;
+    const int q_in_blk = wave * 32 + col;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kt][i], sacc[kt][i + 1]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
-    const bool raise = mx > m_run + kLazy;
-    if (__ballot(raise) != 0) {
-      const float m_new = raise ? mx : m_run;
-      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::kDT; ++dt) oacc[dt] *= alpha;
-      m_run = m_new;
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int kl = key0 + kt * 32 + (i >> 3) * 16 + half * 8 + (i & 7);
+        if ((diag && kl > q_in_blk) || s.n * B + kl >= S) sacc[kt][i] = kNegInf;
+      }
+  };
+
+  // One step: S(i+1) = K(i+1) Q^T (K slot slot^1) issued on the MFMA pipe,
+  // interleaved with the VALU turning S(i) into P(i), then O += P(i) V(i)
+  // (V slot `slot`).  Straight-line; the running max is final for S(i).
+  auto fused = [&](int slot, f32x16(&sc)[2], f32x16(&sn)[2]) {
     const float m_use = m_run == kNegInf ? 0.f : m_run;
+    const char* ks = kring + (slot ^ 1) * C::kTile;
     const char* vs = vring + slot * C::kTile;
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
     if constexpr (C::kBf16) {
-      // P as packed bf16 (the MFMA B operand) and its row sum
       u32x4 pf[4];
-      float psum0 = 0.f, psum1 = 0.f;
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
+      for (int dg = 0; dg < C::kDG; ++dg) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int kt = 0; kt < 2; ++kt) {
+          const int r = kt * 32 + col;
+          const u32x4 a = lds16(ks, r * C::kRow + ((dg * 2 + half) ^ C::swz_k(r)) * 16);
+          sn[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                           __builtin_bit_cast(bf16x8, qf[dg]), sn[kt], 0, 0, 0);
+        }
+        // a share of this lane's 32 probabilities per k-group
+#pragma unroll
+        for (int w2 = 0; w2 < 16 / C::kDG; ++w2) {
+          const int pair = dg * (16 / C::kDG) + w2;  // 0..15
+          const int kc = pair >> 2, w = pair & 3;
           const int i = (kc & 1) * 8 + 2 * w;
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][i], c2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][i + 1], c2, -m_use));
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][i], c2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][i + 1], c2, -m_use));
           pf[kc][w] = pack_bf16x2(p0, p1);
-          psum0 += p0;
-          psum1 += p1;
+          ps0 += p0;
+          ps1 += p1;
         }
       }
-      l_run += psum0 + psum1;
+      l_run += ps0 + ps1;
       // O^T += V^T P^T.  A fragments by transposed LDS reads: 16-lane group G
       // covers d = 32 dt + 16 (G % 2) + lane % 16 and keys 16 kc + 8 (G / 2) +
       // 4 r + 0..3; source lane j of the group points at V row k0 + j / 4,
@@ -411,14 +409,33 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                                                              __builtin_bit_cast(bf16x8, pf[kc]), oacc[dt], 0, 0, 0);
         }
       }
+      // Issue order: K fragment reads run four MFMAs ahead; every Q K^T MFMA
+      // carries a share of the softmax VALU behind it, then every P V MFMA
+      // carries the transposed V reads of the MFMA two places later, so the
+      // MFMA pipe runs under the VALU work and LDS latency stays hidden.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int u = 0; u < 2 * C::kDG; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int u = 0; u < 4 * C::kDT; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (transposed)
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+      }
     } else {
+      qk(slot ^ 1, sn);
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], c2, -m_use));
-          sacc[kt][i] = pv;
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], c2, -m_use));
+          sc[kt][i] = pv;
           psum += pv;
         }
       l_run += psum;
@@ -432,7 +449,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
             const int row = kc * 16 + half * 8 + e;
             const int off = row * C::kRow + (((d >> 2) ^ C::swz_v(row)) << 4) + ((d & 3) << 2);
             const float a = *reinterpret_cast<const float*>(vs + off);
-            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sacc[kc >> 1][(kc & 1) * 8 + e], oacc[dt], 0, 0, 0);
+            oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, sc[kc >> 1][(kc & 1) * 8 + e], oacc[dt], 0, 0, 0);
           }
         }
       }
@@ -441,8 +458,8 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
   // ---------------------------------------------------------------- walk
   // Step i's K sits in K slot i%2, its V in V slot i%2.  At the top of
-  // iteration i, S(i) is computed (if the wave sees the step) and K(i+1), V(i)
-  // were fetched during iteration i-1.
+  // iteration i, S(i) is computed and K(i+1), V(i) were fetched during
+  // iteration i-1.
   load_items(it_beg);
   cur.item = -1;
   seek(it_beg, 0);
@@ -458,12 +475,8 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   __syncthreads();
   start_tile(s0);
   f32x16 sa[2], sb[2];
-  sb[0] = f32x16{};
-  sb[1] = f32x16{};
-  bool vis0 = visible(s0);
-  if (vis0) qk(0, sa);
+  qk(0, sa);
 
-  // one iteration; `sc` holds S of step s0, `sn` receives S of step s1
   auto iteration = [&](int slot, f32x16(&sc)[2], f32x16(&sn)[2]) -> bool {
     // K(i+1) and V(i) are in LDS; every wave is done with the slots refilled here
     wait_loads();
@@ -471,16 +484,35 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     if (cur.valid) fetch(cur, slot, true);  // K(i+2)
     if (s1.valid) fetch(s1, slot ^ 1, false);  // V(i+1)
     const bool pipe = s1.valid && s1.item == s0.item;
-    const bool vis1 = visible(s1);
-    if (pipe && vis1) qk(slot ^ 1, sn);
-    if (vis0) softmax_pv(s0, slot, sc);
+    // rare: masking (causal diagonal, tail, or an invisible step)
+    const int key0 = s0.hs * kKS;
+    if ((s0.n == s0.m && key0 + kKS - 1 > wave * 32) || s0.n * B + key0 + kKS > S) apply_mask(s0, sc);
+    // rare: raise the running max (always at the first step of a tile)
+    {
+      // row max: one v_max3 per pair of scores
+      float mx = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[kt][i]), sc[kt][i + 1]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+      const bool raise = mx > m_run + kLazy;
+      if (__builtin_expect(__ballot(raise) != 0, 0)) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < C::kDT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+      }
+    }
+    fused(slot, sc, sn);  // S(i+1) is speculative when step i+1 starts a new tile
     if (!pipe) {
       finish_tile();
       if (!s1.valid) return false;
       start_tile(s1);
-      if (vis1) qk(slot ^ 1, sn);
+      qk(slot ^ 1, sn);
     }
-    vis0 = vis1;
     s0 = s1;
     s1 = cur;
     advance();

@@ -39,6 +39,8 @@
  *     sa_last_error() describes it.
  *   - Thread safety: calls are reentrant; the error text is per thread.  Calls
  *     that share a workspace must be ordered on one stream.
+ *   - Q, K and V must be finite (no NaN or infinity); results are unspecified
+ *     otherwise.
  */
 #ifndef SPARSE_ATTN_H
 #define SPARSE_ATTN_H
