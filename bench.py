@@ -76,35 +76,45 @@ def traffic_from_profiles(kernel_src: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline_prefill(inp, block_idx, block_cnt, budget_head0):
+def cpu_baseline_prefill(inp, block_idx, block_cnt, tiles_per_head=40, select_heads=(0, 8, 16, 24)):
     """The fp64 oracle on a bounded sample of the prefill workload, scaled to ms
-    per layer: selection for one query head (every row), attention for 32 tiles
-    of that head; selection scaled by the head count, attention by attended pairs."""
+    per layer: selection (pool, score, top-k over every query block) for a few
+    query heads, scaled by the head count; attention for evenly spaced tiles of
+    every query head, scaled by attended pairs."""
     import numpy as np
     import oracle as O
     from head_heterogeneous_block_amd import metrics as M
     from head_heterogeneous_block_amd import workloads as W
     spec = inp.spec
     G = spec.group
-    q = W.to_numpy(inp.q[:, [0]])
-    k = W.to_numpy(inp.k[:, [0]])
-    v = W.to_numpy(inp.v[:, [0]])
-    t0 = time.perf_counter()
-    O.select_blocks_prefill(q, k, budget_head0, spec.block)
-    t_sel = time.perf_counter() - t0
+    t_sel = 0.0
+    for h in select_heads:
+        q = W.to_numpy(inp.q[:, [h]])
+        k = W.to_numpy(inp.k[:, [h // G]])
+        bud = {k2: np.asarray(v2)[[h]] for k2, v2 in inp.budget.items()}
+        t0 = time.perf_counter()
+        O.select_blocks_prefill(q, k, bud, spec.block)
+        t_sel += time.perf_counter() - t0
     nb = spec.n_blocks
-    ms = np.linspace(0, nb - 1, 32).astype(int)
-    sub_idx = block_idx[:, [0]]
-    sub_cnt = block_cnt[:, [0]]
-    t0 = time.perf_counter()
-    O.attention_prefill_gather(q, k, v, sub_idx, sub_cnt, spec.block, tiles=[(0, 0, int(m)) for m in ms])
-    t_att = time.perf_counter() - t0
-    mask = np.zeros_like(sub_cnt)
-    mask[0, 0, ms] = sub_cnt[0, 0, ms]
-    pairs_sample = M.prefill_pairs(sub_idx, mask, spec.seq_len, spec.block)
+    ms = np.unique(np.linspace(0, nb - 1, tiles_per_head).astype(int))
+    t_att = 0.0
+    mask = np.zeros_like(block_cnt)
+    for h in range(spec.n_q_heads):
+        q = W.to_numpy(inp.q[:, [h]])
+        k = W.to_numpy(inp.k[:, [h // G]])
+        v = W.to_numpy(inp.v[:, [h // G]])
+        t0 = time.perf_counter()
+        O.attention_prefill_gather(q, k, v, block_idx[:, [h]], block_cnt[:, [h]], spec.block,
+                                   tiles=[(0, 0, int(m)) for m in ms])
+        t_att += time.perf_counter() - t0
+        mask[0, h, ms] = block_cnt[0, h, ms]
+    pairs_sample = M.prefill_pairs(block_idx, mask, spec.seq_len, spec.block)
     pairs_all = M.prefill_pairs(block_idx, block_cnt, spec.seq_len, spec.block)
-    total_s = t_sel * spec.n_q_heads + t_att * pairs_all / pairs_sample
-    return total_s * 1e3, t_sel + t_att
+    total_s = t_sel * spec.n_q_heads / len(select_heads) + t_att * pairs_all / pairs_sample
+    desc = (f"selection of query heads {list(select_heads)} (all {nb} query blocks each) scaled by "
+            f"{spec.n_q_heads}/{len(select_heads)}; attention of {len(ms)} evenly spaced query blocks of each of "
+            f"the {spec.n_q_heads} heads ({pairs_sample / pairs_all:.2%} of attended pairs) scaled by attended pairs")
+    return total_s * 1e3, t_sel + t_att, desc
 
 
 def cpu_baseline_decode(inp, block_idx, block_cnt):
@@ -260,12 +270,10 @@ def main():
             cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         except Exception:  # noqa: BLE001
             cores = len(os.sched_getaffinity(0))
-        bud0 = {k2: np.asarray(v2)[[0]] for k2, v2 in pin.budget.items()}
-        cpu_ms, spent = cpu_baseline_prefill(pin, bidx, bcnt, bud0)
+        cpu_ms, spent, desc = cpu_baseline_prefill(pin, bidx, bcnt)
         cpu = {"value": cpu_ms, "unit": "ms/layer", "cores": int(cores), "kind": "oracle",
-               "sample": f"fp64 oracle on {pspec.name}: selection of query head 0 (all {pspec.n_blocks} rows) "
-                         f"scaled by {pspec.n_q_heads} heads, attention of 32 tiles of head 0 scaled by "
-                         f"attended pairs; {spent:.1f} s of CPU work"}
+               "sample": f"fp64 oracle on {pspec.name}: {desc}; {spent:.1f} s of CPU work"}
+        print(f"[bench] cpu baseline (prefill) {spent:.1f} s", file=sys.stderr, flush=True)
         if args.only == "all":
             dms, dspent = cpu_baseline_decode(din, dbidx, dbcnt)
             cpu_dec = {"value": dms, "unit": "ms/step", "sample": f"sequence 0 of {dspec.batch}, scaled; "

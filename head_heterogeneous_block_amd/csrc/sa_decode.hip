@@ -19,6 +19,8 @@
 //   combine : fixed-order merge of the chunk partials per (sequence, head).
 // No floating-point atomics: results are bitwise reproducible.
 
+#include <type_traits>
+
 #include "sa_device.hpp"
 #include "sa_kernels.hpp"
 
@@ -265,6 +267,198 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------- attend, bf16 on MFMA
+// One wave per workgroup and per chunk of the union atom list.  The wave
+// streams its atoms through a ring of kDStages LDS stages (one stage = K and V
+// rows of one 16-token atom, gathered with direct-to-LDS buffer loads, so
+// three atoms are in flight while one is computed) and keeps no barrier.
+// Per atom, with the group's query heads as the MFMA columns (zero beyond G):
+//   S^T[key][head] = K Q^T   v_mfma_f32_16x16x32_bf16: A = K rows (LDS,
+//                            16 bytes per lane), B = Q^T (registers);
+//                            lane element i <-> key 4*(lane/16) + i.
+//   O^T[d][head] += V^T P^T  v_mfma_f32_16x16x16_bf16: A = V^T read with
+//                            ds_read_b64_tr_b16, B = P^T straight from the
+//                            S^T accumulators (same key <-> lane layout).
+// Keys whose atom a head did not select, and tokens past the cache end, get
+// probability 0.  Softmax in the log2 domain with a lazily raised running max
+// (raised only when a score beats it by more than 2^kLazy), as in prefill.
+constexpr int kDStages = 4;
+constexpr float kDLazy = 8.f;
+
+template <int D>
+struct DCfg {
+  static constexpr int kRow = D * 2;                 // bytes per K or V row
+  static constexpr int kCpr = kRow / 16;             // 16-byte chunks per row
+  static constexpr int kAtomBytes = kAtom * kRow;    // one tensor's rows of an atom
+  static constexpr int kInsts = kAtomBytes / 1024;   // 1 KB direct loads per tensor and atom
+  static constexpr int kDK = D / 32;                 // k-steps of Q K^T
+  static constexpr int kDT = D / 16;                 // d-tiles of O^T
+  static constexpr int kRowsPer256 = kRow >= 256 ? 1 : 256 / kRow;
+  static constexpr int kKMask = (kCpr < 16 ? kCpr : 16) - 1;
+  // K (16-byte reads, 16 rows per group of lanes) and V (transposed 8-byte
+  // reads of 32-byte row pieces, 4 rows per group): the swizzles spread the
+  // rows read together over distinct LDS banks; V's is even, so the two
+  // 16-byte halves of a 32-byte piece stay adjacent.
+  __device__ static int swz_k(int row) { return (row / kRowsPer256) & kKMask; }
+  __device__ static int swz_v(int row) { return (2 * (row / kRowsPer256)) & (kCpr - 1); }
+  static_assert(kInsts * 1024 == kAtomBytes, "atom rows must fill whole 1 KB loads");
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p) {
+  using C = DCfg<D>;
+  // LDS ring: one variable per stage (K and V rows of one atom each)
+  __shared__ __attribute__((aligned(1024))) char k0[C::kAtomBytes], k1[C::kAtomBytes], k2[C::kAtomBytes],
+      k3[C::kAtomBytes];
+  __shared__ __attribute__((aligned(1024))) char v0[C::kAtomBytes], v1[C::kAtomBytes], v2[C::kAtomBytes],
+      v3[C::kAtomBytes];
+  static_assert(kDStages == 4, "stage variables");
+
+  const int c = blockIdx.x, j = blockIdx.y, bi = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int col = lane & 15;  // MFMA column (query head of the group) / A row
+  const int qg = lane >> 4;   // 16-lane group: k-group of A/B, row group of the output
+  const int nu = p.n_union[(int64_t)bi * p.Hkv + j];
+  const int a_beg = c * p.chunk_atoms;
+  if (a_beg >= nu) return;
+  const int na = min(nu - a_beg, p.chunk_atoms);  // <= 64
+  const uint32_t aw = lane < na ? p.atoms[((int64_t)bi * p.Hkv + j) * p.max_union + a_beg + lane] : 0u;
+
+  // Q^T fragments: lane holds head `col`, d = 32 s + 8 qg .. +7
+  u32x4 qf[C::kDK];
+  {
+    const bool ok = col < p.G;
+    const bf16_t* qrow = reinterpret_cast<const bf16_t*>(p.q) + bi * p.qs0 + (j * p.G + (ok ? col : 0)) * p.qs1;
+#pragma unroll
+    for (int s = 0; s < C::kDK; ++s)
+      qf[s] = ok ? *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * qg) : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const int krs = int(p.ks2 * 2), vrs = int(p.vs2 * 2);
+  const i32x4 krsrc = buffer_rsrc_words(reinterpret_cast<const bf16_t*>(p.k) + bi * p.ks0 + j * p.ks1, p.kv_len * krs);
+  const i32x4 vrsrc = buffer_rsrc_words(reinterpret_cast<const bf16_t*>(p.v) + bi * p.vs0 + j * p.vs1, p.kv_len * vrs);
+  // Direct load u of a tensor writes LDS bytes 1024 u + 16 lane: stage row r,
+  // physical chunk cp; it fetches the row's logical chunk cp ^ swizzle.
+  int k_voff[C::kInsts], v_voff[C::kInsts];
+#pragma unroll
+  for (int u = 0; u < C::kInsts; ++u) {
+    const int byte = u * 1024 + lane * 16;
+    const int r = byte / C::kRow, cp = (byte % C::kRow) / 16;
+    k_voff[u] = r * krs + (cp ^ C::swz_k(r)) * 16;
+    v_voff[u] = r * vrs + (cp ^ C::swz_v(r)) * 16;
+  }
+  auto kst = [&](auto S) -> char* {
+    constexpr int s = decltype(S)::value;
+    return s == 0 ? k0 : s == 1 ? k1 : s == 2 ? k2 : k3;
+  };
+  auto vst = [&](auto S) -> char* {
+    constexpr int s = decltype(S)::value;
+    return s == 0 ? v0 : s == 1 ? v1 : s == 2 ? v2 : v3;
+  };
+  // issue the loads of atom `ai` of the chunk into stage S
+  auto issue = [&](auto S, int ai) {
+    const int atom = int(uint32_t(__builtin_amdgcn_readlane(int(aw), ai)) & 0xffffffu);
+    const int ko = atom * kAtom * krs, vo = atom * kAtom * vrs;
+#pragma unroll
+    for (int u = 0; u < C::kInsts; ++u) dma16_async(krsrc, kst(S) + u * 1024, k_voff[u] + ko);
+#pragma unroll
+    for (int u = 0; u < C::kInsts; ++u) dma16_async(vrsrc, vst(S) + u * 1024, v_voff[u] + vo);
+  };
+
+  f32x4 oacc[C::kDT];
+#pragma unroll
+  for (int t = 0; t < C::kDT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_part = 0.f;
+  const float c2 = p.scale_log2;
+
+  auto step = [&](auto S, int i) {
+    // loads of atom i + 3 go to the stage atom i - 1 used (its reads are done)
+    using SN = std::integral_constant<int, (decltype(S)::value + kDStages - 1) % kDStages>;
+    if (i + kDStages - 1 < na) issue(SN{}, i + kDStages - 1);
+    // wait for atom i: the loads of the atoms after it may stay in flight
+    const int after = min(na - 1 - i, kDStages - 1);
+    if (after >= 3) wait_vmcnt<3 * 2 * C::kInsts>();
+    else if (after == 2) wait_vmcnt<2 * 2 * C::kInsts>();
+    else if (after == 1) wait_vmcnt<2 * C::kInsts>();
+    else wait_vmcnt<0>();
+    const char* ks = kst(S);
+    const char* vs = vst(S);
+    const uint32_t at = uint32_t(__builtin_amdgcn_readlane(int(aw), i));
+    const int tok0 = int(at & 0xffffffu) * kAtom;
+    const bool sel = col < 8 && ((at >> (24 + col)) & 1u);  // head mask: bits 24 + head
+
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < C::kDK; ++s) {
+      const u32x4 a = lds16(ks, col * C::kRow + ((4 * s + qg) ^ C::swz_k(col)) * 16);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[s]),
+                                                     sacc, 0, 0, 0);
+    }
+    float sv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sv[e] = (sel && tok0 + 4 * qg + e < p.kv_len) ? sacc[e] : kNegInf;
+    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mt = mx * c2;
+    const bool raise = mt > m_run + kDLazy;
+    if (__builtin_expect(__ballot(raise) != 0, 0)) {
+      const float m_new = raise ? mt : m_run;
+      const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 when raised from -inf
+      l_part *= alpha;
+#pragma unroll
+      for (int t = 0; t < C::kDT; ++t) oacc[t] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float pr[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c2, -m_use));
+    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const uint32_t pk0 = pack_bf16x2(pr[0], pr[1]), pk1 = pack_bf16x2(pr[2], pr[3]);
+    const v4i16 pb = __builtin_bit_cast(v4i16, uint2{pk0, pk1});
+    // V^T fragments: source lane (group qg, index jj) points at V row
+    // 4 qg + jj / 4, columns 16 t + 4 (jj % 4) .. +3; the lane receives
+    // V[4 qg .. 4 qg + 3][16 t + jj].
+    const int jj = lane & 15;
+    const int vr = 4 * qg + (jj >> 2);
+#pragma unroll
+    for (int t = 0; t < C::kDT; ++t) {
+      const int d = 16 * t + 4 * (jj & 3);
+      const v4i16 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(vs + vr * C::kRow + (((d >> 3) ^ C::swz_v(vr)) << 4) + ((d & 7) << 1)));
+      oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, oacc[t], 0, 0, 0);
+    }
+  };
+
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (na > 1) issue(std::integral_constant<int, 1>{}, 1);
+  if (na > 2) issue(std::integral_constant<int, 2>{}, 2);
+  for (int i = 0; i < na; i += kDStages) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 >= na) break;
+    step(std::integral_constant<int, 1>{}, i + 1);
+    if (i + 2 >= na) break;
+    step(std::integral_constant<int, 2>{}, i + 2);
+    if (i + 3 >= na) break;
+    step(std::integral_constant<int, 3>{}, i + 3);
+  }
+
+  // partial state of this chunk: heads col < G; lane (col, qg) holds
+  // d = 16 t + 4 qg .. +3
+  float l = l_part + __shfl_xor(l_part, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (col < p.G) {
+    const int64_t r = (((int64_t)bi * p.Hkv + j) * p.n_chunks + c) * p.G + col;
+#pragma unroll
+    for (int t = 0; t < C::kDT; ++t) *reinterpret_cast<f32x4*>(p.part_o + r * D + 16 * t + 4 * qg) = oacc[t];
+    if (qg == 0) {
+      p.part_ml[r * 2 + 0] = m_run;
+      p.part_ml[r * 2 + 1] = l;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- combine
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeCombineParams p, int dtype) {
@@ -302,9 +496,9 @@ hipError_t launch_decode_plan(const DecodePlanParams& p, int batch, hipStream_t 
 hipError_t launch_decode_attn(const DecodeAttnParams& p, int dtype, int D, int batch, hipStream_t stream) {
   dim3 grid(p.n_chunks, p.Hkv, batch);
   if (dtype == 0) {
-    if (D == 128 && p.G <= 4) hipLaunchKernelGGL((decode_attn_kernel<bf16_t, 128, 4, 4>), grid, dim3(256), 0, stream, p);
-    else if (D == 128 && p.G <= 8) hipLaunchKernelGGL((decode_attn_kernel<bf16_t, 128, 8, 8>), grid, dim3(256), 0, stream, p);
-    else if (D == 64 && p.G <= 8) hipLaunchKernelGGL((decode_attn_kernel<bf16_t, 64, 4, 8>), grid, dim3(256), 0, stream, p);
+    if (p.G > 8 || p.chunk_atoms > 64) return hipErrorInvalidValue;
+    if (D == 128) hipLaunchKernelGGL(decode_attn_mfma_kernel<128>, grid, dim3(64), 0, stream, p);
+    else if (D == 64) hipLaunchKernelGGL(decode_attn_mfma_kernel<64>, grid, dim3(64), 0, stream, p);
     else return hipErrorInvalidValue;
   } else {
     if (D == 128 && p.G <= 4) hipLaunchKernelGGL((decode_attn_kernel<float, 128, 4, 4>), grid, dim3(256), 0, stream, p);

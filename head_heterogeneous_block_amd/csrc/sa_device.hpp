@@ -14,6 +14,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -62,6 +65,53 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 }
 
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ u32x4 lds16(const char* base, int off) { return *reinterpret_cast<const u32x4*>(base + off); }
+
+// Raw buffer resource over [base, base + bytes): loads at offsets >= bytes
+// return zero.  The range check covers the per-lane (vector) offset, so every
+// row offset goes there; the scalar offset argument of dma16 stays 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from a buffer straight into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 ... lds).  The builtin only exists for the device
+// target, so the host pass of the single-source compile sees an empty body.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+#else
+  (void)r, (void)lds, (void)voff;
+#endif
+}
+
+// The same load issued from inline assembly, for pipelines that keep several
+// loads in flight while they read other LDS buffers.  The compiler does not see
+// this as an LDS write (so it inserts no wait before unrelated LDS reads); the
+// caller waits with wait_vmcnt before it reads the bytes.  The resource is
+// passed as four dwords: base (48 bits), stride 0, num_records, flags.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buffer_rsrc_words(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xffffu), bytes, 0x00020000};
+}
+__device__ __forceinline__ void dma16_async(i32x4 r, char* lds, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t m = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m), "v"(voff), "s"(r) : "memory");
+#else
+  (void)r, (void)lds, (void)voff;
+#endif
+}
+
+// s_waitcnt vmcnt(n) with lgkmcnt and expcnt left free (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Exact integer budget rule: k = min(n, max(min_blocks, ceil(ratio_q16 * n / 2^16))).
 __host__ __device__ __forceinline__ int budget_blocks(int n, int min_blocks, uint32_t ratio_q16) {

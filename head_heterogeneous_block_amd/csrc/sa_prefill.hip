@@ -50,25 +50,8 @@ namespace {
 constexpr int kKS = 64;       // keys per step
 constexpr float kLazy = 8.f;  // log2 headroom before the running max is raised
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
 // swap bits 2 and 3 of a key index (an involution)
 __device__ __forceinline__ int perm_key(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
-
-__device__ __forceinline__ u32x4 lds16(const char* base, int off) { return *reinterpret_cast<const u32x4*>(base + off); }
-
-// 16 bytes per lane from a buffer straight into LDS at lds + 16 * lane
-// (buffer_load_dwordx4 ... lds).  The builtin only exists for the device
-// target, so the host pass of the single-source compile sees an empty body.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int voff, int soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
-#else
-  (void)r, (void)lds, (void)voff, (void)soff;
-#endif
-}
 
 template <typename T, int D, int B>
 struct Cfg {
@@ -253,14 +236,14 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                            ? reinterpret_cast<const char*>(p.k) + (s.kb * p.ks0 + s.kh * p.ks1) * (int64_t)sizeof(T)
                            : reinterpret_cast<const char*>(p.v) + (s.kb * p.vs0 + s.kh * p.vs1) * (int64_t)sizeof(T);
     const int rs = k_side ? krs : vrs;
-    const auto r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, S * rs, 0x00020000);
+    const auto r = buffer_rsrc(base, S * rs);
     const int so = (s.n * B + s.hs * kKS) * rs;
     char* dst = (k_side ? kring : vring) + slot * C::kTile + wave * C::kInstsPerWave * 1024;
 #pragma unroll
-    for (int u = 0; u < C::kInstsPerWave; ++u) dma16(r, dst + u * 1024, k_side ? k_voff[u] : v_voff[u], so);
+    for (int u = 0; u < C::kInstsPerWave; ++u) dma16(r, dst + u * 1024, (k_side ? k_voff[u] : v_voff[u]) + so);
   };
   // all of this wave's direct loads have landed in LDS (vmcnt(0) only)
-  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  auto wait_loads = [&]() { wait_vmcnt<0>(); };
 
   // ---------------------------------------------------------------- tile state
   u32x4 qf[C::kDG];  // Q^T fragments of the wave's 32 queries
