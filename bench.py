@@ -76,7 +76,7 @@ def traffic_from_profiles(kernel_src: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline_prefill(inp, block_idx, block_cnt, tiles_per_head=40, select_heads=(0, 8, 16, 24)):
+def cpu_baseline_prefill(inp, block_idx, block_cnt, tiles_per_head=96, select_heads=(0, 4, 8, 12, 16, 20, 24, 28)):
     """The fp64 oracle on a bounded sample of the prefill workload, scaled to ms
     per layer: selection (pool, score, top-k over every query block) for a few
     query heads, scaled by the head count; attention for evenly spaced tiles of
@@ -257,6 +257,10 @@ def main():
         cont.n_bins = n_bins
         ablation["contiguous_bins_ms"] = timed(lambda: cont.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
         ablation["lpt_bins_ms"] = res["att_ms"]
+        asg = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, bin_order="lpt")
+        asg.block_idx = plan.block_idx
+        asg.block_cnt = plan.block_cnt
+        ablation["lpt_bins_assignment_order_ms"] = timed(lambda: asg.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
         loads = plan.counts.reshape(-1).astype(np.int64)
         cont_load = np.add.reduceat(loads, offs[:-1]) if n_t else loads
         ablation["lpt_makespan_over_mean"] = float(plan.bin_load.max() / plan.bin_load.mean())

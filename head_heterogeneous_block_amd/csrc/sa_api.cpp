@@ -287,6 +287,16 @@ sa_status sa_lpt_schedule(const int64_t* loads, int32_t n_items, int32_t n_bins,
   return ok();
 }
 
+sa_status sa_lpt_order_bins(const int32_t* bin_offsets, int32_t n_bins, int32_t* items_by_bin) {
+  if (n_bins < 1 || !bin_offsets) return fail(SA_ERR_INVALID_ARG, "bin_offsets is NULL or n_bins < 1");
+  if (bin_offsets[0] != 0) return fail(SA_ERR_INVALID_ARG, "bin_offsets[0] must be 0");
+  for (int32_t b = 0; b < n_bins; ++b)
+    if (bin_offsets[b + 1] < bin_offsets[b]) return fail(SA_ERR_INVALID_ARG, "bin_offsets must not decrease");
+  if (bin_offsets[n_bins] > 0 && !items_by_bin) return fail(SA_ERR_INVALID_ARG, "items_by_bin is NULL");
+  for (int32_t b = 0; b < n_bins; ++b) std::sort(items_by_bin + bin_offsets[b], items_by_bin + bin_offsets[b + 1]);
+  return ok();
+}
+
 sa_status sa_prefill_block_counts(const sa_attn_desc* desc, const sa_head_budget* budgets, int32_t* counts,
                                   int32_t* kmax) {
   sa_status s = check_desc(desc, true);

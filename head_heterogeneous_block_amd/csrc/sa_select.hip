@@ -10,9 +10,10 @@
 //    token budget per head (same pages §1).
 //
 // Top-k is exact: scores become order-preserving 32-bit keys; the k'-th largest
-// key is found by a 32-step bitwise search over block-wide counts; blocks with a
-// larger key, and the first (lowest-index) ties, are kept.  Candidates are
-// scanned in index order, so the output comes out ascending with no sort.
+// key is found by a byte-wise radix select over block-wide histograms; blocks
+// with a larger key, and the first (lowest-index) ties, are kept.  Candidates
+// are laid out in index order over the threads, so the output comes out
+// ascending with no sort.
 
 #include "sa_device.hpp"
 #include "sa_kernels.hpp"
@@ -129,36 +130,24 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(PrefillScoreParams 
 }
 
 // ---------------------------------------------------------------- top-k
+// Exclusive prefix sum (in thread order) of a per-thread count; returns the total.
 template <int NT>
-__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* red) {
-  x = wave_sum_u32(x);
-  if constexpr (NT == 64) {
-    return x;
-  } else {
-    const int w = threadIdx.x >> 6;
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[w] = x;
-    __syncthreads();
-    uint32_t t = 0;
+__device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t& before, uint32_t* red) {
+  const int lane = threadIdx.x & 63;
+  uint32_t inc = x;
 #pragma unroll
-    for (int i = 0; i < NT / 64; ++i) t += red[i];
-    return t;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
   }
-}
-
-// Exclusive prefix (in thread order) of a per-thread flag; returns the total.
-template <int NT>
-__device__ __forceinline__ uint32_t block_prefix(bool flag, uint32_t& before, uint32_t* red) {
-  const uint64_t b = __ballot(flag);
-  const uint32_t in_wave = lanes_below(b);
-  const uint32_t wave_tot = __popcll(b);
+  const uint32_t wave_tot = __shfl(inc, 63, 64);
   if constexpr (NT == 64) {
-    before = in_wave;
+    before = inc - x;
     return wave_tot;
   } else {
     const int w = threadIdx.x >> 6;
     __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[w] = wave_tot;
+    if (lane == 63) red[w] = wave_tot;
     __syncthreads();
     uint32_t off = 0, tot = 0;
 #pragma unroll
@@ -166,14 +155,24 @@ __device__ __forceinline__ uint32_t block_prefix(bool flag, uint32_t& before, ui
       off += (i < w) ? red[i] : 0u;
       tot += red[i];
     }
-    before = off + in_wave;
+    before = off + inc - x;
     return tot;
   }
 }
 
+// Thread t owns candidates [t*CPT, t*CPT + CPT) of its row.  The kk-th largest
+// key among the non-forced candidates is found by a radix select over the four
+// bytes of the key (most significant first): a 256-bin histogram of the keys
+// that match the bytes fixed so far, then the bin in which the count from the
+// top reaches kk.  Keys above the threshold are kept, and of the keys equal to
+// it the lowest-index ones; two block-wide scans place the kept candidates in
+// index order.
 template <int NT, int CPT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
-  __shared__ uint32_t red[NT / 64 > 0 ? NT / 64 : 1];
+  constexpr int kDPT = 256 / NT;  // histogram bins per thread
+  __shared__ uint32_t red[NT / 64];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t found[3];
   const int row = blockIdx.x;
   if (row >= p.rows) return;
   const int tid = threadIdx.x;
@@ -212,46 +211,88 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     return;
   }
 
+  // keys of the rankable candidates; 0 marks "not rankable" (no float maps to 0)
   const float* srow = p.s + (int64_t)row * p.s_row;
+  const int n0 = tid * CPT;
   uint32_t key[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    const int n = c * NT + tid;
+    const int n = n0 + c;
     key[c] = (n < n_cand && !forced(n)) ? ordered_key(srow[n]) : 0u;
   }
-  // largest T with count(key >= T) >= kk, i.e. the kk-th largest key
-  uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    uint32_t c = 0;
+
+  uint32_t prefix = 0, pmask = 0, need = (uint32_t)kk;
+  uint32_t T = 0, ties_wanted = 0;
+  bool done = false;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0 && !done; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) c += key[i] >= cand ? 1u : 0u;
-    c = block_sum<NT>(c, red);
-    if (c >= (uint32_t)kk) {
-      T = cand;
-      if (c == (uint32_t)kk) break;  // exactly kk keys >= T: no tie to resolve
+    for (int c = 0; c < CPT; ++c)
+      if (key[c] != 0u && (key[c] & pmask) == prefix) atomicAdd(&hist[(key[c] >> shift) & 255u], 1u);
+    __syncthreads();
+    // bins in descending digit order: thread t holds digits 255 - (kDPT t + u)
+    uint32_t hc[kDPT], loc = 0;
+#pragma unroll
+    for (int u = 0; u < kDPT; ++u) {
+      hc[u] = hist[255 - (kDPT * tid + u)];
+      loc += hc[u];
+    }
+    uint32_t above;
+    block_scan<NT>(loc, above, red);
+#pragma unroll
+    for (int u = 0; u < kDPT; ++u) {
+      if (above < need && above + hc[u] >= need) {
+        found[0] = 255u - uint32_t(kDPT * tid + u);
+        found[1] = need - above;
+        found[2] = hc[u];
+      }
+      above += hc[u];
+    }
+    __syncthreads();
+    const uint32_t digit = found[0], rem = found[1], bin = found[2];
+    prefix |= digit << shift;
+    pmask |= 255u << shift;
+    need = rem;
+    if (rem == bin && prefix != 0u) {
+      // every key of this bin is kept: threshold just below the bin
+      T = prefix - 1u;
+      ties_wanted = 0;
+      done = true;
+    } else if (shift == 0) {
+      T = prefix;
+      ties_wanted = rem;
+      done = true;
     }
   }
-  uint32_t gt = 0;
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) gt += key[i] > T ? 1u : 0u;
-  gt = block_sum<NT>(gt, red);
-  const uint32_t ties_wanted = (uint32_t)kk - gt;
-  uint32_t pos = 0, ties_seen = 0;
+
+  uint32_t n_tie = 0, n_gt = 0;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
-    if (c * NT >= n_cand) break;
-    const int n = c * NT + tid;
-    const bool valid = n < n_cand;
-    const bool is_tie = valid && !forced(n) && key[c] == T;
-    uint32_t tie_before;
-    const uint32_t tie_tot = block_prefix<NT>(is_tie, tie_before, red);
-    const bool take = valid && (forced(n) || key[c] > T || (is_tie && ties_seen + tie_before < ties_wanted));
-    uint32_t before;
-    const uint32_t tot = block_prefix<NT>(take, before, red);
-    if (take) out[pos + before] = n;
-    pos += tot;
-    ties_seen += tie_tot;
+    const int n = n0 + c;
+    if (n < n_cand) {
+      if (forced(n) || key[c] > T) ++n_gt;
+      else if (key[c] == T) ++n_tie;
+    }
+  }
+  uint32_t ties_before;
+  block_scan<NT>(n_tie, ties_before, red);
+  const uint32_t my_ties = ties_before >= ties_wanted ? 0u : min(n_tie, ties_wanted - ties_before);
+  uint32_t pos;
+  block_scan<NT>(n_gt + my_ties, pos, red);
+  uint32_t t_used = 0;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int n = n0 + c;
+    if (n < n_cand) {
+      bool take = forced(n) || key[c] > T;
+      if (!take && key[c] == T && t_used < my_ties) {
+        take = true;
+        ++t_used;
+      }
+      if (take) out[pos++] = n;
+    }
   }
 }
 

@@ -30,7 +30,7 @@ SA_BF16, SA_F32 = 0, 1
 MAX_HEADS = 128
 
 EXPORTED = [
-    "sa_version", "sa_last_error", "sa_lpt_schedule", "sa_prefill_block_counts", "sa_decode_block_counts",
+    "sa_version", "sa_last_error", "sa_lpt_schedule", "sa_lpt_order_bins", "sa_prefill_block_counts", "sa_decode_block_counts",
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_decode_workspace_size", "sa_sparse_attn_decode",
 ]
@@ -68,6 +68,7 @@ _SIG = {
     "sa_version": (ctypes.c_int32, []),
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_lpt_schedule": (ctypes.c_int32, [_i64p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
+    "sa_lpt_order_bins": (ctypes.c_int32, [_i32p, ctypes.c_int32, _i32p]),
     "sa_prefill_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
     "sa_decode_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
     "sa_decode_pooled_size": (ctypes.c_size_t, [_descp, _budp]),
@@ -178,6 +179,14 @@ def sa_lpt_schedule(loads: Sequence[int], n_bins: int):
     return bin_of, off, items, bl
 
 
+def sa_lpt_order_bins(bin_offsets: np.ndarray, items_by_bin: np.ndarray) -> np.ndarray:
+    """Copy of ``items_by_bin`` with every bin's items in ascending item order."""
+    off = np.ascontiguousarray(bin_offsets, dtype=np.int32)
+    items = np.array(items_by_bin, dtype=np.int32, copy=True)
+    _check(_lib.sa_lpt_order_bins(off.ctypes.data_as(_i32p), off.size - 1, items.ctypes.data_as(_i32p)))
+    return items
+
+
 def sa_prefill_block_counts(desc: sa_attn_desc, budgets) -> tuple[np.ndarray, int]:
     nb = -(-desc.q_len // desc.block_size)
     counts = np.empty((desc.batch, desc.n_q_heads, nb), np.int32)
@@ -253,10 +262,12 @@ def sa_sparse_attn_decode(desc: sa_attn_desc, budgets, q, k, v, o, lse, block_id
 class PrefillPlan:
     """Everything a prefill layer needs that depends only on shapes and budgets:
     descriptor, per-head budgets, block counts (LPT loads), kmax and the LPT
-    schedule over ``n_bins`` persistent workgroups (uploaded to the device)."""
+    schedule over ``n_bins`` persistent workgroups (uploaded to the device).
+    ``bin_order``: "index" walks each bin in item order (sa_lpt_order_bins),
+    "lpt" in assignment order."""
 
     def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
-                 kernel_variant: int = 0):
+                 kernel_variant: int = 0, bin_order: str = "index"):
         self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_prefill_block_counts(self.desc, self.budgets)
@@ -270,6 +281,10 @@ class PrefillPlan:
         self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
         if n_bins > 0:
             _, off, items, load = sa_lpt_schedule(self.counts.reshape(-1), n_bins)
+            if bin_order == "index":
+                items = sa_lpt_order_bins(off, items)
+            elif bin_order != "lpt":
+                raise ValueError(bin_order)
             self.bin_load = load
             self.bin_offsets = torch.from_numpy(off).to(dev)
             self.items_by_bin = torch.from_numpy(items).to(dev)

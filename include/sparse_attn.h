@@ -126,6 +126,19 @@ sa_status sa_lpt_schedule(const int64_t* loads, int32_t n_items, int32_t n_bins,
                           int32_t* bin_of_item, int32_t* bin_offsets, int32_t* items_by_bin,
                           int64_t* bin_load);
 
+/* Reorders the items of every bin ascending by item index, in place (host,
+ * synchronous).  The bins keep the same items and loads, so the makespan of
+ * the placement is unchanged; only the order in which a persistent workgroup
+ * walks its bin changes.  With prefill items numbered (b, h, m) head-major,
+ * every workgroup then moves through the heads in the same order, so at any
+ * moment the workgroups read the key and value blocks of the same few KV heads
+ * and those blocks are served from the caches.  The S-HPLB pages fix only
+ * which device (here: bin) an item goes to, not the order inside it.
+ *   bin_offsets[n_bins+1]  [host] as written by sa_lpt_schedule
+ *   items_by_bin[...]      [host] in/out
+ * Invalid offsets are SA_ERR_INVALID_ARG. */
+sa_status sa_lpt_order_bins(const int32_t* bin_offsets, int32_t n_bins, int32_t* items_by_bin);
+
 /* Blocks kept per prefill row, from the budget rule alone (no data needed):
  * counts[b][h][m] for m < ceil(q_len/block_size) ([host] out, int32), and the
  * maximum over all rows in *kmax ([host] out, may be NULL).  These are the

@@ -61,6 +61,22 @@ def test_lpt_golden_and_negative_load():
         SA.sa_lpt_schedule([3, -1], 2)
 
 
+def test_lpt_order_bins_keeps_bins_and_sorts():
+    """Reordering inside the bins: same item set per bin (so the same bin
+    loads), ascending inside each bin; bad offsets are rejected."""
+    rng = np.random.default_rng(5)
+    loads = rng.integers(1, 40, size=777)
+    bin_of, off, items, load = SA.sa_lpt_schedule(loads, 37)
+    got = SA.sa_lpt_order_bins(off, items)
+    for b in range(37):
+        seg, ref = got[off[b]:off[b + 1]], items[off[b]:off[b + 1]]
+        assert seg.tolist() == sorted(ref.tolist())
+        assert int(loads[seg].sum()) == int(load[b])
+        assert np.all(bin_of[seg] == b)
+    with pytest.raises(SA.SaError):
+        SA.sa_lpt_order_bins(np.array([0, 5, 3], np.int32), items)
+
+
 def test_lpt_on_config_tile_loads():
     """The tile loads of the 32K Llama-shaped workload scheduled onto 512 bins:
     identical to the oracle, and the makespan within one item of the mean."""
