@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) so that a "
+                         "counter run can scale its HBM byte counters")
     return ap.parse_args()
 
 
@@ -148,6 +151,14 @@ def main():
     stream = torch.cuda.current_stream(dev)
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     out = {}
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        print("[bench] calibration copy: 1 GiB read + 1 GiB written (torch.neg)", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- prefill
     pspec = W.CONFIGS[args.prefill_config]

@@ -489,7 +489,7 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
   dp.nc_max = w.nc_max;
   dp.Hq = desc->n_q_heads;
   dp.Hkv = desc->n_kv_heads;
-  dp.rows_per_wg = 256;
+  dp.rows_per_wg = 64;  // short streams: many waves balance better than long ones
   dp.scale = scale;
   // jobs: (KV head, granularity) -> the scoring heads, at most 8 per job
   std::vector<sa::DecodeScoreJob> jobs;

@@ -398,8 +398,7 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
 #pragma unroll
     for (int e = 0; e < 4; ++e) sv[e] = (sel && tok0 + 4 * qg + e < p.kv_len) ? sacc[e] : kNegInf;
     float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_xor32(max_xor16(mx));
     const float mt = mx * c2;
     const bool raise = mt > m_run + kDLazy;
     if (__builtin_expect(__ballot(raise) != 0, 0)) {
@@ -446,8 +445,7 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
 
   // partial state of this chunk: heads col < G; lane (col, qg) holds
   // d = 16 t + 4 qg .. +3
-  float l = l_part + __shfl_xor(l_part, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  const float l = sum_xor32(sum_xor16(l_part));
   if (col < p.G) {
     const int64_t r = (((int64_t)bi * p.Hkv + j) * p.n_chunks + c) * p.G + col;
 #pragma unroll
@@ -460,24 +458,58 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
 }
 
 // ---------------------------------------------------------------- combine
+// Fixed-order merge of the chunk partials of one (batch, query head):
+// o = sum_c w_c o_c / sum_c w_c l_c with w_c = 2^(m_c - max_c m_c).  The
+// weights of up to D chunks at a time go through LDS, so the loop over chunks
+// issues independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeCombineParams p, int dtype) {
+  constexpr int kW = D / 64;  // waves
+  __shared__ float w_s[D];
+  __shared__ float red[kW];
   const int h = blockIdx.x, bi = blockIdx.y;
   const int j = h / p.G, gi = h % p.G;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x, lane = d & 63, wv = d >> 6;
   const int nu = p.n_union[(int64_t)bi * p.Hkv + j];
   const int nch = (nu + p.chunk_atoms - 1) / p.chunk_atoms;
   const int64_t base = ((int64_t)bi * p.Hkv + j) * p.n_chunks;
+  auto ml = [&](int c, int k) { return p.part_ml[((base + c) * p.G + gi) * 2 + k]; };
   float mx = kNegInf;
-  for (int c = 0; c < nch; ++c) mx = fmaxf(mx, p.part_ml[((base + c) * p.G + gi) * 2]);
+  for (int c = d; c < nch; c += D) mx = fmaxf(mx, ml(c, 0));
+  mx = wave_max(mx);
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kW; ++i) mx = fmaxf(mx, red[i]);
   const float mu = mx == kNegInf ? 0.f : mx;
-  float acc = 0.f, l = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const int64_t r = (base + c) * p.G + gi;
-    const float f = __builtin_amdgcn_exp2f(p.part_ml[r * 2] - mu);
-    acc += p.part_o[r * D + d] * f;
-    l += p.part_ml[r * 2 + 1] * f;
+  float acc = 0.f, lp = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += D) {
+    const int c = c0 + d;
+    const float w = c < nch ? __builtin_amdgcn_exp2f(ml(c, 0) - mu) : 0.f;
+    lp += c < nch ? w * ml(c, 1) : 0.f;
+    __syncthreads();
+    w_s[d] = w;
+    __syncthreads();
+    const int cn = min(D, nch - c0);
+    const float* po = p.part_o + ((base + c0) * p.G + gi) * D + d;
+    int u = 0;
+    for (; u + 4 <= cn; u += 4) {
+      const float a0 = po[(int64_t)(u + 0) * p.G * D], a1 = po[(int64_t)(u + 1) * p.G * D];
+      const float a2 = po[(int64_t)(u + 2) * p.G * D], a3 = po[(int64_t)(u + 3) * p.G * D];
+      acc = fmaf(a0, w_s[u], acc);
+      acc = fmaf(a1, w_s[u + 1], acc);
+      acc = fmaf(a2, w_s[u + 2], acc);
+      acc = fmaf(a3, w_s[u + 3], acc);
+    }
+    for (; u < cn; ++u) acc = fmaf(po[(int64_t)u * p.G * D], w_s[u], acc);
   }
+  lp = wave_sum(lp);
+  __syncthreads();
+  if (lane == 0) red[wv] = lp;
+  __syncthreads();
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < kW; ++i) l += red[i];
   const float o = l > 0.f ? acc / l : 0.f;
   const int64_t oi = bi * p.os0 + h * p.os1 + d;
   if (p.out_f32 || dtype == 1) reinterpret_cast<float*>(p.o)[oi] = o;

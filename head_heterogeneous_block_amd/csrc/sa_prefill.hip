@@ -272,7 +272,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
   auto finish_tile = [&]() {
     const int bi = t_bh / p.Hq, h = t_bh % p.Hq;
-    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    const float l = sum_xor32(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int qrow = t_m * B + wave * 32 + col;
     if (qrow < S) {
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[kt][i]), sc[kt][i + 1]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c2;
+      mx = max_xor32(mx) * c2;
       const bool raise = mx > m_run + kLazy;
       if (__builtin_expect(__ballot(raise) != 0, 0)) {
         const float m_new = raise ? mx : m_run;

@@ -15,6 +15,8 @@
 // are laid out in index order over the threads, so the output comes out
 // ascending with no sort.
 
+#include <type_traits>
+
 #include "sa_device.hpp"
 #include "sa_kernels.hpp"
 
@@ -134,13 +136,8 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(PrefillScoreParams 
 template <int NT>
 __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t& before, uint32_t* red) {
   const int lane = threadIdx.x & 63;
-  uint32_t inc = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
-  }
-  const uint32_t wave_tot = __shfl(inc, 63, 64);
+  const uint32_t inc = wave_scan_incl(x);
+  const uint32_t wave_tot = uint32_t(__builtin_amdgcn_readlane(int(inc), 63));
   if constexpr (NT == 64) {
     before = inc - x;
     return wave_tot;
@@ -173,6 +170,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   __shared__ uint32_t red[NT / 64];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t found[3];
+  __shared__ uint32_t kbuf[NT * CPT + NT * CPT / 32];
   const int row = blockIdx.x;
   if (row >= p.rows) return;
   const int tid = threadIdx.x;
@@ -211,15 +209,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     return;
   }
 
-  // keys of the rankable candidates; 0 marks "not rankable" (no float maps to 0)
+  // keys of the rankable candidates; 0 marks "not rankable" (no float maps to
+  // 0).  Read coalesced into LDS (one pad word per 32 keys keeps the per-thread
+  // runs on distinct banks), then each thread takes its CPT consecutive keys.
   const float* srow = p.s + (int64_t)row * p.s_row;
+  for (int n = tid; n < NT * CPT; n += NT)
+    kbuf[n + (n >> 5)] = (n < n_cand && !forced(n)) ? ordered_key(srow[n]) : 0u;
+  __syncthreads();
   const int n0 = tid * CPT;
   uint32_t key[CPT];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int n = n0 + c;
-    key[c] = (n < n_cand && !forced(n)) ? ordered_key(srow[n]) : 0u;
-  }
+  for (int c = 0; c < CPT; ++c) key[c] = kbuf[(n0 + c) + ((n0 + c) >> 5)];
 
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)kk;
   uint32_t T = 0, ties_wanted = 0;
@@ -297,60 +297,103 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
 }
 
 // ---------------------------------------------------------------- decode scores
-// One workgroup scores rows_per_wg pooled blocks of one (batch, KV head,
-// granularity) against every scoring query head of that group and granularity.
-// 8 lanes share a pooled row (D/8 floats each); partial dots meet by xor-shuffle.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_scores_kernel(DecodeScoreParams p) {
-  constexpr int kLanes = 8;
-  constexpr int kPer = D / kLanes;  // floats per lane
+// One wave scores rows_per_wg pooled blocks of one (batch, KV head,
+// granularity) against every scoring query head of that group and granularity
+// (at most MAXH).  The fp32 pooled rows stream through a 4-stage LDS ring
+// (8 rows per stage, direct-to-LDS loads, three stages in flight); 16 lanes
+// share a row (D/16 floats each) and their partial dots meet by xor-shuffle.
+constexpr int kSStages = 4;
+
+template <typename T, int D, int MAXH>
+__global__ __launch_bounds__(64) void decode_scores_kernel(DecodeScoreParams p) {
+  constexpr int kRowB = D * 4;             // bytes per pooled row
+  constexpr int kSR = 8;                   // rows per stage
+  constexpr int kStageB = kSR * kRowB;
+  constexpr int kInsts = kStageB / 1024;   // 1 KB direct loads per stage
+  constexpr int kQ = D / 64;               // 16-byte pieces per lane and row
+  static_assert(kInsts * 1024 == kStageB, "stage must fill whole 1 KB loads");
+  __shared__ __attribute__((aligned(1024))) char st0[kStageB], st1[kStageB], st2[kStageB], st3[kStageB];
+  static_assert(kSStages == 4, "stage variables");
   const DecodeScoreJob& job = p.jobs[blockIdx.y];
   const int bi = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int sub = tid % kLanes;
-  const int rloc = tid / kLanes;  // 32 rows per pass
+  const int lane = threadIdx.x;
+  const int sub = lane & 15, rq = lane >> 4;
   const int nc = p.pool_nc[job.pool];
-  const float* kp = p.pooled + p.pool_off[job.pool] + ((int64_t)bi * p.Hkv + job.kvh) * nc * D;
-  float qv[8][kPer];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i >= job.n_heads) break;
-    const char* qrow = reinterpret_cast<const char*>(p.q) +
-                       (bi * p.qs0 + job.heads[i] * p.qs1) * (int64_t)sizeof(T);
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int d = sub * kPer + e;
-      if constexpr (sizeof(T) == 2)
-        qv[i][e] = bf16_to_f32(reinterpret_cast<const bf16_t*>(qrow)[d]);
-      else
-        qv[i][e] = reinterpret_cast<const float*>(qrow)[d];
-    }
-  }
   const int r0 = blockIdx.x * p.rows_per_wg;
-  const int r1 = min(nc, r0 + p.rows_per_wg);
-  // the 8 lanes of a row always take the same trip count, so the xor-shuffles
-  // below stay inside active lane groups
-  for (int r = r0 + rloc; r < r1; r += 256 / kLanes) {
-    float kv[kPer];
+  if (r0 >= nc) return;
+  const int nr = min(p.rows_per_wg, nc - r0);
+  const int n_st = (nr + kSR - 1) / kSR;
+  const int nh = job.n_heads;
+  const float* kp = p.pooled + p.pool_off[job.pool] + (((int64_t)bi * p.Hkv + job.kvh) * nc + r0) * D;
+  const i32x4 rsrc = buffer_rsrc_words(kp, nr * kRowB);  // rows past the chunk read zero
+
+  // query slices: lane holds d = 64 q + 4 sub .. +3 for q < kQ
+  f32x4 qv[MAXH][kQ];
 #pragma unroll
-    for (int e = 0; e < kPer; e += 4) {
-      const f32x4 w = *reinterpret_cast<const f32x4*>(kp + (int64_t)r * D + sub * kPer + e);
-      kv[e] = w[0];
-      kv[e + 1] = w[1];
-      kv[e + 2] = w[2];
-      kv[e + 3] = w[3];
+  for (int i = 0; i < MAXH; ++i) {
+    const int hh = job.heads[i < nh ? i : 0];
+    const T* qrow = reinterpret_cast<const T*>(p.q) + bi * p.qs0 + hh * p.qs1;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 64 * q + 4 * sub + e;
+        if constexpr (sizeof(T) == 2) qv[i][q][e] = bf16_to_f32(qrow[d]);
+        else qv[i][q][e] = qrow[d];
+      }
+  }
+  auto stage = [&](auto S) -> char* {
+    constexpr int s = decltype(S)::value;
+    return s == 0 ? st0 : s == 1 ? st1 : s == 2 ? st2 : st3;
+  };
+  auto issue = [&](auto S, int si) {
+#pragma unroll
+    for (int u = 0; u < kInsts; ++u) dma16_async(rsrc, stage(S) + u * 1024, si * kStageB + u * 1024 + lane * 16);
+  };
+  float* srow[MAXH];
+#pragma unroll
+  for (int i = 0; i < MAXH; ++i) srow[i] = p.s + ((int64_t)bi * p.Hq + job.heads[i < nh ? i : 0]) * p.nc_max + r0;
+
+  auto step = [&](auto S, int si) {
+    using SN = std::integral_constant<int, (decltype(S)::value + kSStages - 1) % kSStages>;
+    if (si + kSStages - 1 < n_st) issue(SN{}, si + kSStages - 1);
+    const int after = min(n_st - 1 - si, kSStages - 1);
+    if (after >= 3) wait_vmcnt<3 * kInsts>();
+    else if (after == 2) wait_vmcnt<2 * kInsts>();
+    else if (after == 1) wait_vmcnt<kInsts>();
+    else wait_vmcnt<0>();
+    const char* sp = stage(S);
+#pragma unroll
+    for (int pp = 0; pp < kSR / 4; ++pp) {
+      const int row = 4 * pp + rq;
+      f32x4 kv[kQ];
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) kv[q] = __builtin_bit_cast(f32x4, lds16(sp, row * kRowB + q * 256 + sub * 16));
+      const int r = si * kSR + row;
+#pragma unroll
+      for (int i = 0; i < MAXH; ++i) {
+        if (i >= nh) break;
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < kQ; ++q)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = fmaf(qv[i][q][e], kv[q][e], acc);
+        acc = row_sum16(acc);
+        if (sub == 0 && r < nr) srow[i][r] = acc * p.scale;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i >= job.n_heads) break;
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) acc = fmaf(qv[i][e], kv[e], acc);
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      acc += __shfl_xor(acc, 4, 64);
-      if (sub == 0) p.s[((int64_t)bi * p.Hq + job.heads[i]) * p.nc_max + r] = acc * p.scale;
-    }
+  };
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (n_st > 1) issue(std::integral_constant<int, 1>{}, 1);
+  if (n_st > 2) issue(std::integral_constant<int, 2>{}, 2);
+  for (int i = 0; i < n_st; i += kSStages) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 >= n_st) break;
+    step(std::integral_constant<int, 1>{}, i + 1);
+    if (i + 2 >= n_st) break;
+    step(std::integral_constant<int, 2>{}, i + 2);
+    if (i + 3 >= n_st) break;
+    step(std::integral_constant<int, 3>{}, i + 3);
   }
 }
 
@@ -402,16 +445,25 @@ hipError_t launch_topk(const TopkParams& p, int max_cand, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_scores(const DecodeScoreParams& p, int dtype, int D, int batch, hipStream_t stream) {
-  int max_nc = 0;
-  for (int i = 0; i < 4; ++i) max_nc = max(max_nc, p.pool_nc[i]);
-  dim3 grid((max_nc + p.rows_per_wg - 1) / p.rows_per_wg, p.n_jobs, batch);
-  if (dtype == 0 && D == 128) hipLaunchKernelGGL((decode_scores_kernel<bf16_t, 128>), grid, dim3(256), 0, stream, p);
-  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((decode_scores_kernel<bf16_t, 64>), grid, dim3(256), 0, stream, p);
-  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((decode_scores_kernel<float, 128>), grid, dim3(256), 0, stream, p);
-  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((decode_scores_kernel<float, 64>), grid, dim3(256), 0, stream, p);
+template <int MAXH>
+hipError_t decode_scores_launch(const DecodeScoreParams& p, int dtype, int D, dim3 grid, hipStream_t stream) {
+  if (dtype == 0 && D == 128) hipLaunchKernelGGL((decode_scores_kernel<bf16_t, 128, MAXH>), grid, dim3(64), 0, stream, p);
+  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((decode_scores_kernel<bf16_t, 64, MAXH>), grid, dim3(64), 0, stream, p);
+  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((decode_scores_kernel<float, 128, MAXH>), grid, dim3(64), 0, stream, p);
+  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((decode_scores_kernel<float, 64, MAXH>), grid, dim3(64), 0, stream, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_decode_scores(const DecodeScoreParams& p, int dtype, int D, int batch, hipStream_t stream) {
+  int max_nc = 0, max_h = 1;
+  for (int i = 0; i < 4; ++i) max_nc = max(max_nc, p.pool_nc[i]);
+  for (int i = 0; i < p.n_jobs; ++i) max_h = max(max_h, p.jobs[i].n_heads);
+  dim3 grid((max_nc + p.rows_per_wg - 1) / p.rows_per_wg, p.n_jobs, batch);
+  if (max_h <= 2) return decode_scores_launch<2>(p, dtype, D, grid, stream);
+  if (max_h <= 4) return decode_scores_launch<4>(p, dtype, D, grid, stream);
+  if (max_h <= 8) return decode_scores_launch<8>(p, dtype, D, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sa
