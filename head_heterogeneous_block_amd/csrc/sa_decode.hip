@@ -38,17 +38,31 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodePlanPar
   const int n_words = (p.n_atoms + 31) / 32;
   for (int i = tid; i < p.G * n_words; i += kPlanThreads) bits[i] = 0u;
   __syncthreads();
-  for (int gi = 0; gi < p.G; ++gi) {
-    const int h = j * p.G + gi;
-    const int g = p.heads.gran[h];
-    const int apb = g / kAtom;  // atoms per block
-    const int cnt = p.block_cnt[(int64_t)bi * p.Hq + h];
-    const int32_t* idx = p.block_idx + ((int64_t)bi * p.Hq + h) * p.kmax;
-    uint32_t* w = bits + gi * n_words;
-    for (int t = tid; t < cnt * apb; t += kPlanThreads) {
-      const int n = idx[t / apb];
-      const int a = n * apb + t % apb;
-      if (n >= 0 && a < p.n_atoms) atomicOr(&w[a >> 5], 1u << (a & 31));
+  // Every selected block sets its atoms' bits: a block of g = 16 * apb tokens
+  // covers apb consecutive atoms, all in one 32-bit word (apb divides 32 and
+  // the block starts at a multiple of apb).  The block indices of all heads of
+  // a round are loaded before any is used.
+  constexpr int kGM = 8;
+  int cnt[kGM], apb[kGM];
+#pragma unroll
+  for (int gi = 0; gi < kGM; ++gi) {
+    const int h = j * p.G + (gi < p.G ? gi : 0);
+    cnt[gi] = gi < p.G ? p.block_cnt[(int64_t)bi * p.Hq + h] : 0;
+    apb[gi] = p.heads.gran[h] / kAtom;
+  }
+  for (int b0 = 0; b0 < p.kmax; b0 += kPlanThreads) {
+    int nv[kGM];
+#pragma unroll
+    for (int gi = 0; gi < kGM; ++gi) {
+      const int b = b0 + tid;
+      nv[gi] = b < cnt[gi] ? p.block_idx[((int64_t)bi * p.Hq + j * p.G + gi) * p.kmax + b] : -1;
+    }
+#pragma unroll
+    for (int gi = 0; gi < kGM; ++gi) {
+      if (nv[gi] < 0) continue;
+      const int a = nv[gi] * apb[gi];
+      const int na = min(apb[gi], p.n_atoms - a);
+      if (na > 0) atomicOr(&bits[gi * n_words + (a >> 5)], ((na >= 32 ? 0u : (1u << na)) - 1u) << (a & 31));
     }
   }
   __syncthreads();
@@ -65,13 +79,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodePlanPar
       for (int gi = 0; gi < p.G; ++gi) u |= bits[gi * n_words + wi];
     const uint32_t c = __popc(u);
     // exclusive scan of c across the block
-    uint32_t x = c;
+    const uint32_t x = wave_scan_incl(c);
     const int lane = tid & 63, wv = tid >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
     if (lane == 63) wave_tot[wv] = x;
     __syncthreads();
     uint32_t off = base_s;

@@ -140,18 +140,21 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, int v
 }
 
 // The same load issued from inline assembly, for pipelines that keep several
-// loads in flight while they read other LDS buffers.  The compiler does not see
+// loads in flight while they read other LDS buffers.  The LDS address and the
+// resource must be wave-uniform (they are taken from the first active lane).  The compiler does not see
 // this as an LDS write (so it inserts no wait before unrelated LDS reads); the
 // caller waits with wait_vmcnt before it reads the bytes.  The resource is
 // passed as four dwords: base (48 bits), stride 0, num_records, flags.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 buffer_rsrc_words(const void* base, int bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return i32x4{int(uint32_t(a)), int(uint32_t(a >> 32) & 0xffffu), bytes, 0x00020000};
+  return i32x4{__builtin_amdgcn_readfirstlane(int(uint32_t(a))),
+               __builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
 }
 __device__ __forceinline__ void dma16_async(i32x4 r, char* lds, int voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const uint32_t m = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds));
+  const uint32_t m = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)lds)));
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m), "v"(voff), "s"(r) : "memory");
 #else
   (void)r, (void)lds, (void)voff;

@@ -213,24 +213,68 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   // 0).  Read coalesced into LDS (one pad word per 32 keys keeps the per-thread
   // runs on distinct banks), then each thread takes its CPT consecutive keys.
   const float* srow = p.s + (int64_t)row * p.s_row;
-  for (int n = tid; n < NT * CPT; n += NT)
-    kbuf[n + (n >> 5)] = (n < n_cand && !forced(n)) ? ordered_key(srow[n]) : 0u;
+  {
+    // all CPT loads of a thread issued before any is used (one round trip)
+    float v[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) v[c] = srow[min(c * NT + tid, n_cand - 1)];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int n = c * NT + tid;
+      kbuf[n + (n >> 5)] = (n < n_cand && !forced(n)) ? ordered_key(v[c]) : 0u;
+    }
+  }
   __syncthreads();
   const int n0 = tid * CPT;
   uint32_t key[CPT];
 #pragma unroll
   for (int c = 0; c < CPT; ++c) key[c] = kbuf[(n0 + c) + ((n0 + c) >> 5)];
 
+  // Radix select on keys relative to the row minimum: rel = key - kmin + 1
+  // (0 stays "not rankable").  Digits start at the top set bit of the range,
+  // so the first histogram already spreads keys of similar magnitude.
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c)
+    if (key[c] != 0u) {
+      kmin = min(kmin, key[c]);
+      kmax = max(kmax, key[c]);
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if constexpr (NT > 64) {
+    __shared__ uint32_t mm[2][NT / 64];
+    if ((tid & 63) == 0) {
+      mm[0][tid >> 6] = kmin;
+      mm[1][tid >> 6] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      kmin = min(kmin, mm[0][i]);
+      kmax = max(kmax, mm[1][i]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) key[c] = key[c] != 0u ? key[c] - kmin + 1u : 0u;  // now rel
+  const uint32_t range = kmax - kmin + 1u;  // >= 1: kk >= 1 rankable keys exist
+  const int bits = 32 - __clz(range);
+
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)kk;
-  uint32_t T = 0, ties_wanted = 0;
-  bool done = false;
+  uint32_t T = 0, ties_wanted = 0;  // on rel
+  int width = bits < 8 ? bits : 8;
+  int shift = bits - width;
 #pragma unroll 1
-  for (int shift = 24; shift >= 0 && !done; shift -= 8) {
+  while (true) {
+    const uint32_t dmask = (1u << width) - 1u;
     for (int i = tid; i < 256; i += NT) hist[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
-      if (key[c] != 0u && (key[c] & pmask) == prefix) atomicAdd(&hist[(key[c] >> shift) & 255u], 1u);
+      if (key[c] != 0u && (key[c] & pmask) == prefix) atomicAdd(&hist[(key[c] >> shift) & dmask], 1u);
     __syncthreads();
     // bins in descending digit order: thread t holds digits 255 - (kDPT t + u)
     uint32_t hc[kDPT], loc = 0;
@@ -253,20 +297,22 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     __syncthreads();
     const uint32_t digit = found[0], rem = found[1], bin = found[2];
     prefix |= digit << shift;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
     need = rem;
     if (rem == bin && prefix != 0u) {
       // every key of this bin is kept: threshold just below the bin
       T = prefix - 1u;
       ties_wanted = 0;
-      done = true;
-    } else if (shift == 0) {
+      break;
+    }
+    if (shift == 0) {
       T = prefix;
       ties_wanted = rem;
-      done = true;
+      break;
     }
+    width = shift < 8 ? shift : 8;
+    shift -= width;
   }
-
   uint32_t n_tie = 0, n_gt = 0;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
