@@ -346,6 +346,9 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     sn[0] = f32x16{};
     sn[1] = f32x16{};
     if constexpr (C::kBf16) {
+      // the wave in its MFMA section issues ahead of a wave that is waiting,
+      // fetching or advancing its cursor, so the MFMA pipe stays fed
+      __builtin_amdgcn_s_setprio(1);
       u32x4 pf[4];
       float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
@@ -410,6 +413,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (transposed)
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
       }
+      __builtin_amdgcn_s_setprio(0);
     } else {
       qk(slot ^ 1, sn);
       float psum = 0.f;
