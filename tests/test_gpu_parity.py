@@ -71,6 +71,8 @@ PREFILL_SHAPES = [
     ("d64-b128", dict(seq_len=1536, n_q_heads=4, n_kv_heads=1, head_dim=64)),
     ("b64", dict(seq_len=1500, n_q_heads=4, n_kv_heads=2, block=64)),
     ("one-block", dict(seq_len=100, n_q_heads=2, n_kv_heads=1)),
+    ("tiny-17", dict(seq_len=17, n_q_heads=2, n_kv_heads=1)),
+    ("one-token", dict(seq_len=1, n_q_heads=4, n_kv_heads=2)),
 ]
 
 
@@ -215,6 +217,36 @@ def test_decode_reduced_all(L):
     inp = W.make_decode(spec, 31, device=DEV)
     plan, o, lse = _decode_gpu(inp)
     _check_decode(inp, plan, o, lse, list(range(spec.batch)))
+
+
+@pytest.mark.parametrize("name,over", [
+    ("d64", dict(head_dim=64)),
+    ("gqa8", dict(n_q_heads=16, n_kv_heads=2, n_streaming=4)),
+    ("tiny-L", dict(kv_len=40, tok_lo=16, tok_hi=64, stream_local=4)),
+], ids=["d64", "gqa8", "tiny-L"])
+def test_decode_bf16_shapes(name, over):
+    """The bf16 MFMA decode path at other head sizes and group sizes, and a
+    cache shorter than one 64-token block (every head keeps all its blocks)."""
+    base = dict(batch=2, kv_len=4096 + 24, tok_lo=256, tok_hi=1024, stream_local=8)
+    base.update(over)
+    spec = W.CONFIGS[4].with_(**base)
+    _say("case: decode bf16", name)
+    inp = W.make_decode(spec, 33, device=DEV)
+    plan, o, lse = _decode_gpu(inp)
+    _check_decode(inp, plan, o, lse, list(range(spec.batch)))
+
+
+def test_decode_bf16_output():
+    """bf16 output: within the fp32 tolerance plus half a bf16 ulp of the value."""
+    spec = W.CONFIGS[4].with_(batch=2, kv_len=8192, tok_lo=256, tok_hi=2048, stream_local=16)
+    inp = W.make_decode(spec, 34, device=DEV)
+    plan, o, lse = _decode_gpu(inp, out_f32=False)
+    assert o.dtype == torch.bfloat16
+    q, k, v = W.to_numpy(inp.q), W.to_numpy(inp.k), W.to_numpy(inp.v)
+    gidx, gcnt = plan.block_idx.cpu().numpy(), plan.block_cnt.cpu().numpy()
+    ro, _ = O.decode_attention(q, k, v, gidx, gcnt, inp.budget["granularity"])
+    og = o.float().cpu().numpy()
+    assert np.all(np.abs(og - ro) <= TOL_BF16 + bf16_half_ulp(ro))
 
 
 def test_decode_gqa8_fp32():
