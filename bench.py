@@ -272,6 +272,12 @@ def main():
         asg.block_idx = plan.block_idx
         asg.block_cnt = plan.block_cnt
         ablation["lpt_bins_assignment_order_ms"] = timed(lambda: asg.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+        # two-level placement: chunks of (KV head, 64 query blocks) onto the 8 XCDs, then LPT inside each
+        xcd = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, xcd_groups=8, xcd_chunk=64)
+        xcd.block_idx = plan.block_idx
+        xcd.block_cnt = plan.block_cnt
+        ablation["lpt_xcd_two_level_ms"] = timed(lambda: xcd.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+        ablation["lpt_xcd_two_level_makespan_over_mean"] = float(xcd.bin_load.max() / xcd.bin_load.mean())
         loads = plan.counts.reshape(-1).astype(np.int64)
         cont_load = np.add.reduceat(loads, offs[:-1]) if n_t else loads
         ablation["lpt_makespan_over_mean"] = float(plan.bin_load.max() / plan.bin_load.mean())

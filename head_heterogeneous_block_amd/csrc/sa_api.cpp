@@ -287,6 +287,61 @@ sa_status sa_lpt_schedule(const int64_t* loads, int32_t n_items, int32_t n_bins,
   return ok();
 }
 
+sa_status sa_lpt_schedule_grouped(const int64_t* loads, const int32_t* chunk_of_item, int32_t n_items,
+                                  int32_t n_chunks, int32_t n_groups, int32_t n_bins, int32_t* bin_of_item,
+                                  int32_t* bin_offsets, int32_t* items_by_bin, int64_t* bin_load) {
+  if (n_items < 0 || n_chunks < 1 || n_groups < 1 || n_bins < 1) return fail(SA_ERR_INVALID_ARG, "bad sizes");
+  if (n_bins % n_groups) return fail(SA_ERR_INVALID_ARG, "n_bins %d is not a multiple of n_groups %d", n_bins, n_groups);
+  if (n_items > 0 && (!loads || !chunk_of_item || !bin_of_item || !items_by_bin))
+    return fail(SA_ERR_INVALID_ARG, "NULL array");
+  if (!bin_offsets) return fail(SA_ERR_INVALID_ARG, "bin_offsets is NULL");
+  std::vector<int64_t> cload(n_chunks, 0);
+  for (int32_t i = 0; i < n_items; ++i) {
+    if (loads[i] < 0) return fail(SA_ERR_INVALID_ARG, "load of item %d is negative", i);
+    if (chunk_of_item[i] < 0 || chunk_of_item[i] >= n_chunks)
+      return fail(SA_ERR_INVALID_ARG, "chunk of item %d out of range", i);
+    cload[chunk_of_item[i]] += loads[i];
+  }
+  // level 1: chunks onto groups; level 2: each group's items onto its bins
+  std::vector<int32_t> group_of_chunk(n_chunks), off1(n_groups + 1), tmp1(n_chunks);
+  sa_status st = sa_lpt_schedule(cload.data(), n_chunks, n_groups, group_of_chunk.data(), off1.data(), tmp1.data(),
+                                 nullptr);
+  if (st) return st;
+  const int32_t per = n_bins / n_groups;
+  std::vector<std::vector<int32_t>> bin_items(n_bins);
+  std::vector<int64_t> load(n_bins, 0);
+  std::vector<int32_t> members;
+  std::vector<int64_t> mload;
+  for (int32_t g = 0; g < n_groups; ++g) {
+    members.clear();
+    mload.clear();
+    for (int32_t i = 0; i < n_items; ++i)
+      if (group_of_chunk[chunk_of_item[i]] == g) {
+        members.push_back(i);
+        mload.push_back(loads[i]);
+      }
+    const int32_t m = int32_t(members.size());
+    std::vector<int32_t> b_of(m), off(per + 1), its(m);
+    std::vector<int64_t> bl(per);
+    if ((st = sa_lpt_schedule(mload.data(), m, per, b_of.data(), off.data(), its.data(), bl.data()))) return st;
+    for (int32_t lb = 0; lb < per; ++lb) {
+      const int32_t gb = lb * n_groups + g;  // bin gb runs on group gb % n_groups
+      for (int32_t t = off[lb]; t < off[lb + 1]; ++t) bin_items[gb].push_back(members[its[t]]);
+      load[gb] = bl[lb];
+    }
+  }
+  bin_offsets[0] = 0;
+  for (int32_t b = 0; b < n_bins; ++b) {
+    bin_offsets[b + 1] = bin_offsets[b] + int32_t(bin_items[b].size());
+    for (size_t t = 0; t < bin_items[b].size(); ++t) {
+      items_by_bin[bin_offsets[b] + t] = bin_items[b][t];
+      bin_of_item[bin_items[b][t]] = b;
+    }
+    if (bin_load) bin_load[b] = load[b];
+  }
+  return ok();
+}
+
 sa_status sa_lpt_order_bins(const int32_t* bin_offsets, int32_t n_bins, int32_t* items_by_bin) {
   if (n_bins < 1 || !bin_offsets) return fail(SA_ERR_INVALID_ARG, "bin_offsets is NULL or n_bins < 1");
   if (bin_offsets[0] != 0) return fail(SA_ERR_INVALID_ARG, "bin_offsets[0] must be 0");

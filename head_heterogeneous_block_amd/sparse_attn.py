@@ -30,7 +30,8 @@ SA_BF16, SA_F32 = 0, 1
 MAX_HEADS = 128
 
 EXPORTED = [
-    "sa_version", "sa_last_error", "sa_lpt_schedule", "sa_lpt_order_bins", "sa_prefill_block_counts", "sa_decode_block_counts",
+    "sa_version", "sa_last_error", "sa_lpt_schedule", "sa_lpt_schedule_grouped", "sa_lpt_order_bins",
+    "sa_prefill_block_counts", "sa_decode_block_counts",
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_decode_workspace_size", "sa_sparse_attn_decode",
 ]
@@ -69,6 +70,8 @@ _SIG = {
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_lpt_schedule": (ctypes.c_int32, [_i64p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
     "sa_lpt_order_bins": (ctypes.c_int32, [_i32p, ctypes.c_int32, _i32p]),
+    "sa_lpt_schedule_grouped": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                 ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
     "sa_prefill_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
     "sa_decode_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
     "sa_decode_pooled_size": (ctypes.c_size_t, [_descp, _budp]),
@@ -179,6 +182,23 @@ def sa_lpt_schedule(loads: Sequence[int], n_bins: int):
     return bin_of, off, items, bl
 
 
+def sa_lpt_schedule_grouped(loads: Sequence[int], chunk_of_item: Sequence[int], n_chunks: int, n_groups: int,
+                            n_bins: int):
+    """Two-level placement (chunks onto groups, then items onto each group's
+    bins).  Returns numpy ``(bin_of_item, bin_offsets, items_by_bin, bin_load)``."""
+    ld = np.ascontiguousarray(np.asarray(loads, dtype=np.int64))
+    ch = np.ascontiguousarray(np.asarray(chunk_of_item, dtype=np.int32))
+    n = ld.size
+    bin_of = np.empty(n, np.int32)
+    off = np.empty(n_bins + 1 if n_bins > 0 else 1, np.int32)
+    items = np.empty(n, np.int32)
+    bl = np.empty(max(n_bins, 1), np.int64)
+    _check(_lib.sa_lpt_schedule_grouped(ld.ctypes.data_as(_i64p), ch.ctypes.data_as(_i32p), n, n_chunks, n_groups,
+                                        n_bins, bin_of.ctypes.data_as(_i32p), off.ctypes.data_as(_i32p),
+                                        items.ctypes.data_as(_i32p), bl.ctypes.data_as(_i64p)))
+    return bin_of, off, items, bl
+
+
 def sa_lpt_order_bins(bin_offsets: np.ndarray, items_by_bin: np.ndarray) -> np.ndarray:
     """Copy of ``items_by_bin`` with every bin's items in ascending item order."""
     off = np.ascontiguousarray(bin_offsets, dtype=np.int32)
@@ -264,10 +284,12 @@ class PrefillPlan:
     descriptor, per-head budgets, block counts (LPT loads), kmax and the LPT
     schedule over ``n_bins`` persistent workgroups (uploaded to the device).
     ``bin_order``: "index" walks each bin in item order (sa_lpt_order_bins),
-    "lpt" in assignment order."""
+    "lpt" in assignment order.  ``xcd_groups`` > 0 uses the two-level placement
+    (sa_lpt_schedule_grouped): chunks of ``xcd_chunk`` query blocks of one
+    (sequence, KV head) onto ``xcd_groups`` cache partitions, then LPT inside."""
 
     def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
-                 kernel_variant: int = 0, bin_order: str = "index"):
+                 kernel_variant: int = 0, bin_order: str = "index", xcd_groups: int = 0, xcd_chunk: int = 64):
         self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_prefill_block_counts(self.desc, self.budgets)
@@ -280,7 +302,20 @@ class PrefillPlan:
         self.block_cnt = torch.empty((q.shape[0], q.shape[1], self.nb), dtype=torch.int32, device=dev)
         self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
         if n_bins > 0:
-            _, off, items, load = sa_lpt_schedule(self.counts.reshape(-1), n_bins)
+            loads = self.counts.reshape(-1)
+            if xcd_groups > 0:
+                # item = (b * Hq + h) * NB + m; chunk = ((b * Hkv + h / G) * n_m + m / xcd_chunk)
+                Hq, Hkv = q.shape[1], k.shape[1]
+                it = np.arange(loads.size)
+                m = it % self.nb
+                bh = it // self.nb
+                b, h = bh // Hq, bh % Hq
+                n_m = -(-self.nb // xcd_chunk)
+                chunk = ((b * Hkv + h // (Hq // Hkv)) * n_m + m // xcd_chunk).astype(np.int32)
+                _, off, items, load = sa_lpt_schedule_grouped(loads, chunk, int(chunk.max()) + 1 if chunk.size else 1,
+                                                              xcd_groups, n_bins)
+            else:
+                _, off, items, load = sa_lpt_schedule(loads, n_bins)
             if bin_order == "index":
                 items = sa_lpt_order_bins(off, items)
             elif bin_order != "lpt":

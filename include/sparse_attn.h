@@ -126,6 +126,25 @@ sa_status sa_lpt_schedule(const int64_t* loads, int32_t n_items, int32_t n_bins,
                           int32_t* bin_of_item, int32_t* bin_offsets, int32_t* items_by_bin,
                           int64_t* bin_load);
 
+/* Two-level greedy longest-load-first placement for a GPU whose compute units
+ * sit in n_groups partitions with a cache of their own (8 XCDs on MI355X;
+ * workgroup b of a persistent grid runs on partition b % n_groups).  Items are
+ * first bundled into chunks chosen by the caller (chunk_of_item[i] in
+ * [0, n_chunks)); level 1 places the chunks on the groups with
+ * sa_lpt_schedule's rule (chunk load = sum of its items' loads); level 2 places
+ * each group's items on that group's n_bins / n_groups bins, again with
+ * sa_lpt_schedule's rule, bin b of the group being b * n_groups + group.  Items
+ * of one chunk so share a partition's cache.  This adapts the S-HPLB greedy
+ * placement ("S-HPLB ...", Italian summary §2.B, Chinese summary §2.2) to a
+ * device with partitioned caches; on one partition it is sa_lpt_schedule.
+ *   loads, chunk_of_item [host][n_items]; outputs as for sa_lpt_schedule.
+ * n_bins must be a multiple of n_groups; bad sizes or indices are
+ * SA_ERR_INVALID_ARG. */
+sa_status sa_lpt_schedule_grouped(const int64_t* loads, const int32_t* chunk_of_item, int32_t n_items,
+                                  int32_t n_chunks, int32_t n_groups, int32_t n_bins,
+                                  int32_t* bin_of_item, int32_t* bin_offsets, int32_t* items_by_bin,
+                                  int64_t* bin_load);
+
 /* Reorders the items of every bin ascending by item index, in place (host,
  * synchronous).  The bins keep the same items and loads, so the makespan of
  * the placement is unchanged; only the order in which a persistent workgroup

@@ -77,6 +77,33 @@ def test_lpt_order_bins_keeps_bins_and_sorts():
         SA.sa_lpt_order_bins(np.array([0, 5, 3], np.int32), items)
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_lpt_grouped_is_two_oracle_placements(seed):
+    """Two-level placement = the oracle's LPT of chunk loads onto groups, then
+    the oracle's LPT of each group's items (in item order) onto its bins, bin
+    b of group g being b * n_groups + g."""
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 900))
+    n_chunks = int(rng.integers(1, 40))
+    n_groups = int(rng.integers(1, 9))
+    per = int(rng.integers(1, 9))
+    loads = rng.integers(0, 60, size=n)
+    chunk = rng.integers(0, n_chunks, size=n)
+    bin_of, off, items, bl = SA.sa_lpt_schedule_grouped(loads, chunk, n_chunks, n_groups, n_groups * per)
+    cl = np.bincount(chunk, weights=loads, minlength=n_chunks).astype(np.int64)
+    g_of_chunk = O.lpt_schedule(cl.tolist(), n_groups)[0]
+    for g in range(n_groups):
+        mem = np.flatnonzero(np.asarray(g_of_chunk)[chunk] == g)
+        rb, roff, ritems, rload = O.lpt_schedule(loads[mem].tolist(), per)
+        for lb in range(per):
+            gb = lb * n_groups + g
+            assert items[off[gb]:off[gb + 1]].tolist() == mem[ritems[roff[lb]:roff[lb + 1]]].tolist()
+            assert int(bl[gb]) == int(rload[lb])
+    assert np.all(bin_of[items] == np.repeat(np.arange(n_groups * per), np.diff(off)))
+    with pytest.raises(SA.SaError):
+        SA.sa_lpt_schedule_grouped(loads, chunk, n_chunks, 3, 7)
+
+
 def test_lpt_on_config_tile_loads():
     """The tile loads of the 32K Llama-shaped workload scheduled onto 512 bins:
     identical to the oracle, and the makespan within one item of the mean."""

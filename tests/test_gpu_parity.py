@@ -118,6 +118,16 @@ def test_prefill_schedules_bitwise_equal():
         _say("schedule", n_bins)
         _, _, o, lse, _ = prefill_gpu(inp, n_bins=n_bins)
         outs.append((o, lse))
+    # two-level (cache-partition) placement and assignment-order bins
+    for kw in (dict(xcd_groups=8, xcd_chunk=4), dict(bin_order="lpt")):
+        _say("schedule", kw)
+        plan = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=64, out_f32=True, **kw)
+        o = torch.empty(inp.q.shape, dtype=torch.float32, device=DEV)
+        lse = torch.empty(inp.q.shape[:3], dtype=torch.float32, device=DEV)
+        plan.select(inp.q, inp.k)
+        plan.attend(inp.q, inp.k, inp.v, o, lse)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
     for o, lse in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
 
