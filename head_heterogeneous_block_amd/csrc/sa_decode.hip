@@ -474,7 +474,7 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeCombineParams p, int dtype) {
   constexpr int kW = D / 64;  // waves
-  __shared__ float w_s[D];
+  __shared__ float w_s[D + 16];  // 16 words of slack for the 16-wide unrolled reads
   __shared__ float red[kW];
   const int h = blockIdx.x, bi = blockIdx.y;
   const int j = h / p.G, gi = h % p.G;
@@ -501,16 +501,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeCombineParams p
     __syncthreads();
     const int cn = min(D, nch - c0);
     const float* po = p.part_o + ((base + c0) * p.G + gi) * D + d;
-    int u = 0;
-    for (; u + 4 <= cn; u += 4) {
-      const float a0 = po[(int64_t)(u + 0) * p.G * D], a1 = po[(int64_t)(u + 1) * p.G * D];
-      const float a2 = po[(int64_t)(u + 2) * p.G * D], a3 = po[(int64_t)(u + 3) * p.G * D];
-      acc = fmaf(a0, w_s[u], acc);
-      acc = fmaf(a1, w_s[u + 1], acc);
-      acc = fmaf(a2, w_s[u + 2], acc);
-      acc = fmaf(a3, w_s[u + 3], acc);
+    const int64_t cs = (int64_t)p.G * D;  // chunk stride
+    // 16 independent loads per round trip; chunks past cn read chunk 0 with weight 0
+    for (int u0 = 0; u0 < cn; u0 += 16) {
+      float a[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) a[u] = po[(u0 + u < cn ? u0 + u : 0) * cs];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) acc = fmaf(a[u], u0 + u < cn ? w_s[u0 + u] : 0.f, acc);
     }
-    for (; u < cn; ++u) acc = fmaf(po[(int64_t)u * p.G * D], w_s[u], acc);
   }
   lp = wave_sum(lp);
   __syncthreads();
