@@ -37,8 +37,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--prefill-config", type=int, default=2)
-    ap.add_argument("--decode-config", type=int, default=4)
+    ap.add_argument("--prefill-workload", default="llama3.1-8b-prefill-128k")
+    ap.add_argument("--decode-workload", default="llama3.1-8b-decode-128k-b16")
     ap.add_argument("--bins-per-cu", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
@@ -137,8 +137,8 @@ def cpu_baseline_decode(inp, block_idx, block_cnt):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the block-sparse path has no "
-              "multi-GPU leg in this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the block-sparse path is a "
+              "single-GPU path with no multi-GPU leg", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -161,9 +161,9 @@ def main():
         print("[bench] calibration copy: 1 GiB read + 1 GiB written (torch.neg)", file=sys.stderr, flush=True)
 
     # ---------------------------------------------------------------- prefill
-    pspec = W.CONFIGS[args.prefill_config]
+    pspec = W.BY_NAME[args.prefill_workload]
     t0 = time.time()
-    pin = W.make_prefill(pspec, W.default_seed(args.prefill_config), device=dev)
+    pin = W.make_prefill(pspec, W.seed_of(pspec), device=dev)
     torch.cuda.synchronize()
     print(f"[bench] prefill inputs {pspec.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     n_bins = n_cu * args.bins_per_cu
@@ -175,10 +175,10 @@ def main():
     att = lambda: plan.attend(pin.q, pin.k, pin.v, o)  # noqa: E731
 
     # ---------------------------------------------------------------- decode
-    dspec = W.CONFIGS[args.decode_config]
+    dspec = W.BY_NAME[args.decode_workload]
     if args.only in ("decode", "all"):
         t0 = time.time()
-        din = W.make_decode(dspec, W.default_seed(args.decode_config), device=dev)
+        din = W.make_decode(dspec, W.seed_of(dspec), device=dev)
         dplan = SA.DecodePlan(din.q, din.k, din.v, din.budget)
         dplan.pool(din.k)
         do = torch.empty_like(din.q)

@@ -94,21 +94,26 @@ class DecodeSpec:
         return dataclasses.replace(self, **kw)
 
 
-CONFIGS = [
-    PrefillSpec("tiny-causal-prefill-f32", "f32", 1, 4, 1, 64, 1024, 64, "count",
-                counts=(2, 4, 6, 8), n_hot=3),
-    PrefillSpec("llama3.1-8b-prefill-32k", "bf16", 1, 32, 8, 128, 32768, 128, "loguniform",
-                lo=0.02, hi=0.50, mean=0.125),
-    PrefillSpec("llama3.1-8b-prefill-128k", "bf16", 1, 32, 8, 128, 131072, 128, "loguniform",
-                lo=0.01, hi=0.40, mean=0.0625),
-    PrefillSpec("qwen2.5-72b-prefill-64k", "bf16", 1, 64, 8, 128, 65536, 128, "bimodal",
-                lo=0.03, hi=0.30, mean=0.12, frac_high=0.30),
-    DecodeSpec("llama3.1-8b-decode-128k-b16", "bf16", 16, 32, 8, 128, 131072),
-]
+TINY_F32 = PrefillSpec("tiny-causal-prefill-f32", "f32", 1, 4, 1, 64, 1024, 64, "count",
+                       counts=(2, 4, 6, 8), n_hot=3)
+LLAMA_32K = PrefillSpec("llama3.1-8b-prefill-32k", "bf16", 1, 32, 8, 128, 32768, 128, "loguniform",
+                        lo=0.02, hi=0.50, mean=0.125)
+LLAMA_128K = PrefillSpec("llama3.1-8b-prefill-128k", "bf16", 1, 32, 8, 128, 131072, 128, "loguniform",
+                         lo=0.01, hi=0.40, mean=0.0625)
+QWEN_64K = PrefillSpec("qwen2.5-72b-prefill-64k", "bf16", 1, 64, 8, 128, 65536, 128, "bimodal",
+                       lo=0.03, hi=0.30, mean=0.12, frac_high=0.30)
+DECODE_128K = DecodeSpec("llama3.1-8b-decode-128k-b16", "bf16", 16, 32, 8, 128, 131072)
+
+# all named workloads; a workload's default seed is 1000 + its position here
+WORKLOADS = [TINY_F32, LLAMA_32K, LLAMA_128K, QWEN_64K, DECODE_128K]
+BY_NAME = {w.name: w for w in WORKLOADS}
 
 
-def default_seed(index: int) -> int:
-    return 1000 + index
+def seed_of(spec) -> int:
+    """Default seed of a named workload (by name, so variants made with
+    ``with_`` keep the seed of the workload they derive from only if renamed
+    back; pass an explicit seed for those)."""
+    return 1000 + [w.name for w in WORKLOADS].index(spec.name)
 
 
 def _rng(seed: int, purpose: int, *extra: int) -> np.random.Generator:

@@ -107,8 +107,8 @@ def test_lpt_grouped_is_two_oracle_placements(seed):
 def test_lpt_on_config_tile_loads():
     """The tile loads of the 32K Llama-shaped workload scheduled onto 512 bins:
     identical to the oracle, and the makespan within one item of the mean."""
-    spec = W.CONFIGS[1]
-    bud = W.prefill_budgets(spec, W.default_seed(1))
+    spec = W.LLAMA_32K
+    bud = W.prefill_budgets(spec, W.seed_of(W.LLAMA_32K))
     import torch
     q = torch.empty((1, spec.n_q_heads, spec.seq_len, spec.head_dim), dtype=torch.bfloat16, device="meta")
     k = torch.empty((1, spec.n_kv_heads, spec.seq_len, spec.head_dim), dtype=torch.bfloat16, device="meta")
@@ -124,7 +124,7 @@ def test_lpt_on_config_tile_loads():
 
 def test_block_counts_match_budget_rule():
     import torch
-    for spec, seed in ((W.CONFIGS[0], 1000), (W.CONFIGS[2].with_(seq_len=8192 + 64), 7), (W.CONFIGS[3], 1003)):
+    for spec, seed in ((W.TINY_F32, 1000), (W.LLAMA_128K.with_(seq_len=8192 + 64), 7), (W.QWEN_64K, 1003)):
         bud = W.prefill_budgets(spec, seed)
         q = torch.empty((1, spec.n_q_heads, spec.seq_len, spec.head_dim), device="meta",
                         dtype=torch.float32 if spec.dtype == "f32" else torch.bfloat16)
@@ -135,7 +135,7 @@ def test_block_counts_match_budget_rule():
             ref = [O.budget_blocks(m + 1, bud["min_blocks"][h], bud["ratio_q16"][h]) for m in range(spec.n_blocks)]
             assert counts[0, h].tolist() == ref
         assert kmax == counts.max()
-    dspec = W.CONFIGS[4]
+    dspec = W.DECODE_128K
     bud = W.decode_budgets(dspec, 1004)
     q = torch.empty((dspec.batch, dspec.n_q_heads, dspec.head_dim), dtype=torch.bfloat16, device="meta")
     k = torch.empty((dspec.batch, dspec.n_kv_heads, dspec.kv_len, dspec.head_dim), dtype=torch.bfloat16,

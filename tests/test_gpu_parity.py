@@ -40,8 +40,8 @@ def _bud_sub(budget, heads):
 
 @pytest.mark.parametrize("schedule", ["natural", "lpt"])
 def test_prefill_config0_fp32_all_rows(schedule):
-    spec = W.CONFIGS[0]
-    inp = W.make_prefill(spec, W.default_seed(0), device=DEV)
+    spec = W.TINY_F32
+    inp = W.make_prefill(spec, W.seed_of(W.TINY_F32), device=DEV)
     _say("case: config0 fp32", schedule)
     idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=8 if schedule == "lpt" else 0)
     q, k, v = to_host(inp)
@@ -79,7 +79,7 @@ PREFILL_SHAPES = [
 @pytest.mark.parametrize("name,over", PREFILL_SHAPES, ids=[s[0] for s in PREFILL_SHAPES])
 @pytest.mark.parametrize("n_bins", [0, 37])
 def test_prefill_bf16_all_rows(name, over, n_bins):
-    spec = W.CONFIGS[1].with_(**over)
+    spec = W.LLAMA_32K.with_(**over)
     inp = W.make_prefill(spec, 77, device=DEV)
     _say("case:", name, "bins", n_bins)
     idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins)
@@ -96,7 +96,7 @@ def test_prefill_bf16_all_rows(name, over, n_bins):
 
 
 def test_prefill_bf16_output_and_determinism():
-    spec = W.CONFIGS[1].with_(seq_len=2048 + 128, n_q_heads=8, n_kv_heads=2)
+    spec = W.LLAMA_32K.with_(seq_len=2048 + 128, n_q_heads=8, n_kv_heads=2)
     inp = W.make_prefill(spec, 5, device=DEV)
     idx, cnt, o16, _, plan = prefill_gpu(inp, out_f32=False, with_lse=False)
     q, k, v = to_host(inp)
@@ -111,7 +111,7 @@ def test_prefill_bf16_output_and_determinism():
 def test_prefill_schedules_bitwise_equal():
     """Every tile is computed by one workgroup with the same arithmetic whatever
     the schedule: outputs must be identical bit for bit."""
-    spec = W.CONFIGS[1].with_(seq_len=4096, n_q_heads=8, n_kv_heads=2)
+    spec = W.LLAMA_32K.with_(seq_len=4096, n_q_heads=8, n_kv_heads=2)
     inp = W.make_prefill(spec, 9, device=DEV)
     outs = []
     for n_bins in (0, 1, 64, 512, 97):
@@ -135,11 +135,10 @@ def test_prefill_schedules_bitwise_equal():
 # ---------------------------------------------------------------- prefill, full sizes
 
 
-@pytest.mark.parametrize("which", [1, 2, 3])
-def test_prefill_full_size_sampled(which):
-    spec = W.CONFIGS[which]
-    _say("case: full config", which, spec.name)
-    inp = W.make_prefill(spec, W.default_seed(which), device=DEV)
+@pytest.mark.parametrize("spec", [W.LLAMA_32K, W.LLAMA_128K, W.QWEN_64K], ids=lambda s: s.name)
+def test_prefill_full_size_sampled(spec):
+    _say("case: full-size workload", spec.name)
+    inp = W.make_prefill(spec, W.seed_of(spec), device=DEV)
     n_bins = 512
     idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins)
     gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
@@ -160,7 +159,7 @@ def test_prefill_full_size_sampled(which):
         _say("head", h, "pinned", pinned, "exempt", exempt)
         assert pinned >= 0.9 * (pinned + exempt)
     # attention on sampled tiles, oracle over the GPU's block lists
-    rng = np.random.default_rng(which)
+    rng = np.random.default_rng(W.seed_of(spec))
     ms = sorted(set([0, 1, nb - 1] + rng.integers(0, nb, 5).tolist()))
     tiles = [(0, i, m) for i in range(len(heads)) for m in ms]
     sub_idx = gidx[:, heads]
@@ -222,7 +221,7 @@ def _check_decode(inp, plan, o, lse, seqs):
 
 @pytest.mark.parametrize("L", [8192, 8192 + 40, 1000])
 def test_decode_reduced_all(L):
-    spec = W.CONFIGS[4].with_(batch=3, kv_len=L, tok_lo=256, tok_hi=2048, stream_local=16)
+    spec = W.DECODE_128K.with_(batch=3, kv_len=L, tok_lo=256, tok_hi=2048, stream_local=16)
     _say("case: decode L", L)
     inp = W.make_decode(spec, 31, device=DEV)
     plan, o, lse = _decode_gpu(inp)
@@ -239,7 +238,7 @@ def test_decode_bf16_shapes(name, over):
     cache shorter than one 64-token block (every head keeps all its blocks)."""
     base = dict(batch=2, kv_len=4096 + 24, tok_lo=256, tok_hi=1024, stream_local=8)
     base.update(over)
-    spec = W.CONFIGS[4].with_(**base)
+    spec = W.DECODE_128K.with_(**base)
     _say("case: decode bf16", name)
     inp = W.make_decode(spec, 33, device=DEV)
     plan, o, lse = _decode_gpu(inp)
@@ -248,7 +247,7 @@ def test_decode_bf16_shapes(name, over):
 
 def test_decode_bf16_output():
     """bf16 output: within the fp32 tolerance plus half a bf16 ulp of the value."""
-    spec = W.CONFIGS[4].with_(batch=2, kv_len=8192, tok_lo=256, tok_hi=2048, stream_local=16)
+    spec = W.DECODE_128K.with_(batch=2, kv_len=8192, tok_lo=256, tok_hi=2048, stream_local=16)
     inp = W.make_decode(spec, 34, device=DEV)
     plan, o, lse = _decode_gpu(inp, out_f32=False)
     assert o.dtype == torch.bfloat16
@@ -260,7 +259,7 @@ def test_decode_bf16_output():
 
 
 def test_decode_gqa8_fp32():
-    spec = W.CONFIGS[4].with_(dtype="f32", batch=2, n_q_heads=16, n_kv_heads=2, kv_len=4096, tok_lo=256,
+    spec = W.DECODE_128K.with_(dtype="f32", batch=2, n_q_heads=16, n_kv_heads=2, kv_len=4096, tok_lo=256,
                               tok_hi=1024, stream_local=8, n_streaming=4)
     inp = W.make_decode(spec, 32, device=DEV)
     plan, o, lse = _decode_gpu(inp)
@@ -268,9 +267,9 @@ def test_decode_gqa8_fp32():
 
 
 def test_decode_full_size_sampled():
-    spec = W.CONFIGS[4]
+    spec = W.DECODE_128K
     _say("case: full decode config")
-    inp = W.make_decode(spec, W.default_seed(4), device=DEV)
+    inp = W.make_decode(spec, W.seed_of(W.DECODE_128K), device=DEV)
     plan, o, lse = _decode_gpu(inp)
     _check_decode(inp, plan, o, lse, [0, 9])
     assert torch.isfinite(o).all()

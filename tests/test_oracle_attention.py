@@ -55,7 +55,7 @@ def test_full_budget_is_textbook_causal_attention(S, B):
 def test_full_budget_bf16_inputs_through_selection():
     """Selection with a budget covering every causal block, then attention:
     identical to textbook causal attention on the widened bf16 values."""
-    spec = W.CONFIGS[1].with_(seq_len=1024, n_q_heads=8, n_kv_heads=2, head_dim=64, budget_kind="count",
+    spec = W.LLAMA_32K.with_(seq_len=1024, n_q_heads=8, n_kv_heads=2, head_dim=64, budget_kind="count",
                               counts=(10**6,))
     inp = W.make_prefill(spec, 3)
     q, k, v = (W.to_numpy(t) for t in (inp.q, inp.k, inp.v))
@@ -100,7 +100,7 @@ def test_one_block_known_logits():
 
 def test_invariances_constant_v_shift_permutation_gqa():
     rng = np.random.default_rng(12)
-    spec = W.CONFIGS[0].with_(seq_len=512, n_q_heads=4, n_kv_heads=2, counts=(3, 5))
+    spec = W.TINY_F32.with_(seq_len=512, n_q_heads=4, n_kv_heads=2, counts=(3, 5))
     inp = W.make_prefill(spec, 12)
     q, k, v = (W.to_numpy(t).astype(np.float64) for t in (inp.q, inp.k, inp.v))
     idx, cnt = O.select_blocks_prefill(q, k, inp.budget, spec.block)
@@ -131,12 +131,12 @@ def test_invariances_constant_v_shift_permutation_gqa():
     np.testing.assert_allclose(om, o, atol=1e-15)
 
 
-@pytest.mark.parametrize("which,S", [(0, None), (1, 2048)])
-def test_gather_form_equals_dense_masked_form(which, S):
-    spec = W.CONFIGS[which]
+@pytest.mark.parametrize("base,S", [(W.TINY_F32, None), (W.LLAMA_32K, 2048)], ids=["tiny-f32", "llama-2k"])
+def test_gather_form_equals_dense_masked_form(base, S):
+    spec = base
     if S:
         spec = spec.with_(seq_len=S, n_q_heads=8, n_kv_heads=2)
-    inp = W.make_prefill(spec, 20 + which)
+    inp = W.make_prefill(spec, 20 + W.seed_of(base) - 1000)
     q, k, v = (W.to_numpy(t) for t in (inp.q, inp.k, inp.v))
     idx, cnt = O.select_blocks_prefill(q, k, inp.budget, spec.block)
     o1, l1 = O.attention_prefill_gather(q, k, v, idx, cnt, spec.block)
@@ -146,7 +146,7 @@ def test_gather_form_equals_dense_masked_form(which, S):
 
 
 def test_decode_full_budget_is_library_attention():
-    spec = W.CONFIGS[4].with_(batch=2, kv_len=1024, n_streaming=0, tok_lo=1024, tok_hi=1025, n_hot=2)
+    spec = W.DECODE_128K.with_(batch=2, kv_len=1024, n_streaming=0, tok_lo=1024, tok_hi=1025, n_hot=2)
     inp = W.make_decode(spec, 9)
     q, k, v = (W.to_numpy(t) for t in (inp.q, inp.k, inp.v))
     idx, cnt = O.decode_select(q, k, inp.budget)
@@ -164,7 +164,7 @@ def test_decode_full_budget_is_library_attention():
 
 
 def test_decode_gather_equals_dense_mask():
-    spec = W.CONFIGS[4].with_(batch=2, kv_len=4096, n_streaming=3, tok_lo=256, tok_hi=1024, stream_local=8)
+    spec = W.DECODE_128K.with_(batch=2, kv_len=4096, n_streaming=3, tok_lo=256, tok_hi=1024, stream_local=8)
     inp = W.make_decode(spec, 13)
     q, k, v = (W.to_numpy(t) for t in (inp.q, inp.k, inp.v))
     idx, cnt = O.decode_select(q, k, inp.budget)

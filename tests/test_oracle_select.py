@@ -144,7 +144,7 @@ def test_select_row_edge_budgets():
 def test_amplified_plants_are_selected():
     """With a strong planted direction every causal hot block outranks the noise,
     so a budget that has room for them must keep all of them."""
-    spec = W.CONFIGS[0].with_(hot_k=8.0, hot_q=1.0, counts=(6, 6, 6, 6))
+    spec = W.TINY_F32.with_(hot_k=8.0, hot_q=1.0, counts=(6, 6, 6, 6))
     inp = W.make_prefill(spec, 7)
     q, k = W.to_numpy(inp.q), W.to_numpy(inp.k)
     idx, cnt = O.select_blocks_prefill(q, k, inp.budget, spec.block)
@@ -159,7 +159,7 @@ def test_amplified_plants_are_selected():
 
 
 def test_select_prefill_invariants_and_counts():
-    spec = W.CONFIGS[1].with_(seq_len=4096)
+    spec = W.LLAMA_32K.with_(seq_len=4096)
     inp = W.make_prefill(spec, 11)
     q, k = W.to_numpy(inp.q), W.to_numpy(inp.k)
     idx, cnt = O.select_blocks_prefill(q, k, inp.budget, spec.block)
@@ -175,8 +175,8 @@ def test_select_prefill_invariants_and_counts():
 
 
 def test_config0_loads_from_selection():
-    spec = W.CONFIGS[0]
-    inp = W.make_prefill(spec, W.default_seed(0))
+    spec = W.TINY_F32
+    inp = W.make_prefill(spec, W.seed_of(W.TINY_F32))
     idx, cnt = O.select_blocks_prefill(W.to_numpy(inp.q), W.to_numpy(inp.k), inp.budget, spec.block)
     assert cnt.reshape(4, -1).sum(1).tolist() == [31, 58, 81, 100]
     # algorithmic flops: 4*D per visible pair, diagonal blocks half (+B/2)
@@ -187,7 +187,7 @@ def test_config0_loads_from_selection():
 
 
 def test_decode_streaming_heads_fixed_and_retrieval_plants():
-    spec = W.CONFIGS[4].with_(batch=2, kv_len=8192, n_streaming=3, tok_lo=256, tok_hi=1024,
+    spec = W.DECODE_128K.with_(batch=2, kv_len=8192, n_streaming=3, tok_lo=256, tok_hi=1024,
                               stream_local=16, hot_k=6.0, hot_q=8.0)
     inp = W.make_decode(spec, 5)
     q, k = W.to_numpy(inp.q), W.to_numpy(inp.k)
