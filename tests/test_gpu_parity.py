@@ -258,6 +258,30 @@ def test_decode_bf16_output():
     assert np.all(np.abs(og - ro) <= TOL_BF16 + bf16_half_ulp(ro))
 
 
+def test_decode_pooled_key_cache():
+    """The pooled-key cache (the Index step) against the oracle's block means:
+    one fp32 array [b][Hkv][ceil(L/g)][D] per granularity the scoring heads use,
+    ascending, packed back to back."""
+    spec = W.DECODE_128K.with_(batch=2, kv_len=4096 + 24, tok_lo=256, tok_hi=1024, stream_local=8)
+    inp = W.make_decode(spec, 35, device=DEV)
+    plan = SA.DecodePlan(inp.q, inp.k, inp.v, inp.budget)
+    plan.pool(inp.k)
+    torch.cuda.synchronize()
+    got_all = plan.k_pooled.cpu().numpy()
+    k = W.to_numpy(inp.k)
+    grans = sorted({int(inp.budget["granularity"][h]) for h in range(spec.n_q_heads) if not inp.budget["streaming"][h]})
+    off = 0
+    for g in grans:
+        nc = -(-spec.kv_len // g)
+        n = spec.batch * spec.n_kv_heads * nc * spec.head_dim
+        got = got_all[off:off + n].reshape(spec.batch, spec.n_kv_heads, nc, spec.head_dim)
+        ref = O.pool_blocks(k, g)
+        err = float(np.max(np.abs(got - ref)))
+        _say("pooled g", g, "max abs err", err)
+        assert err <= 1e-5  # fp32 sums of <= 64 bf16 values
+        off += n
+
+
 def test_decode_gqa8_fp32():
     spec = W.DECODE_128K.with_(dtype="f32", batch=2, n_q_heads=16, n_kv_heads=2, kv_len=4096, tok_lo=256,
                               tok_hi=1024, stream_local=8, n_streaming=4)
