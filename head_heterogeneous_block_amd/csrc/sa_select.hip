@@ -74,10 +74,16 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 }
 
 // ---------------------------------------------------------------- prefill block scores
-// s[bh][m][n] = scale * <Qbar[bh][m], Kbar[bkv][n]> for the causal 64x64 tiles.
+// s[bh][m][n] = scale * <Qbar[bh][m], Kbar[bkv][n]> for the causal 128x128
+// tiles, in fp32 on the MFMA pipe (v_mfma_f32_32x32x2f32; each wave one 64x64
+// quadrant as 2x2 MFMA tiles).  fp32 keeps the scores exact enough for the
+// 1e-4 relative gaps the selection is checked against.  Qbar and Kbar rows are
+// staged through LDS in 32-wide d chunks, shared by the four waves.
+constexpr int kScoreTile = 128;
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_scores_kernel(PrefillScoreParams p) {
-  constexpr int kT = 64;
+  constexpr int kT = kScoreTile;
   constexpr int kDC = 32;  // d columns staged per pass
   __shared__ float qs[kT][kDC + 1];
   __shared__ float ks[kT][kDC + 1];
@@ -89,45 +95,61 @@ __global__ __launch_bounds__(256) void prefill_scores_kernel(PrefillScoreParams 
   const float* qp = p.qp + (int64_t)bh * p.NB * D;
   const float* kp = p.kp + (int64_t)bkv * p.NB * D;
   const int tid = threadIdx.x;
-  const int tm = tid / 16, tn = tid % 16;
-  float acc[4][4] = {};
+  const int lane = tid & 63, wave = tid >> 6;
+  const int mi = wave >> 1, ni = wave & 1;  // this wave's 64 x 64 quadrant
+  const int col = lane & 31, kh = lane >> 5;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
   for (int d0 = 0; d0 < D; d0 += kDC) {
-    for (int i = tid; i < kT * kDC / 4; i += 256) {
+    f32x4 va[kT * kDC / 4 / 256], vb[kT * kDC / 4 / 256];
+#pragma unroll
+    for (int u = 0; u < kT * kDC / 4 / 256; ++u) {
+      const int i = u * 256 + tid;
       const int r = i / (kDC / 4), c = (i % (kDC / 4)) * 4;
-      f32x4 a = (m0 + r < p.NB) ? *reinterpret_cast<const f32x4*>(qp + (int64_t)(m0 + r) * D + d0 + c) : f32x4{};
-      f32x4 b = (n0 + r < p.NB) ? *reinterpret_cast<const f32x4*>(kp + (int64_t)(n0 + r) * D + d0 + c) : f32x4{};
+      va[u] = (m0 + r < p.NB) ? *reinterpret_cast<const f32x4*>(qp + (int64_t)(m0 + r) * D + d0 + c) : f32x4{};
+      vb[u] = (n0 + r < p.NB) ? *reinterpret_cast<const f32x4*>(kp + (int64_t)(n0 + r) * D + d0 + c) : f32x4{};
+    }
+#pragma unroll
+    for (int u = 0; u < kT * kDC / 4 / 256; ++u) {
+      const int i = u * 256 + tid;
+      const int r = i / (kDC / 4), c = (i % (kDC / 4)) * 4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qs[r][c + e] = a[e];
-        ks[r][c + e] = b[e];
+        qs[r][c + e] = va[u][e];
+        ks[r][c + e] = vb[u][e];
       }
     }
     __syncthreads();
-#pragma unroll 4
-    for (int d = 0; d < kDC; ++d) {
-      float a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = qs[tm + 16 * i][d];
-        b[i] = ks[tn + 16 * i][d];
+    for (int kk = 0; kk < kDC; kk += 2) {
+      float av[2], bv[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        av[t] = qs[mi * 64 + t * 32 + col][kk + kh];
+        bv[t] = ks[ni * 64 + t * 32 + col][kk + kh];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
     __syncthreads();
   }
-  float* srow = p.s + (int64_t)bh * p.NB * p.NB;
+  // acc[a][b][i] holds row 8 (i / 4) + 4 kh + i % 4 of row tile a, column col of column tile b
+  float* sbase = p.s + (int64_t)bh * p.NB * p.NB;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + tm + 16 * i;
-    if (m >= p.NB) continue;
+  for (int b = 0; b < 2; ++b) {
+    const int n = n0 + ni * 64 + b * 32 + col;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tn + 16 * j;
-      if (n <= m) srow[(int64_t)m * p.NB + n] = acc[i][j] * p.scale;
-    }
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + mi * 64 + a * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
+        if (m < p.NB && n <= m) sbase[(int64_t)m * p.NB + n] = acc[a][b][i] * p.scale;
+      }
   }
 }
 
@@ -462,7 +484,7 @@ hipError_t launch_pool(const PoolParams& p, int dtype, int D, int batch, hipStre
 }
 
 hipError_t launch_prefill_scores(const PrefillScoreParams& p, int D, int batch, hipStream_t stream) {
-  const int t = (p.NB + 63) / 64;
+  const int t = (p.NB + kScoreTile - 1) / kScoreTile;
   dim3 grid(t, t, batch * p.Hq);
   if (D == 128) hipLaunchKernelGGL((prefill_scores_kernel<128>), grid, dim3(256), 0, stream, p);
   else if (D == 64) hipLaunchKernelGGL((prefill_scores_kernel<64>), grid, dim3(256), 0, stream, p);
