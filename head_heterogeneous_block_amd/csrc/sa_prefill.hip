@@ -327,12 +327,15 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int key0 = s.hs * kKS;
     const bool diag = s.n == s.m;
     const int q_in_blk = wave * 32 + col;
+    // straight-line selects (no per-element branches): the first masked key of
+    // this lane's query row, then one compare per score
+    const int lim = min(diag ? q_in_blk : B, S - s.n * B - 1);  // largest visible key of the block
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kl = key0 + kt * 32 + (i >> 3) * 16 + half * 8 + (i & 7);
-        if ((diag && kl > q_in_blk) || s.n * B + kl >= S) sacc[kt][i] = kNegInf;
+        sacc[kt][i] = kl > lim ? kNegInf : sacc[kt][i];
       }
   };
 
