@@ -211,6 +211,7 @@ DecodeSelectWs decode_select_ws(const sa_attn_desc* d, const sa_head_budget* b, 
 }
 
 constexpr int kChunkAtoms = 32;
+constexpr int kAtomPad = 16;  // tokens an atom may reach past the cache end
 
 struct DecodeAttnWs {
   size_t atoms, n_union, part_o, part_ml, total;
@@ -676,6 +677,13 @@ sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* 
   if (!aligned16(workspace)) return fail(SA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const int64_t n_atoms = cdiv(desc->kv_len, sa::kAtom);
   if (int64_t(G) * cdiv(n_atoms, 32) * 4 > 64 * 1024) return fail(SA_ERR_UNSUPPORTED, "kv_len too long for the plan");
+  {
+    // the attention kernels address a (sequence, KV head) slice with 32-bit offsets
+    const int64_t es = elem_size(desc->dtype);
+    if (int64_t(desc->kv_len + kAtomPad) * desc->k_stride[2] * es >= (1ll << 31) ||
+        int64_t(desc->kv_len + kAtomPad) * desc->v_stride[2] * es >= (1ll << 31))
+      return fail(SA_ERR_UNSUPPORTED, "one (sequence, KV head) slice of K or V must span < 2 GiB");
+  }
   if ((s = check_device())) return s;
   hipStream_t st = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);

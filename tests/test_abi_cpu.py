@@ -187,6 +187,33 @@ def test_invalid_budgets_rejected(kw):
     assert e.value.status == SA.SA_ERR_INVALID_ARG
 
 
+def test_slices_beyond_32_bit_offsets_rejected():
+    """A (sequence, KV head) slice of K or V at or beyond 2 GiB would overflow the
+    kernels' 32-bit buffer offsets: rejected before any launch."""
+    import torch
+    L = 1 << 16
+    q = torch.empty((1, 4, L, 128), dtype=torch.bfloat16, device="meta")
+    # rows 64 KiB apart (a wide packed-projection buffer): 2^16 rows span 4 GiB
+    k = torch.empty_strided((1, 2, L, 128), (2 * L * 32768, 32768, 32768, 1), dtype=torch.bfloat16,
+                            device="meta")
+    d = SA.make_prefill_desc(q, k, k, q, 128)
+    b = SA.make_budgets({"min_blocks": [2] * 4, "ratio_q16": [0] * 4, "n_sink": [1] * 4, "n_local": [1] * 4,
+                         "granularity": [128] * 4})
+    fake = ctypes.c_void_p(1 << 20)
+    st = SA._lib.sa_sparse_attn_prefill(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 2, None, None, 0,
+                                        0, None, 0, None)
+    assert st == SA.SA_ERR_UNSUPPORTED and "2 GiB" in SA._lib.sa_last_error().decode()
+    qd = torch.empty((1, 4, 128), dtype=torch.bfloat16, device="meta")
+    kd = torch.empty_strided((1, 1, L, 128), (L * 32768, L * 32768, 32768, 1), dtype=torch.bfloat16,
+                             device="meta")
+    dd = SA.make_decode_desc(qd, kd, kd, qd)
+    bd = SA.make_budgets({"min_blocks": [2] * 4, "ratio_q16": [0] * 4, "n_sink": [1] * 4, "n_local": [1] * 4,
+                          "granularity": [64] * 4})
+    st = SA._lib.sa_sparse_attn_decode(ctypes.byref(dd), bd, fake, fake, fake, fake, None, fake, fake, 2, 0, fake,
+                                       1 << 40, None)
+    assert st == SA.SA_ERR_UNSUPPORTED and "2 GiB" in SA._lib.sa_last_error().decode()
+
+
 def test_device_calls_fail_cleanly_without_gpu():
     import torch
     if torch.cuda.is_available():
