@@ -168,7 +168,9 @@ def main():
     print(f"[bench] prefill inputs {pspec.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     n_bins = n_cu * args.bins_per_cu
     t0 = time.perf_counter()
-    plan = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins)
+    # work queue: n_bins persistent workgroups take the tiles longest first
+    # inside each (sequence, KV head) group
+    plan = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True)
     lpt_ms = (time.perf_counter() - t0) * 1e3
     o = torch.empty_like(pin.q)
     sel = lambda: plan.select(pin.q, pin.k)  # noqa: E731
@@ -267,7 +269,18 @@ def main():
         cont.items_by_bin = torch.arange(n_t, dtype=torch.int32, device=dev)
         cont.n_bins = n_bins
         ablation["contiguous_bins_ms"] = timed(lambda: cont.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
-        ablation["lpt_bins_ms"] = res["att_ms"]
+        ablation["queue_lpt_grouped_ms"] = res["att_ms"]
+        # the same queue in plain longest-first order (no grouping by KV head)
+        flat = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True)
+        flat.block_idx = plan.block_idx
+        flat.block_cnt = plan.block_cnt
+        flat.items_by_bin = torch.from_numpy(SA.sa_lpt_queue_order(plan.counts.reshape(-1))).to(dev)
+        ablation["queue_lpt_flat_ms"] = timed(lambda: flat.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+        # static LPT bins, each walked in item order
+        lpt = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins)
+        lpt.block_idx = plan.block_idx
+        lpt.block_cnt = plan.block_cnt
+        ablation["lpt_bins_ms"] = timed(lambda: lpt.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
         asg = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, bin_order="lpt")
         asg.block_idx = plan.block_idx
         asg.block_cnt = plan.block_cnt
@@ -280,7 +293,7 @@ def main():
         ablation["lpt_xcd_two_level_makespan_over_mean"] = float(xcd.bin_load.max() / xcd.bin_load.mean())
         loads = plan.counts.reshape(-1).astype(np.int64)
         cont_load = np.add.reduceat(loads, offs[:-1]) if n_t else loads
-        ablation["lpt_makespan_over_mean"] = float(plan.bin_load.max() / plan.bin_load.mean())
+        ablation["lpt_makespan_over_mean"] = float(lpt.bin_load.max() / lpt.bin_load.mean())
         ablation["contiguous_makespan_over_mean"] = float(cont_load.max() / cont_load.mean())
 
     cpu = None
@@ -317,10 +330,10 @@ def main():
                                f"Hkv={pspec.n_kv_heads}, D={pspec.head_dim}, block={pspec.block}) + decode "
                                f"{dspec.name} (batch={dspec.batch}, L={dspec.kv_len})",
                    "global_batch": 1, "seq_len": pspec.seq_len, "parallelism": "single GPU",
-                   "lpt_bins": n_bins},
+                   "schedule": f"work queue: {n_bins} workgroups, tiles longest first per (sequence, KV head)"},
         "prefill": {"select_ms": res.get("sel_ms"), "attention_ms": res.get("att_ms"),
                     "attended_tflops": tflops, "attended_flops": flops,
-                    "mfma_frac": roofline["frac"], "lpt_host_ms": lpt_ms},
+                    "mfma_frac": roofline["frac"], "schedule_host_ms": lpt_ms},
         "decode": {"select_ms": res.get("dsel_ms"), "attention_ms": res.get("datt_ms"),
                    "step_ms": res.get("dstep_ms"), "bytes": dbytes, "step_gbps": dgbps,
                    "hbm_frac": dgbps / (M.PEAK_HBM_BYTES / 1e9) if dgbps else None,

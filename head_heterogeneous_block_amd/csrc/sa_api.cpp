@@ -353,6 +353,21 @@ sa_status sa_lpt_order_bins(const int32_t* bin_offsets, int32_t n_bins, int32_t*
   return ok();
 }
 
+sa_status sa_lpt_queue_order(const int64_t* loads, const int32_t* group_of_item, int32_t n_items, int32_t* order) {
+  if (n_items < 0) return fail(SA_ERR_INVALID_ARG, "n_items < 0");
+  if (n_items > 0 && (!loads || !order)) return fail(SA_ERR_INVALID_ARG, "loads or order is NULL");
+  for (int32_t i = 0; i < n_items; ++i) {
+    if (loads[i] < 0) return fail(SA_ERR_INVALID_ARG, "negative load at item %d", i);
+    order[i] = i;
+  }
+  const auto group = [&](int32_t i) { return group_of_item ? group_of_item[i] : 0; };
+  std::stable_sort(order, order + n_items, [&](int32_t a, int32_t b) {
+    if (group(a) != group(b)) return group(a) < group(b);
+    return loads[a] > loads[b];
+  });
+  return ok();
+}
+
 sa_status sa_prefill_block_counts(const sa_attn_desc* desc, const sa_head_budget* budgets, int32_t* counts,
                                   int32_t* kmax) {
   sa_status s = check_desc(desc, true);
@@ -587,24 +602,26 @@ size_t sa_prefill_workspace_size(const sa_attn_desc* desc, int32_t kmax, int32_t
   (void)desc;
   (void)kmax;
   (void)n_bins;
-  return 0;
+  return 256;  // the work-queue counter
 }
 
 sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
                                  float* lse, const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
                                  const int32_t* bin_offsets, const int32_t* items_by_bin, int32_t n_bins,
                                  int32_t out_f32, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   sa_status s = check_desc(desc, true);
   if (s) return s;
   if (!q || !k || !v || !o || !block_idx || !block_cnt) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(SA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
   if (kmax < 1) return fail(SA_ERR_INVALID_ARG, "kmax must be >= 1");
-  if ((bin_offsets == nullptr) != (items_by_bin == nullptr))
-    return fail(SA_ERR_INVALID_ARG, "bin_offsets and items_by_bin must both be given or both NULL");
-  if (bin_offsets && n_bins < 1) return fail(SA_ERR_INVALID_ARG, "n_bins must be >= 1");
+  if (bin_offsets && !items_by_bin) return fail(SA_ERR_INVALID_ARG, "bin_offsets without items_by_bin");
+  if (items_by_bin && n_bins < 1) return fail(SA_ERR_INVALID_ARG, "n_bins must be >= 1");
+  const bool queue = items_by_bin && !bin_offsets;
+  if (queue && (!workspace || workspace_bytes < 4 || (reinterpret_cast<uintptr_t>(workspace) & 3)))
+    return fail(SA_ERR_INVALID_ARG, "the work queue needs a 4-byte aligned workspace of >= 4 bytes");
+  if (desc->batch >= 32768 || desc->n_kv_heads >= 65536)
+    return fail(SA_ERR_UNSUPPORTED, "batch must be < 32768 and n_kv_heads < 65536");
   const int64_t nb = cdiv(desc->q_len, desc->block_size);
   const int64_t n_tiles = int64_t(desc->batch) * desc->n_q_heads * nb;
   if (n_tiles > (1ll << 30)) return fail(SA_ERR_UNSUPPORTED, "too many tiles");
@@ -645,7 +662,8 @@ sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const 
   p.n_tiles = int(n_tiles);
   p.scale_log2 = scale_of(desc) * 1.4426950408889634f;
   p.out_f32 = out_f32 ? 1 : 0;
-  const int grid = bin_offsets ? n_bins : int(n_tiles);
+  p.queue = queue ? static_cast<int*>(workspace) : nullptr;
+  const int grid = items_by_bin ? n_bins : int(n_tiles);
   hipError_t e = sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, grid, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
   return ok();

@@ -103,6 +103,32 @@ __device__ __forceinline__ uint32_t wave_scan_incl(uint32_t x) {
   return x;
 }
 
+// Unsigned min / max over the 64 lanes (every lane active), result in every lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
+  x = min(x, dpp_u32<0xB1>(x));
+  x = min(x, dpp_u32<0x4E>(x));
+  x = min(x, dpp_u32<0x141>(x));
+  x = min(x, dpp_u32<0x140>(x));
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = min(uint32_t(r[0]), uint32_t(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return min(uint32_t(r[0]), uint32_t(r[1]));
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  x = max(x, dpp_u32<0xB1>(x));
+  x = max(x, dpp_u32<0x4E>(x));
+  x = max(x, dpp_u32<0x141>(x));
+  x = max(x, dpp_u32<0x140>(x));
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(uint32_t(r[0]), uint32_t(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(uint32_t(r[0]), uint32_t(r[1]));
+}
+
 // Wave64 reductions, result valid in every lane.
 __device__ __forceinline__ float wave_max(float x) { return max_xor32(max_xor16(row_max16(x))); }
 __device__ __forceinline__ float wave_sum(float x) { return sum_xor32(sum_xor16(row_sum16(x))); }

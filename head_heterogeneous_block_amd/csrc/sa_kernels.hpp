@@ -88,8 +88,10 @@ struct PrefillParams {
   int Hq, G, S, NB, n_tiles;
   float scale_log2;
   int out_f32;
+  int* queue;  // work-queue counter (nullable): items_by_bin is then one global order
 };
-// workgroup of B/32 waves, 32 queries each; grid = persistent bins or tiles
+// workgroup of B/32 waves, 32 queries each; grid = persistent bins, queue
+// workers or tiles
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int grid, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode attention

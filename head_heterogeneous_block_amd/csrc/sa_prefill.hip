@@ -94,9 +94,16 @@ struct Step {
   int tile;  // (b * Hq + h) * NB + m
   int m;     // query block of the tile
   int bh;    // b * Hq + h
-  int kb;    // batch of the tile
-  int kh;    // KV head h / G
+  int kvs;
 };
+
+template <typename F>
+__device__ __forceinline__ F kernel_arg(int offset) {
+  auto kp = (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return *(const __attribute__((address_space(4))) F*)(kp + offset);
+}
+#define COLD(field) kernel_arg<decltype(PrefillParams::field)>(offsetof(PrefillParams, field))
 
 template <typename T, int D, int B>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
@@ -107,19 +114,43 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;   // MFMA column (query) / A-row (key, d) index
   const int half = lane >> 5;  // MFMA k-half
 
+  // Work queue (p.queue set): the workgroups take the items of one global
+  // list in order, each claiming its next item from the counter when it starts
+  // the current one, so faster compute units simply take more items.  Wave 0
+  // makes the claims and hands each to the other waves through LDS.
+  __shared__ int q_slot;
+  int q_pend = 0;  // wave 0, lane 0: the claim in flight
+  auto claim = [&]() {
+    if (wave == 0 && lane == 0) q_pend = atomicAdd(COLD(queue), 1);
+  };
+  auto take_claim = [&]() -> int {
+    __syncthreads();  // every wave has read the previous claim
+    if (wave == 0) {
+      const int v = __builtin_amdgcn_readfirstlane(q_pend);
+      if (lane == 0) q_slot = v;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(q_slot);
+  };
+  const bool qmode = p.queue != nullptr;
+
   int it_beg, it_end;
-  if (p.bin_offsets) {
+  if (qmode) {
+    claim();
+    it_beg = take_claim();
+    claim();
+    it_end = p.n_tiles;  // positions in the global list
+  } else if (p.bin_offsets) {
     it_beg = p.bin_offsets[blockIdx.x];
     it_end = p.bin_offsets[blockIdx.x + 1];
   } else {
     it_beg = blockIdx.x;
     it_end = (int)blockIdx.x < p.n_tiles ? (int)blockIdx.x + 1 : (int)blockIdx.x;
   }
-  const int NB = p.NB;
   const int S = p.S;
   const float c2 = p.scale_log2;
   const int krs = int(p.ks2 * (int64_t)sizeof(T));
@@ -137,8 +168,9 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int it = base + lane;
     int t = -1, c = 0;
     if (it < it_end) {
-      t = p.items_by_bin ? p.items_by_bin[it] : it;
-      if (t >= 0 && t < p.n_tiles) c = min(p.block_cnt[t], p.kmax);
+      const int32_t* items = COLD(items_by_bin);
+      t = items ? items[it] : it;
+      if (t >= 0 && t < COLD(n_tiles)) c = min(COLD(block_cnt)[t], COLD(kmax));
       else t = -1;
     }
     iw_tile = t;
@@ -146,27 +178,56 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   };
   auto load_blocks = [&](int tile, int cnt, int base) {
     const int jj = base + lane;
-    return jj < cnt ? p.block_idx[(int64_t)tile * p.kmax + jj] : -1;
+    return jj < cnt ? COLD(block_idx)[(int64_t)tile * COLD(kmax) + jj] : -1;
+  };
+  // queue mode: tile and block count of the item at position it
+  auto queue_item = [&](int it, int& tile, int& cnt) {
+    tile = COLD(items_by_bin)[it];
+    if (tile >= 0 && tile < COLD(n_tiles)) {
+      cnt = min(COLD(block_cnt)[tile], COLD(kmax));
+    } else {
+      tile = -1;
+      cnt = 0;
+    }
   };
   // cursor over the lookahead step (the others are copies of it)
   int c_cnt = 0, c_wbase = 0, c_win = -1;  // blocks of the cursor's tile: window at c_wbase
   int nx_item = -1, nx_win = -1;            // prefetched first window of item nx_item
+  int nx_tile = -1, nx_cnt = 0;             // queue mode: its tile and block count
+  int q_next = 0;                           // queue mode: the item after the cursor's
   Step cur;
   cur.valid = 0;
 
   auto item_tile = [&](int it, int& tile, int& cnt) {
+    if (qmode) {
+      if (it == nx_item) {
+        tile = nx_tile;
+        cnt = nx_cnt;
+      } else {
+        queue_item(it, tile, cnt);
+      }
+      return;
+    }
     if (it - ibase >= 64) load_items(it);
     tile = __builtin_amdgcn_readlane(iw_tile, it - ibase);
     cnt = __builtin_amdgcn_readlane(iw_cnt, it - ibase);
   };
   auto prefetch_next = [&](int it) {
     nx_item = -1;
-    if (it >= it_end || it - ibase >= 64) return;
-    const int tile = __builtin_amdgcn_readlane(iw_tile, it - ibase);
-    const int cnt = __builtin_amdgcn_readlane(iw_cnt, it - ibase);
+    if (it >= it_end) return;
+    int tile, cnt;
+    if (qmode) {
+      queue_item(it, tile, cnt);
+    } else {
+      if (it - ibase >= 64) return;
+      tile = __builtin_amdgcn_readlane(iw_tile, it - ibase);
+      cnt = __builtin_amdgcn_readlane(iw_cnt, it - ibase);
+    }
     if (tile < 0) return;
     nx_win = load_blocks(tile, cnt, 0);
     nx_item = it;
+    nx_tile = tile;
+    nx_cnt = cnt;
   };
   // first valid block at or after position j of item `it` (moving to later items)
   auto seek = [&](int it, int j) {
@@ -183,13 +244,17 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         cur.tile = tile;
         c_cnt = tile >= 0 ? cnt : 0;
         c_wbase = 0;
+        if (qmode) {
+          q_next = take_claim();  // claimed when the previous item started
+          claim();
+        }
         if (tile >= 0) {
           c_win = (nx_item == it) ? nx_win : load_blocks(tile, c_cnt, 0);
+          const int NB = COLD(NB), Hq = COLD(Hq);
           cur.m = tile % NB;
           cur.bh = tile / NB;
-          cur.kb = cur.bh / p.Hq;
-          cur.kh = (cur.bh % p.Hq) / p.G;
-          prefetch_next(it + 1);
+          cur.kvs = ((cur.bh / Hq) << 16) | ((cur.bh % Hq) / COLD(G));
+          prefetch_next(qmode ? q_next : it + 1);
         }
       }
       for (; j < c_cnt; ++j) {
@@ -205,7 +270,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           return;
         }
       }
-      ++it;
+      it = qmode ? q_next : it + 1;
       j = 0;
     }
   };
@@ -232,15 +297,16 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     v_voff[u] = r * vrs + (cp ^ C::swz_v(r)) * 16;
   }
   auto fetch = [&](const Step& s, int slot, bool k_side) {
+    const int kb = s.kvs >> 16, kh = s.kvs & 0xffff;
     const char* base = k_side
-                           ? reinterpret_cast<const char*>(p.k) + (s.kb * p.ks0 + s.kh * p.ks1) * (int64_t)sizeof(T)
-                           : reinterpret_cast<const char*>(p.v) + (s.kb * p.vs0 + s.kh * p.vs1) * (int64_t)sizeof(T);
+                           ? reinterpret_cast<const char*>(p.k) + (kb * p.ks0 + kh * p.ks1) * (int64_t)sizeof(T)
+                           : reinterpret_cast<const char*>(p.v) + (kb * p.vs0 + kh * p.vs1) * (int64_t)sizeof(T);
     const int rs = k_side ? krs : vrs;
-    const auto r = buffer_rsrc(base, S * rs);
-    const int so = (s.n * B + s.hs * kKS) * rs;
+    const int row = s.n * B + s.hs * kKS;
+    const auto r = buffer_rsrc(base + (int64_t)row * rs, max(S - row, 0) * rs);
     char* dst = (k_side ? kring : vring) + slot * C::kTile + wave * C::kInstsPerWave * 1024;
 #pragma unroll
-    for (int u = 0; u < C::kInstsPerWave; ++u) dma16(r, dst + u * 1024, (k_side ? k_voff[u] : v_voff[u]) + so);
+    for (int u = 0; u < C::kInstsPerWave; ++u) dma16(r, dst + u * 1024, k_side ? k_voff[u] : v_voff[u]);
   };
   // all of this wave's direct loads have landed in LDS (vmcnt(0) only)
   auto wait_loads = [&]() { wait_vmcnt<0>(); };
@@ -254,10 +320,11 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   auto start_tile = [&](const Step& s) {
     t_bh = s.bh;
     t_m = s.m;
-    const int bi = s.bh / p.Hq, h = s.bh % p.Hq;
+    const int Hq = COLD(Hq);
+    const int bi = s.bh / Hq, h = s.bh % Hq;
     const int qrow = s.m * B + wave * 32 + col;
-    const char* rp = reinterpret_cast<const char*>(p.q) +
-                     (bi * p.qs0 + h * p.qs1 + (int64_t)qrow * p.qs2) * (int64_t)sizeof(T);
+    const char* rp = reinterpret_cast<const char*>(COLD(q)) +
+                     (bi * COLD(qs0) + h * COLD(qs1) + (int64_t)qrow * COLD(qs2)) * (int64_t)sizeof(T);
 #pragma unroll
     for (int dg = 0; dg < C::kDG; ++dg) {
       // bf16: lane half g holds d = 16*dg + 8*g .. +7; fp32: d = 8*dg + 4*g .. +3
@@ -271,12 +338,15 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   };
 
   auto finish_tile = [&]() {
-    const int bi = t_bh / p.Hq, h = t_bh % p.Hq;
+    const int Hq = COLD(Hq);
+    const int bi = t_bh / Hq, h = t_bh % Hq;
     const float l = sum_xor32(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int qrow = t_m * B + wave * 32 + col;
     if (qrow < S) {
-      const int64_t orow = bi * p.os0 + h * p.os1 + (int64_t)qrow * p.os2;
+      const int64_t orow = bi * COLD(os0) + h * COLD(os1) + (int64_t)qrow * COLD(os2);
+      void* const out = COLD(o);
+      const bool out_f32 = COLD(out_f32);
 #pragma unroll
       for (int dt = 0; dt < C::kDT; ++dt) {
 #pragma unroll
@@ -284,16 +354,16 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           const int d = dt * 32 + r4 * 8 + half * 4;
           const float o0 = oacc[dt][r4 * 4 + 0] * inv, o1 = oacc[dt][r4 * 4 + 1] * inv;
           const float o2 = oacc[dt][r4 * 4 + 2] * inv, o3 = oacc[dt][r4 * 4 + 3] * inv;
-          if (C::kBf16 && !p.out_f32) {
-            *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(p.o) + orow + d) =
+          if (C::kBf16 && !out_f32) {
+            *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(out) + orow + d) =
                 uint2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
           } else {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.o) + orow + d) = f32x4{o0, o1, o2, o3};
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow + d) = f32x4{o0, o1, o2, o3};
           }
         }
       }
-      if (p.lse && half == 0)
-        p.lse[(int64_t)t_bh * S + qrow] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : kNegInf;
+      float* const lse = COLD(lse);
+      if (lse && half == 0) lse[(int64_t)t_bh * S + qrow] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : kNegInf;
     }
   };
 
@@ -512,6 +582,10 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
 }
 
+__global__ void queue_reset_kernel(int* counter) {
+  if (threadIdx.x == 0) *counter = 0;
+}
+
 template <typename T, int D, int B>
 hipError_t launch_t(const PrefillParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_kernel<T, D, B>), dim3(grid), dim3(2 * B), 0, stream, p);
@@ -521,6 +595,12 @@ hipError_t launch_t(const PrefillParams& p, int grid, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int grid, hipStream_t stream) {
+  if (p.queue) {
+    // a kernel, not a memset, so that the call can be captured in a graph
+    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, stream, p.queue);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (dtype == 0) {
     if (D == 128 && B == 128) return launch_t<bf16_t, 128, 128>(p, grid, stream);
     if (D == 128 && B == 64) return launch_t<bf16_t, 128, 64>(p, grid, stream);

@@ -188,7 +188,8 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t& before, uin
 // index order.
 template <int NT, int CPT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
-  constexpr int kDPT = 256 / NT;  // histogram bins per thread
+  constexpr int kDPT = NT >= 256 ? 1 : 256 / NT;  // histogram bins per bin-holding thread
+  constexpr int kBinThreads = 256 / kDPT;          // threads that hold bins
   __shared__ uint32_t red[NT / 64];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t found[3];
@@ -262,11 +263,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
       kmin = min(kmin, key[c]);
       kmax = max(kmax, key[c]);
     }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-  }
+  kmin = wave_umin(kmin);
+  kmax = wave_umax(kmax);
   if constexpr (NT > 64) {
     __shared__ uint32_t mm[2][NT / 64];
     if ((tid & 63) == 0) {
@@ -302,7 +300,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     uint32_t hc[kDPT], loc = 0;
 #pragma unroll
     for (int u = 0; u < kDPT; ++u) {
-      hc[u] = hist[255 - (kDPT * tid + u)];
+      hc[u] = tid < kBinThreads ? hist[255 - (kDPT * tid + u)] : 0u;
       loc += hc[u];
     }
     uint32_t above;
@@ -503,12 +501,13 @@ hipError_t launch_topk(const TopkParams& p, int max_cand, hipStream_t stream) {
     if (max_cand <= 4096) return topk_launch<256, 16>(p, stream);
     if (max_cand <= 8192) return topk_launch<256, 32>(p, stream);
   } else {
+    // decode rows are few (batch x heads): wide workgroups, few keys per thread
     if (max_cand <= 256) return topk_launch<256, 1>(p, stream);
     if (max_cand <= 1024) return topk_launch<256, 4>(p, stream);
     if (max_cand <= 2048) return topk_launch<256, 8>(p, stream);
-    if (max_cand <= 4096) return topk_launch<256, 16>(p, stream);
-    if (max_cand <= 8192) return topk_launch<256, 32>(p, stream);
-    if (max_cand <= 16384) return topk_launch<256, 64>(p, stream);
+    if (max_cand <= 4096) return topk_launch<512, 8>(p, stream);
+    if (max_cand <= 8192) return topk_launch<1024, 8>(p, stream);
+    if (max_cand <= 16384) return topk_launch<1024, 16>(p, stream);
   }
   return hipErrorInvalidValue;
 }

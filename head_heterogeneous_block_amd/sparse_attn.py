@@ -31,6 +31,7 @@ MAX_HEADS = 128
 
 EXPORTED = [
     "sa_version", "sa_last_error", "sa_lpt_schedule", "sa_lpt_schedule_grouped", "sa_lpt_order_bins",
+    "sa_lpt_queue_order",
     "sa_prefill_block_counts", "sa_decode_block_counts",
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_decode_workspace_size", "sa_sparse_attn_decode",
@@ -70,6 +71,7 @@ _SIG = {
     "sa_last_error": (ctypes.c_char_p, []),
     "sa_lpt_schedule": (ctypes.c_int32, [_i64p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
     "sa_lpt_order_bins": (ctypes.c_int32, [_i32p, ctypes.c_int32, _i32p]),
+    "sa_lpt_queue_order": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, _i32p]),
     "sa_lpt_schedule_grouped": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
     "sa_prefill_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
@@ -207,6 +209,21 @@ def sa_lpt_order_bins(bin_offsets: np.ndarray, items_by_bin: np.ndarray) -> np.n
     return items
 
 
+def sa_lpt_queue_order(loads: Sequence[int], group_of_item: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Item order for the work queue: groups ascending, largest load first inside a group."""
+    ld = np.ascontiguousarray(loads, dtype=np.int64)
+    n = ld.size
+    order = np.empty(n, dtype=np.int32)
+    gp = None
+    if group_of_item is not None:
+        gp = np.ascontiguousarray(group_of_item, dtype=np.int32)
+        if gp.size != n:
+            raise ValueError("group_of_item must have one entry per item")
+    _check(_lib.sa_lpt_queue_order(ld.ctypes.data_as(_i64p), gp.ctypes.data_as(_i32p) if gp is not None else None, n,
+                                   order.ctypes.data_as(_i32p)))
+    return order
+
+
 def sa_prefill_block_counts(desc: sa_attn_desc, budgets) -> tuple[np.ndarray, int]:
     nb = -(-desc.q_len // desc.block_size)
     counts = np.empty((desc.batch, desc.n_q_heads, nb), np.int32)
@@ -286,10 +303,13 @@ class PrefillPlan:
     ``bin_order``: "index" walks each bin in item order (sa_lpt_order_bins),
     "lpt" in assignment order.  ``xcd_groups`` > 0 uses the two-level placement
     (sa_lpt_schedule_grouped): chunks of ``xcd_chunk`` query blocks of one
-    (sequence, KV head) onto ``xcd_groups`` cache partitions, then LPT inside."""
+    (sequence, KV head) onto ``xcd_groups`` cache partitions, then LPT inside.
+    ``queue``: instead of fixed bins, the ``n_bins`` workgroups take the tiles
+    longest first from a shared counter (the greedy rule applied online)."""
 
     def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
-                 kernel_variant: int = 0, bin_order: str = "index", xcd_groups: int = 0, xcd_chunk: int = 64):
+                 kernel_variant: int = 0, bin_order: str = "index", xcd_groups: int = 0, xcd_chunk: int = 64,
+                 queue: bool = False):
         self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_prefill_block_counts(self.desc, self.budgets)
@@ -301,7 +321,19 @@ class PrefillPlan:
         self.block_idx = torch.empty((q.shape[0], q.shape[1], self.nb, self.kmax), dtype=torch.int32, device=dev)
         self.block_cnt = torch.empty((q.shape[0], q.shape[1], self.nb), dtype=torch.int32, device=dev)
         self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
-        if n_bins > 0:
+        self.attn_ws = _workspace(sa_prefill_workspace_size(self.desc, self.kmax, n_bins), dev)
+        self.queue = queue
+        if queue:
+            if n_bins < 1:
+                raise ValueError("the work queue needs n_bins >= 1 workgroups")
+            # item = (b * Hq + h) * NB + m, grouped by (b, KV head) = (b * Hq + h) // G
+            G = q.shape[1] // k.shape[1]
+            group = (np.arange(self.counts.size, dtype=np.int64) // self.nb // G).astype(np.int32)
+            order = sa_lpt_queue_order(self.counts.reshape(-1), group)
+            self.bin_load = None
+            self.bin_offsets = None
+            self.items_by_bin = torch.from_numpy(order).to(dev)
+        elif n_bins > 0:
             loads = self.counts.reshape(-1)
             if xcd_groups > 0:
                 # item = (b * Hq + h) * NB + m; chunk = ((b * Hkv + h / G) * n_m + m / xcd_chunk)
@@ -333,7 +365,7 @@ class PrefillPlan:
 
     def attend(self, q, k, v, o, lse=None) -> None:
         sa_sparse_attn_prefill(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
-                               self.bin_offsets, self.items_by_bin, self.n_bins, self.out_f32)
+                               self.bin_offsets, self.items_by_bin, self.n_bins, self.out_f32, self.attn_ws)
 
 
 class DecodePlan:

@@ -158,6 +158,21 @@ sa_status sa_lpt_schedule_grouped(const int64_t* loads, const int32_t* chunk_of_
  * Invalid offsets are SA_ERR_INVALID_ARG. */
 sa_status sa_lpt_order_bins(const int32_t* bin_offsets, int32_t n_bins, int32_t* items_by_bin);
 
+/* Order of the items for the prefill work queue (host, synchronous): the
+ * greedy longest-processing-time rule of the S-HPLB pages (§2.B, §2.2) applied
+ * online by workgroups that each take the next item when they finish one,
+ * with the items grouped by group_of_item: groups in ascending order, inside
+ * a group the largest load first, equal loads in item order.  With the group
+ * of a prefill tile set to its (sequence, KV head), the tiles running at any
+ * moment read the keys and values of one KV head, which stay in the caches,
+ * and every group still ends with its smallest tiles.
+ *   loads[n_items]          [host] int64 >= 0
+ *   group_of_item[n_items]  [host] int32, may be NULL (one group)
+ *   order[n_items]          [host] out: item indices in queue order
+ * Negative loads are SA_ERR_INVALID_ARG. */
+sa_status sa_lpt_queue_order(const int64_t* loads, const int32_t* group_of_item, int32_t n_items,
+                             int32_t* order);
+
 /* Blocks kept per prefill row, from the budget rule alone (no data needed):
  * counts[b][h][m] for m < ceil(q_len/block_size) ([host] out, int32), and the
  * maximum over all rows in *kmax ([host] out, may be NULL).  These are the
@@ -212,10 +227,18 @@ size_t sa_prefill_workspace_size(const sa_attn_desc* desc, int32_t kmax, int32_t
  * KV head h/G: o = softmax(scale * q k^T) v over those keys.
  *   q, k, v [dev] dtype desc->dtype; o [dev] fp32 if out_f32 else desc->dtype;
  *   lse [dev] fp32 [batch][n_q_heads][q_len] natural-log sum-exp (may be NULL).
- *   Schedule: bin_offsets [dev] (n_bins+1) and items_by_bin [dev] from
- *   sa_lpt_schedule over the tiles item = (b*n_q_heads + h)*n_blocks + m; one
- *   persistent workgroup walks each bin.  NULL schedule = one workgroup per tile
- *   in natural order (n_bins ignored).  Every tile must appear exactly once. */
+ *   Schedule over the tiles item = (b*n_q_heads + h)*n_blocks + m, one of:
+ *   - bins: bin_offsets [dev] (n_bins+1) and items_by_bin [dev] from
+ *     sa_lpt_schedule; one persistent workgroup walks each bin;
+ *   - work queue: bin_offsets NULL, items_by_bin [dev] one global order of all
+ *     tiles (longest first is the greedy longest-processing-time rule run
+ *     online); n_bins persistent workgroups each take the next tile of the
+ *     order when they finish one.  The counter lives in workspace (>= 4 bytes,
+ *     sa_prefill_workspace_size) and is reset by the call on the stream, so
+ *     calls that share a workspace must not overlap;
+ *   - both NULL: one workgroup per tile in natural order (n_bins ignored).
+ *   Every tile must appear exactly once.  workspace may be NULL except in the
+ *   work-queue mode. */
 sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k,
                                  const void* v, void* o, float* lse, const int32_t* block_idx,
                                  const int32_t* block_cnt, int32_t kmax,

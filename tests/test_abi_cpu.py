@@ -78,6 +78,30 @@ def test_lpt_order_bins_keeps_bins_and_sorts():
 
 
 @pytest.mark.parametrize("seed", range(4))
+def test_lpt_queue_order(seed):
+    """Work-queue order: a permutation, groups ascending, inside a group the
+    loads do not increase and equal loads keep item order (the same order a
+    stable lexicographic sort on (group, -load) gives)."""
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(0, 5000))
+    loads = rng.integers(0, 40, size=n)
+    groups = np.sort(rng.integers(0, 9, size=n)) if seed % 2 else rng.integers(0, 9, size=n)
+    order = SA.sa_lpt_queue_order(loads, groups)
+    assert sorted(order.tolist()) == list(range(n))
+    g, l = groups[order], loads[order]
+    assert np.all(np.diff(g) >= 0)
+    same = np.diff(g) == 0
+    assert np.all(np.diff(l)[same] <= 0)
+    ties = same & (np.diff(l) == 0)
+    assert np.all(np.diff(order)[ties] > 0)
+    np.testing.assert_array_equal(order, np.lexsort((-loads, groups)))
+    # no groups: plain longest first
+    np.testing.assert_array_equal(SA.sa_lpt_queue_order(loads), np.argsort(-loads, kind="stable"))
+    with pytest.raises(SA.SaError):
+        SA.sa_lpt_queue_order([1, -2, 3])
+
+
+@pytest.mark.parametrize("seed", range(4))
 def test_lpt_grouped_is_two_oracle_placements(seed):
     """Two-level placement = the oracle's LPT of chunk loads onto groups, then
     the oracle's LPT of each group's items (in item order) onto its bins, bin

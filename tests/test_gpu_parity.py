@@ -77,12 +77,13 @@ PREFILL_SHAPES = [
 
 
 @pytest.mark.parametrize("name,over", PREFILL_SHAPES, ids=[s[0] for s in PREFILL_SHAPES])
-@pytest.mark.parametrize("n_bins", [0, 37])
-def test_prefill_bf16_all_rows(name, over, n_bins):
+@pytest.mark.parametrize("sched", ["natural", "bins37", "queue23"])
+def test_prefill_bf16_all_rows(name, over, sched):
     spec = W.LLAMA_32K.with_(**over)
     inp = W.make_prefill(spec, 77, device=DEV)
-    _say("case:", name, "bins", n_bins)
-    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins)
+    _say("case:", name, "schedule", sched)
+    n_bins = {"natural": 0, "bins37": 37, "queue23": 23}[sched]
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins, queue=sched.startswith("queue"))
     q, k, v = to_host(inp)
     oidx, ocnt, scores = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, return_scores=True)
     gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
@@ -118,16 +119,22 @@ def test_prefill_schedules_bitwise_equal():
         _say("schedule", n_bins)
         _, _, o, lse, _ = prefill_gpu(inp, n_bins=n_bins)
         outs.append((o, lse))
-    # two-level (cache-partition) placement and assignment-order bins
-    for kw in (dict(xcd_groups=8, xcd_chunk=4), dict(bin_order="lpt")):
+    # two-level (cache-partition) placement, assignment-order bins, and the
+    # work queue with one worker, some, and more workers than tiles (each
+    # queue plan attends twice: the counter is reset by every call)
+    for kw in (dict(xcd_groups=8, xcd_chunk=4), dict(bin_order="lpt"), dict(queue=True),
+               dict(queue=True, n_bins=1), dict(queue=True, n_bins=5000)):
         _say("schedule", kw)
-        plan = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=64, out_f32=True, **kw)
-        o = torch.empty(inp.q.shape, dtype=torch.float32, device=DEV)
-        lse = torch.empty(inp.q.shape[:3], dtype=torch.float32, device=DEV)
+        kw = dict(kw)
+        nb = kw.pop("n_bins", 64)
+        plan = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=nb, out_f32=True, **kw)
         plan.select(inp.q, inp.k)
-        plan.attend(inp.q, inp.k, inp.v, o, lse)
-        torch.cuda.synchronize()
-        outs.append((o, lse))
+        for _ in range(2 if plan.queue else 1):
+            o = torch.full(inp.q.shape, float("nan"), dtype=torch.float32, device=DEV)
+            lse = torch.full(inp.q.shape[:3], float("nan"), dtype=torch.float32, device=DEV)
+            plan.attend(inp.q, inp.k, inp.v, o, lse)
+            torch.cuda.synchronize()
+            outs.append((o, lse))
     for o, lse in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
 
