@@ -303,10 +303,10 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                            : reinterpret_cast<const char*>(p.v) + (kb * p.vs0 + kh * p.vs1) * (int64_t)sizeof(T);
     const int rs = k_side ? krs : vrs;
     const int row = s.n * B + s.hs * kKS;
-    const auto r = buffer_rsrc(base + (int64_t)row * rs, max(S - row, 0) * rs);
+    const i32x4 r = buffer_rsrc_words(base + (int64_t)row * rs, max(S - row, 0) * rs);
     char* dst = (k_side ? kring : vring) + slot * C::kTile + wave * C::kInstsPerWave * 1024;
 #pragma unroll
-    for (int u = 0; u < C::kInstsPerWave; ++u) dma16(r, dst + u * 1024, k_side ? k_voff[u] : v_voff[u]);
+    for (int u = 0; u < C::kInstsPerWave; ++u) dma16_async(r, dst + u * 1024, k_side ? k_voff[u] : v_voff[u]);
   };
   // all of this wave's direct loads have landed in LDS (vmcnt(0) only)
   auto wait_loads = [&]() { wait_vmcnt<0>(); };
