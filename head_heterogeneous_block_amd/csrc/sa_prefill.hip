@@ -296,6 +296,13 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     k_voff[u] = perm_key(r) * krs + (cp ^ C::swz_k(r)) * 16;
     v_voff[u] = r * vrs + (cp ^ C::swz_v(r)) * 16;
   }
+  // The buffer starts at the step's first key row and ends at the sequence
+  // end, so the per-lane offsets stay fixed (no per-step vector arithmetic)
+  // and rows past the end read as zero.  The loads are issued from inline
+  // assembly: the compiler then does not make the fragment reads of the other
+  // ring slots wait for them, so each step's gathers have a whole step to
+  // land; the wait and barrier at the top of the next iteration order them
+  // before their slots are read.
   auto fetch = [&](const Step& s, int slot, bool k_side) {
     const int kb = s.kvs >> 16, kh = s.kvs & 0xffff;
     const char* base = k_side
