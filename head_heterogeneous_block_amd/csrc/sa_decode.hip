@@ -36,13 +36,13 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodePlanPar
   const int j = blockIdx.x, bi = blockIdx.y;
   const int tid = threadIdx.x;
   const int n_words = (p.n_atoms + 31) / 32;
-  for (int i = tid; i < p.G * n_words; i += kPlanThreads) bits[i] = 0u;
-  __syncthreads();
   // Every selected block sets its atoms' bits: a block of g = 16 * apb tokens
   // covers apb consecutive atoms, all in one 32-bit word (apb divides 32 and
-  // the block starts at a multiple of apb).  The block indices of all heads of
-  // a round are loaded before any is used.
-  constexpr int kGM = 8;
+  // the block starts at a multiple of apb).  The block counts and the block
+  // indices of all heads of a round are loaded together (the indices do not
+  // wait for the counts), and the bitmaps are cleared while they are in flight.
+  constexpr int kGM = 8;  // heads per group, at most
+  constexpr int kR = 2;   // rounds of kPlanThreads blocks per head in one batch of loads
   int cnt[kGM], apb[kGM];
 #pragma unroll
   for (int gi = 0; gi < kGM; ++gi) {
@@ -50,20 +50,31 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodePlanPar
     cnt[gi] = gi < p.G ? p.block_cnt[(int64_t)bi * p.Hq + h] : 0;
     apb[gi] = p.heads.gran[h] / kAtom;
   }
-  for (int b0 = 0; b0 < p.kmax; b0 += kPlanThreads) {
-    int nv[kGM];
+  int nv[kR][kGM];
+  auto load = [&](int b0) {
 #pragma unroll
-    for (int gi = 0; gi < kGM; ++gi) {
-      const int b = b0 + tid;
-      nv[gi] = b < cnt[gi] ? p.block_idx[((int64_t)bi * p.Hq + j * p.G + gi) * p.kmax + b] : -1;
-    }
+    for (int r = 0; r < kR; ++r)
 #pragma unroll
-    for (int gi = 0; gi < kGM; ++gi) {
-      if (nv[gi] < 0) continue;
-      const int a = nv[gi] * apb[gi];
-      const int na = min(apb[gi], p.n_atoms - a);
-      if (na > 0) atomicOr(&bits[gi * n_words + (a >> 5)], ((na >= 32 ? 0u : (1u << na)) - 1u) << (a & 31));
-    }
+      for (int gi = 0; gi < kGM; ++gi) {
+        const int b = b0 + r * kPlanThreads + tid;
+        nv[r][gi] = gi < p.G && b < p.kmax ? p.block_idx[((int64_t)bi * p.Hq + j * p.G + gi) * p.kmax + b] : -1;
+      }
+  };
+  load(0);
+  for (int i = tid; i < p.G * n_words; i += kPlanThreads) bits[i] = 0u;
+  __syncthreads();
+  for (int b0 = 0; b0 < p.kmax; b0 += kR * kPlanThreads) {
+    if (b0 > 0) load(b0);
+#pragma unroll
+    for (int r = 0; r < kR; ++r)
+#pragma unroll
+      for (int gi = 0; gi < kGM; ++gi) {
+        const int b = b0 + r * kPlanThreads + tid;
+        if (b >= cnt[gi] || nv[r][gi] < 0) continue;
+        const int a = nv[r][gi] * apb[gi];
+        const int na = min(apb[gi], p.n_atoms - a);
+        if (na > 0) atomicOr(&bits[gi * n_words + (a >> 5)], ((na >= 32 ? 0u : (1u << na)) - 1u) << (a & 31));
+      }
   }
   __syncthreads();
   // ordered compaction of the union, 32 atoms (one word) per thread per pass
@@ -74,9 +85,12 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodePlanPar
   uint32_t* out = p.atoms + ((int64_t)bi * p.Hkv + j) * p.max_union;
   for (int w0 = 0; w0 < n_words; w0 += kPlanThreads) {
     const int wi = w0 + tid;
-    uint32_t u = 0;
-    if (wi < n_words)
-      for (int gi = 0; gi < p.G; ++gi) u |= bits[gi * n_words + wi];
+    uint32_t hw[kGM], u = 0;  // this word of every head's bitmap, and their union
+#pragma unroll
+    for (int gi = 0; gi < kGM; ++gi) {
+      hw[gi] = wi < n_words && gi < p.G ? bits[gi * n_words + wi] : 0u;
+      u |= hw[gi];
+    }
     const uint32_t c = __popc(u);
     // exclusive scan of c across the block
     const uint32_t x = wave_scan_incl(c);
@@ -92,7 +106,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodePlanPar
       rem &= rem - 1;
       const int a = wi * 32 + b;
       uint32_t mask = 0;
-      for (int gi = 0; gi < p.G; ++gi) mask |= ((bits[gi * n_words + wi] >> b) & 1u) << gi;
+#pragma unroll
+      for (int gi = 0; gi < kGM; ++gi) mask |= ((hw[gi] >> b) & 1u) << gi;
       if (off < (uint32_t)p.max_union) out[off] = uint32_t(a) | (mask << 24);
       ++off;
     }
