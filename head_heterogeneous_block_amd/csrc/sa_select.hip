@@ -188,10 +188,8 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t x, uint32_t& before, uin
 // index order.
 template <int NT, int CPT>
 __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
-  constexpr int kDPT = NT >= 256 ? 1 : 256 / NT;  // histogram bins per bin-holding thread
-  constexpr int kBinThreads = 256 / kDPT;          // threads that hold bins
   __shared__ uint32_t red[NT / 64];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[2][256];
   __shared__ uint32_t found[3];
   __shared__ uint32_t kbuf[NT * CPT + NT * CPT / 32];
   const int row = blockIdx.x;
@@ -287,33 +285,38 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   uint32_t T = 0, ties_wanted = 0;  // on rel
   int width = bits < 8 ? bits : 8;
   int shift = bits - width;
+  // Two barriers per pass: the histograms alternate between two buffers (the
+  // one for the next pass is cleared during this one), and wave 0 alone scans
+  // the 256 bins (4 per lane, descending digit order) to find the digit.
+  for (int i = tid; i < 256; i += NT) hist[0][i] = 0u;
+  __syncthreads();
 #pragma unroll 1
-  while (true) {
+  for (int pass = 0;; ++pass) {
+    uint32_t* const h = hist[pass & 1];
     const uint32_t dmask = (1u << width) - 1u;
-    for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int c = 0; c < CPT; ++c)
-      if (key[c] != 0u && (key[c] & pmask) == prefix) atomicAdd(&hist[(key[c] >> shift) & dmask], 1u);
+      if (key[c] != 0u && (key[c] & pmask) == prefix) atomicAdd(&h[(key[c] >> shift) & dmask], 1u);
     __syncthreads();
-    // bins in descending digit order: thread t holds digits 255 - (kDPT t + u)
-    uint32_t hc[kDPT], loc = 0;
+    if (tid < 64) {
+      uint32_t hc[4], loc = 0;
 #pragma unroll
-    for (int u = 0; u < kDPT; ++u) {
-      hc[u] = tid < kBinThreads ? hist[255 - (kDPT * tid + u)] : 0u;
-      loc += hc[u];
-    }
-    uint32_t above;
-    block_scan<NT>(loc, above, red);
-#pragma unroll
-    for (int u = 0; u < kDPT; ++u) {
-      if (above < need && above + hc[u] >= need) {
-        found[0] = 255u - uint32_t(kDPT * tid + u);
-        found[1] = need - above;
-        found[2] = hc[u];
+      for (int u = 0; u < 4; ++u) {
+        hc[u] = h[255 - (4 * tid + u)];
+        loc += hc[u];
       }
-      above += hc[u];
+      uint32_t above = wave_scan_incl(loc) - loc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (above < need && above + hc[u] >= need) {
+          found[0] = 255u - uint32_t(4 * tid + u);
+          found[1] = need - above;
+          found[2] = hc[u];
+        }
+        above += hc[u];
+      }
     }
+    for (int i = tid; i < 256; i += NT) hist[(pass + 1) & 1][i] = 0u;
     __syncthreads();
     const uint32_t digit = found[0], rem = found[1], bin = found[2];
     prefix |= digit << shift;
@@ -333,6 +336,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
     width = shift < 8 ? shift : 8;
     shift -= width;
   }
+  // One scan of the packed counts (ties << 16 | kept-above) places every kept
+  // candidate: the ties taken are the lowest-index ones.
   uint32_t n_tie = 0, n_gt = 0;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
@@ -342,11 +347,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
       else if (key[c] == T) ++n_tie;
     }
   }
-  uint32_t ties_before;
-  block_scan<NT>(n_tie, ties_before, red);
+  uint32_t before;
+  block_scan<NT>((n_tie << 16) | n_gt, before, red);
+  const uint32_t gt_before = before & 0xffffu, ties_before = before >> 16;
   const uint32_t my_ties = ties_before >= ties_wanted ? 0u : min(n_tie, ties_wanted - ties_before);
-  uint32_t pos;
-  block_scan<NT>(n_gt + my_ties, pos, red);
+  uint32_t pos = gt_before + min(ties_before, ties_wanted);
   uint32_t t_used = 0;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
