@@ -210,7 +210,7 @@ DecodeSelectWs decode_select_ws(const sa_attn_desc* d, const sa_head_budget* b, 
   return w;
 }
 
-constexpr int kChunkAtoms = 32;
+constexpr int kChunkAtoms = 40;  // atoms per decode attention wave: about one full round of waves at 128K
 constexpr int kAtomPad = 16;  // tokens an atom may reach past the cache end
 
 struct DecodeAttnWs {
