@@ -65,7 +65,19 @@ def timed(fn, stream, reps):
     return ts[len(ts) // 2], sum(ts) / len(ts), ts
 
 
-def traffic_from_profiles(kernel_src: str):
+PREFILL_KERNEL_SOURCES = ("sa_prefill.hip", "sa_prefill_common.hpp", "sa_device.hpp")
+
+
+def prefill_kernel_hash() -> str:
+    """sha256 over the source files of the prefill attention kernel, in order."""
+    h = hashlib.sha256()
+    for name in PREFILL_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "head_heterogeneous_block_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profiles():
     """HBM bytes per launch of the prefill attention kernel from the committed
     rocprofv3 counter summary, or None if absent or taken on other kernel code."""
     path = os.path.join(ROOT, "profiles", "prefill_attention_traffic.json")
@@ -73,7 +85,7 @@ def traffic_from_profiles(kernel_src: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    h = prefill_kernel_hash()
     if rec.get("kernel_source_sha256") != h:
         return None
     return rec.get("bytes_per_launch")
@@ -237,8 +249,7 @@ def main():
 
     prefill_ms = res.get("sel_ms", 0.0) + res.get("att_ms", 0.0)
     tflops = flops / (res["att_mean_ms"] * 1e-3) / 1e12 if "att_ms" in res else None
-    kernel_src = os.path.join(ROOT, "head_heterogeneous_block_amd", "csrc", "sa_prefill.hip")
-    traffic = traffic_from_profiles(kernel_src)
+    traffic = traffic_from_profiles()
     roofline = {
         "bound": "mfma",
         "achieved": tflops,
