@@ -384,9 +384,9 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
     const int atom = int(uint32_t(__builtin_amdgcn_readlane(int(aw), ai)) & 0xffffffu);
     const int ko = atom * kAtom * krs, vo = atom * kAtom * vrs;
 #pragma unroll
-    for (int u = 0; u < C::kInsts; ++u) dma16_async(krsrc, kst(S) + u * 1024, k_voff[u] + ko);
+    for (int u = 0; u < C::kInsts; ++u) dma16_stream(krsrc, kst(S) + u * 1024, k_voff[u] + ko);
 #pragma unroll
-    for (int u = 0; u < C::kInsts; ++u) dma16_async(vrsrc, vst(S) + u * 1024, v_voff[u] + vo);
+    for (int u = 0; u < C::kInsts; ++u) dma16_stream(vrsrc, vst(S) + u * 1024, v_voff[u] + vo);
   };
 
   f32x4 oacc[C::kDT];

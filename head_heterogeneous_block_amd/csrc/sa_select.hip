@@ -419,7 +419,7 @@ __global__ __launch_bounds__(64) void decode_scores_kernel(DecodeScoreParams p) 
   };
   auto issue = [&](auto S, int si) {
 #pragma unroll
-    for (int u = 0; u < kInsts; ++u) dma16_async(rsrc, stage(S) + u * 1024, si * kStageB + u * 1024 + lane * 16);
+    for (int u = 0; u < kInsts; ++u) dma16_stream(rsrc, stage(S) + u * 1024, si * kStageB + u * 1024 + lane * 16);
   };
   float* srow[MAXH];
 #pragma unroll
