@@ -48,7 +48,8 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 #pragma unroll
     for (int e = 0; e < kE; ++e) acc[e] = 0.f;
     for (int r = rg; r < cnt; r += kRG) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(base + (int64_t)(lo + r) * rs + ch * 16);
+      // read once: non-temporal, so the rows are not kept in the caches
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(lo + r) * rs + ch * 16));
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
