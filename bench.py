@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the decode step over the same cache held in 128-token pages")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) so that a "
                          "counter run can scale its HBM byte counters")
@@ -232,6 +234,23 @@ def main():
         res["dsel_ms"] = timed(dsel, stream, reps)[0]
         res["datt_ms"] = timed(datt, stream, reps)[0]
         res["dstep_ms"] = timed(lambda: (dsel(), datt()), stream, reps)[0]
+        if not args.no_paged:
+            # the same decode step over the cache scattered into per-KV-head
+            # pools of 128-token pages (the pools are built once, untimed)
+            pk = W.make_paged(din.k, din.v, 128, W.seed_of(dspec))
+            pplan = SA.PagedDecodePlan(din.q, pk.k_pages, pk.v_pages, pk.table, dspec.kv_len, din.budget)
+            pplan.pool(pk.k_pages)
+            po = torch.empty_like(din.q)
+            pstep = lambda: (pplan.select(din.q, pk.k_pages), pplan.attend(din.q, pk.k_pages, pk.v_pages, po))  # noqa: E731
+            pstep()
+            do_ref = torch.empty_like(din.q)
+            dplan.select(din.q, din.k)
+            dplan.attend(din.q, din.k, din.v, do_ref)
+            torch.cuda.synchronize()
+            res["paged_same"] = bool(torch.equal(po, do_ref))
+            res["paged_step_ms"] = timed(pstep, stream, reps)[0]
+            del pk, pplan
+            torch.cuda.empty_cache()
 
     bidx = plan.block_idx.cpu().numpy()
     bcnt = plan.block_cnt.cpu().numpy()
@@ -349,6 +368,11 @@ def main():
                    "step_ms": res.get("dstep_ms"), "bytes": dbytes, "step_gbps": dgbps,
                    "hbm_frac": dgbps / (M.PEAK_HBM_BYTES / 1e9) if dgbps else None,
                    "kv_gbps_attention_kernel": kv_gbps},
+        "decode_paged": None if "paged_step_ms" not in res else {
+            "page_size": 128, "step_ms": res["paged_step_ms"],
+            "step_gbps": dbytes["total"] / (res["paged_step_ms"] * 1e-3) / 1e9,
+            "hbm_frac": dbytes["total"] / (res["paged_step_ms"] * 1e-3) / M.PEAK_HBM_BYTES,
+            "same_output_as_contiguous": res["paged_same"]},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "cpu_baseline_decode": cpu_dec,

@@ -408,8 +408,17 @@ size_t sa_decode_pooled_size(const sa_attn_desc* desc, const sa_head_budget* bud
   return n;
 }
 
+static sa::PageTable page_table_of(const sa_kv_pages* pages) {
+  sa::PageTable t;
+  t.table = pages ? pages->table : nullptr;
+  t.page_size = pages ? pages->page_size : 0;
+  t.max_pages = pages ? pages->max_pages : 0;
+  t.pages_per_head = pages ? pages->pages_per_head : 0;
+  return t;
+}
+
 static sa_status pool_decode_into(const sa_attn_desc* d, const sa_head_budget* b, const void* k, float* out,
-                                  hipStream_t st) {
+                                  hipStream_t st, const sa_kv_pages* pages = nullptr) {
   size_t off = 0;
   for (int g : decode_pools(d, b)) {
     sa::PoolParams pp;
@@ -417,6 +426,7 @@ static sa_status pool_decode_into(const sa_attn_desc* d, const sa_head_budget* b
     pp.s0 = d->k_stride[0];
     pp.s1 = d->k_stride[1];
     pp.s2 = d->k_stride[2];
+    pp.pages = page_table_of(pages);
     pp.out = out + off;
     pp.heads = d->n_kv_heads;
     pp.T = d->kv_len;
@@ -439,6 +449,36 @@ sa_status sa_pool_keys_decode(const sa_attn_desc* desc, const sa_head_budget* bu
   if (!aligned16(k) || !aligned16(k_pooled)) return fail(SA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   if ((s = check_device())) return s;
   if ((s = pool_decode_into(desc, budgets, k, k_pooled, (hipStream_t)stream))) return s;
+  return ok();
+}
+
+// Checks of a paged cache description shared by the paged entry points.
+static sa_status check_pages(const sa_attn_desc* d, const sa_kv_pages* pages) {
+  if (!pages || !pages->table) return fail(SA_ERR_INVALID_ARG, "pages or pages->table is NULL");
+  if (pages->page_size < 64 || pages->page_size % 64)
+    return fail(SA_ERR_INVALID_ARG, "page_size %d is not a positive multiple of 64", pages->page_size);
+  if (pages->pages_per_head < 1) return fail(SA_ERR_INVALID_ARG, "pages_per_head must be >= 1");
+  if (int64_t(pages->max_pages) * pages->page_size < d->kv_len)
+    return fail(SA_ERR_INVALID_ARG, "max_pages %d pages of %d tokens do not cover kv_len %d", pages->max_pages,
+                pages->page_size, d->kv_len);
+  if (reinterpret_cast<uintptr_t>(pages->table) & 3) return fail(SA_ERR_INVALID_ARG, "page table must be 4-byte aligned");
+  const int64_t es = elem_size(d->dtype);
+  const int64_t rows = int64_t(pages->pages_per_head) * pages->page_size;
+  if ((rows + kAtomPad) * d->k_stride[2] * es >= (1ll << 31) || (rows + kAtomPad) * d->v_stride[2] * es >= (1ll << 31))
+    return fail(SA_ERR_UNSUPPORTED, "one KV head's page pool must span < 2 GiB");
+  return SA_OK;
+}
+
+sa_status sa_pool_keys_decode_paged(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* k_pages,
+                                    const sa_kv_pages* pages, float* k_pooled, void* stream) {
+  sa_status s = check_desc(desc, false);
+  if (s) return s;
+  if ((s = check_budgets(desc, budgets, false))) return s;
+  if ((s = check_pages(desc, pages))) return s;
+  if (!k_pages || !k_pooled) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(k_pages) || !aligned16(k_pooled)) return fail(SA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if ((s = check_device())) return s;
+  if ((s = pool_decode_into(desc, budgets, k_pages, k_pooled, (hipStream_t)stream, pages))) return s;
   return ok();
 }
 
@@ -675,13 +715,17 @@ size_t sa_decode_workspace_size(const sa_attn_desc* desc, const sa_head_budget* 
   return decode_attn_ws(desc, budgets).total;
 }
 
-sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* q,
-                                const void* k, const void* v, void* o, float* lse, const int32_t* block_idx,
-                                const int32_t* block_cnt, int32_t kmax, int32_t out_f32, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+static sa_status decode_impl(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* q, const void* k,
+                             const void* v, const sa_kv_pages* pages, void* o, float* lse, const int32_t* block_idx,
+                             const int32_t* block_cnt, int32_t kmax, int32_t out_f32, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   sa_status s = check_desc(desc, false);
   if (s) return s;
   if ((s = check_budgets(desc, budgets, false))) return s;
+  if (pages) {
+    if ((s = check_pages(desc, pages))) return s;
+    if (desc->dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "paged caches are supported for bf16 only");
+  }
   if (!q || !k || !v || !o || !block_idx || !block_cnt) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned16(k) || !aligned16(v)) return fail(SA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
   const int G = desc->n_q_heads / desc->n_kv_heads;
@@ -695,7 +739,7 @@ sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* 
   if (!aligned16(workspace)) return fail(SA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const int64_t n_atoms = cdiv(desc->kv_len, sa::kAtom);
   if (int64_t(G) * cdiv(n_atoms, 32) * 4 > 64 * 1024) return fail(SA_ERR_UNSUPPORTED, "kv_len too long for the plan");
-  {
+  if (!pages) {
     // the attention kernels address a (sequence, KV head) slice with 32-bit offsets
     const int64_t es = elem_size(desc->dtype);
     if (int64_t(desc->kv_len + kAtomPad) * desc->k_stride[2] * es >= (1ll << 31) ||
@@ -746,6 +790,7 @@ sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* 
   ap.G = G;
   ap.kv_len = desc->kv_len;
   ap.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+  ap.pages = page_table_of(pages);
   ap.part_o = part_o;
   ap.part_ml = part_ml;
   if ((e = sa::launch_decode_attn(ap, desc->dtype, desc->head_dim, desc->batch, st)) != hipSuccess)
@@ -767,6 +812,23 @@ sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* 
   if ((e = sa::launch_decode_combine(cp, desc->dtype, desc->head_dim, desc->batch, st)) != hipSuccess)
     return hip_fail(e, "decode combine");
   return ok();
+}
+
+sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* q,
+                                const void* k, const void* v, void* o, float* lse, const int32_t* block_idx,
+                                const int32_t* block_cnt, int32_t kmax, int32_t out_f32, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return decode_impl(desc, budgets, q, k, v, nullptr, o, lse, block_idx, block_cnt, kmax, out_f32, workspace,
+                     workspace_bytes, stream);
+}
+
+sa_status sa_sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* q,
+                                      const void* k_pages, const void* v_pages, const sa_kv_pages* pages, void* o,
+                                      float* lse, const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
+                                      int32_t out_f32, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!pages) return fail(SA_ERR_INVALID_ARG, "pages is NULL");
+  return decode_impl(desc, budgets, q, k_pages, v_pages, pages, o, lse, block_idx, block_cnt, kmax, out_f32,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

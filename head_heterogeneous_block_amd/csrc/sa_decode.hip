@@ -359,8 +359,21 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
   }
 
   const int krs = int(p.ks2 * 2), vrs = int(p.vs2 * 2);
-  const i32x4 krsrc = buffer_rsrc_words(reinterpret_cast<const bf16_t*>(p.k) + bi * p.ks0 + j * p.ks1, p.kv_len * krs);
-  const i32x4 vrsrc = buffer_rsrc_words(reinterpret_cast<const bf16_t*>(p.v) + bi * p.vs0 + j * p.vs1, p.kv_len * vrs);
+  // The buffer is the (sequence, KV head) slice of the cache, or with pages the
+  // KV head's page pool; arow (lane l: atom a_beg + l) is the row of the atom's
+  // first token in it.  Rows past the buffer read as zero.
+  const bool paged = p.pages.table != nullptr;
+  const int n_rows = paged ? p.pages.pages_per_head * p.pages.page_size : p.kv_len;
+  const i32x4 krsrc = buffer_rsrc_words(reinterpret_cast<const bf16_t*>(p.k) + (paged ? 0 : bi * p.ks0) + j * p.ks1,
+                                        n_rows * krs);
+  const i32x4 vrsrc = buffer_rsrc_words(reinterpret_cast<const bf16_t*>(p.v) + (paged ? 0 : bi * p.vs0) + j * p.vs1,
+                                        n_rows * vrs);
+  int arow = int(aw & 0xffffffu) * kAtom;
+  if (paged && lane < na) {
+    const int ps = p.pages.page_size;
+    const int phys = p.pages.table[((int64_t)bi * p.Hkv + j) * p.pages.max_pages + arow / ps];
+    arow = (phys >= 0 && phys < p.pages.pages_per_head) ? phys * ps + arow % ps : n_rows;
+  }
   // Direct load u of a tensor writes LDS bytes 1024 u + 16 lane: stage row r,
   // physical chunk cp; it fetches the row's logical chunk cp ^ swizzle.
   int k_voff[C::kInsts], v_voff[C::kInsts];
@@ -381,8 +394,8 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
   };
   // issue the loads of atom `ai` of the chunk into stage S
   auto issue = [&](auto S, int ai) {
-    const int atom = int(uint32_t(__builtin_amdgcn_readlane(int(aw), ai)) & 0xffffffu);
-    const int ko = atom * kAtom * krs, vo = atom * kAtom * vrs;
+    const int row = __builtin_amdgcn_readlane(arow, ai);
+    const int ko = row * krs, vo = row * vrs;
 #pragma unroll
     for (int u = 0; u < C::kInsts; ++u) dma16_stream(krsrc, kst(S) + u * 1024, k_voff[u] + ko);
 #pragma unroll
@@ -556,6 +569,7 @@ hipError_t launch_decode_attn(const DecodeAttnParams& p, int dtype, int D, int b
     else if (D == 64) hipLaunchKernelGGL(decode_attn_mfma_kernel<64>, grid, dim3(64), 0, stream, p);
     else return hipErrorInvalidValue;
   } else {
+    if (p.pages.table) return hipErrorInvalidValue;  // paged caches: bf16 only
     if (D == 128 && p.G <= 4) hipLaunchKernelGGL((decode_attn_kernel<float, 128, 4, 4>), grid, dim3(256), 0, stream, p);
     else if (D == 128 && p.G <= 8) hipLaunchKernelGGL((decode_attn_kernel<float, 128, 8, 8>), grid, dim3(256), 0, stream, p);
     else if (D == 64 && p.G <= 8) hipLaunchKernelGGL((decode_attn_kernel<float, 64, 4, 8>), grid, dim3(256), 0, stream, p);

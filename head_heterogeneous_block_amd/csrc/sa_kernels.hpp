@@ -19,11 +19,20 @@ struct HeadTable {
 };
 
 // ---------------------------------------------------------------- pooling
+// Paged KV: each KV head has its own pool of physical pages of page_size
+// token rows; page_table[(b * heads + h) * max_pages + p] is the physical page
+// (in head h's pool) of logical page p of sequence b.
+struct PageTable {
+  const int32_t* table;  // nullptr: contiguous cache
+  int page_size, max_pages, pages_per_head;
+};
+
 struct PoolParams {
-  const void* x;         // [batch][heads][T][D] (strided)
+  const void* x;         // [batch][heads][T][D] (strided); paged: pools at x + h * s1, rows s2 apart
   int64_t s0, s1, s2;    // strides in elements
   float* out;            // [batch][heads][nb][D] fp32, contiguous
   int heads, T, g, nb, blocks_per_wg;
+  PageTable pages;       // g divides page_size
 };
 hipError_t launch_pool(const PoolParams& p, int dtype, int D, int batch, hipStream_t stream);
 
@@ -119,6 +128,7 @@ struct DecodeAttnParams {
   int max_union, chunk_atoms, n_chunks;  // chunks per (b, kvh)
   int Hq, Hkv, G, kv_len;
   float scale_log2;
+  PageTable pages;  // paged: k, v are the pools (head stride ks1 / vs1, row stride ks2 / vs2)
   float* part_o;    // [batch][Hkv][n_chunks][G][D]
   float* part_ml;   // [batch][Hkv][n_chunks][G][2]  (max in log2 domain, sum)
 };

@@ -37,13 +37,25 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   const int tid = threadIdx.x;
   const int ch = tid % kCh, rg = tid / kCh;
   const int h = blockIdx.y, bi = blockIdx.z;
-  const char* base = reinterpret_cast<const char*>(p.x) + (bi * p.s0 + h * p.s1) * (int64_t)sizeof(T);
+  const bool paged = p.pages.table != nullptr;
+  const char* base = reinterpret_cast<const char*>(p.x) + ((paged ? 0 : bi * p.s0) + h * p.s1) * (int64_t)sizeof(T);
   const int64_t rs = p.s2 * (int64_t)sizeof(T);
   for (int bb = 0; bb < p.blocks_per_wg; ++bb) {
     const int n = blockIdx.x * p.blocks_per_wg + bb;
     if (n >= p.nb) break;
-    const int lo = n * p.g;
+    int lo = n * p.g;
     const int cnt = min(p.g, p.T - lo);
+    if (paged) {
+      // the block lies in one page (g divides the page size): its first row in
+      // the pool; rows of an out-of-range page entry are not read
+      const int ps = p.pages.page_size;
+      const int phys = p.pages.table[((int64_t)bi * p.heads + h) * p.pages.max_pages + lo / ps];
+      if (phys < 0 || phys >= p.pages.pages_per_head) {
+        for (int d = tid; d < D; d += 256) p.out[(((int64_t)bi * p.heads + h) * p.nb + n) * D + d] = 0.f;
+        continue;
+      }
+      lo = phys * ps + lo % ps;
+    }
     float acc[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) acc[e] = 0.f;

@@ -35,6 +35,7 @@ EXPORTED = [
     "sa_prefill_block_counts", "sa_decode_block_counts",
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_decode_workspace_size", "sa_sparse_attn_decode",
+    "sa_pool_keys_decode_paged", "sa_sparse_attn_decode_paged",
 ]
 
 
@@ -58,6 +59,11 @@ class sa_attn_desc(ctypes.Structure):
 class sa_head_budget(ctypes.Structure):
     _fields_ = [("min_blocks", ctypes.c_int32), ("ratio_q16", ctypes.c_uint32), ("n_sink", ctypes.c_int32),
                 ("n_local", ctypes.c_int32), ("granularity", ctypes.c_int32)]
+
+
+class sa_kv_pages(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("pages_per_head", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -87,6 +93,10 @@ _SIG = {
     "sa_decode_workspace_size": (ctypes.c_size_t, [_descp, _budp, ctypes.c_int32]),
     "sa_sparse_attn_decode": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+    "sa_pool_keys_decode_paged": (ctypes.c_int32, [_descp, _budp, _P, ctypes.POINTER(sa_kv_pages), _P, _P]),
+    "sa_sparse_attn_decode_paged": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, ctypes.POINTER(sa_kv_pages), _P,
+                                                     _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P,
+                                                     ctypes.c_size_t, _P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -161,6 +171,35 @@ def make_decode_desc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: Optio
     d.k_stride[:] = [k.stride(0), k.stride(1), k.stride(2)]
     d.v_stride[:] = [v.stride(0), v.stride(1), v.stride(2)]
     return d
+
+
+def make_paged_decode_desc(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, kv_len: int,
+                           o: Optional[torch.Tensor] = None, scale: float = 0.0) -> sa_attn_desc:
+    """Descriptor for q/o ``[b, Hq, D]`` and a paged cache whose pools k_pages /
+    v_pages are ``[Hkv, pages_per_head, page_size, D]`` (row-contiguous pages)."""
+    b, hq, D = q.shape
+    d = sa_attn_desc()
+    d.batch, d.n_q_heads, d.n_kv_heads, d.head_dim = b, hq, k_pages.shape[0], D
+    d.q_len, d.kv_len, d.block_size, d.dtype = 1, kv_len, 0, _dtype_code(q)
+    d.softmax_scale = scale
+    oo = o if o is not None else q
+    d.q_stride[:] = [q.stride(0), q.stride(1), 0]
+    d.o_stride[:] = [oo.stride(0), oo.stride(1), 0]
+    for t, st in ((k_pages, d.k_stride), (v_pages, d.v_stride)):
+        if t.stride(1) != t.shape[2] * t.stride(2):
+            raise ValueError("the pages of a pool must follow each other row by row")
+        st[:] = [0, t.stride(0), t.stride(2)]
+    return d
+
+
+def make_pages(table: torch.Tensor, page_size: int, pages_per_head: int) -> sa_kv_pages:
+    """Page description for a device int32 table ``[b, Hkv, max_pages]``."""
+    if table.dtype != torch.int32 or not table.is_contiguous():
+        raise ValueError("the page table must be a contiguous int32 tensor")
+    p = sa_kv_pages()
+    p.table = table.data_ptr()
+    p.page_size, p.max_pages, p.pages_per_head = page_size, table.shape[2], pages_per_head
+    return p
 
 
 # ---------------------------------------------------------------- host calls
@@ -292,6 +331,21 @@ def sa_sparse_attn_decode(desc: sa_attn_desc, budgets, q, k, v, o, lse, block_id
                                       workspace.numel(), _stream(q)))
 
 
+def sa_pool_keys_decode_paged(desc: sa_attn_desc, budgets, k_pages: torch.Tensor, pages: sa_kv_pages,
+                              k_pooled: torch.Tensor) -> None:
+    _check(_lib.sa_pool_keys_decode_paged(ctypes.byref(desc), budgets, _ptr(k_pages), ctypes.byref(pages),
+                                          _ptr(k_pooled), _stream(k_pages)))
+
+
+def sa_sparse_attn_decode_paged(desc: sa_attn_desc, budgets, q, k_pages, v_pages, pages: sa_kv_pages, o, lse,
+                                block_idx, block_cnt, kmax: int, workspace: torch.Tensor,
+                                out_f32: bool = False) -> None:
+    _check(_lib.sa_sparse_attn_decode_paged(ctypes.byref(desc), budgets, _ptr(q), _ptr(k_pages), _ptr(v_pages),
+                                            ctypes.byref(pages), _ptr(o), _ptr(lse), _ptr(block_idx),
+                                            _ptr(block_cnt), kmax, 1 if out_f32 else 0, _ptr(workspace),
+                                            workspace.numel(), _stream(q)))
+
+
 # ---------------------------------------------------------------- conveniences
 # (allocation + the calls above, in order; still no compute outside the library)
 
@@ -395,3 +449,31 @@ class DecodePlan:
     def attend(self, q, k, v, o, lse=None) -> None:
         sa_sparse_attn_decode(self.desc, self.budgets, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
                               self.attn_ws, self.out_f32)
+
+
+class PagedDecodePlan(DecodePlan):
+    """DecodePlan over a paged cache: pools ``[Hkv, pages_per_head, page_size,
+    D]`` and a page table ``[b, Hkv, max_pages]`` (``table``).  Selection reads
+    the pooled-key cache built by ``pool``, as for a contiguous cache."""
+
+    def __init__(self, q, k_pages, v_pages, table, kv_len: int, budget: dict, out_f32: bool = False):
+        self.desc = make_paged_decode_desc(q, k_pages, v_pages, kv_len)
+        self.pages = make_pages(table, k_pages.shape[2], k_pages.shape[1])
+        self.table = table  # keeps the table alive while the plan holds its address
+        self.budgets = make_budgets(budget)
+        self.counts, self.kmax = sa_decode_block_counts(self.desc, self.budgets)
+        self.out_f32 = out_f32
+        dev = q.device
+        self.block_idx = torch.empty((q.shape[0], q.shape[1], self.kmax), dtype=torch.int32, device=dev)
+        self.block_cnt = torch.empty((q.shape[0], q.shape[1]), dtype=torch.int32, device=dev)
+        self.k_pooled = torch.empty(max(sa_decode_pooled_size(self.desc, self.budgets) // 4, 4),
+                                    dtype=torch.float32, device=dev)
+        self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
+        self.attn_ws = _workspace(sa_decode_workspace_size(self.desc, self.budgets, self.kmax), dev)
+
+    def pool(self, k_pages) -> None:
+        sa_pool_keys_decode_paged(self.desc, self.budgets, k_pages, self.pages, self.k_pooled)
+
+    def attend(self, q, k_pages, v_pages, o, lse=None) -> None:
+        sa_sparse_attn_decode_paged(self.desc, self.budgets, q, k_pages, v_pages, self.pages, o, lse,
+                                    self.block_idx, self.block_cnt, self.kmax, self.attn_ws, self.out_f32)

@@ -26,7 +26,7 @@ import numpy as np
 import torch
 
 # purposes of the independent random streams
-_P_Q, _P_K, _P_V, _P_DIR, _P_HOT, _P_BUDGET = range(6)
+_P_Q, _P_K, _P_V, _P_DIR, _P_HOT, _P_BUDGET, _P_PAGES = range(7)
 
 
 @dataclass(frozen=True)
@@ -324,6 +324,41 @@ def make_decode(spec: DecodeSpec, seed: int, device="cpu") -> DecodeInputs:
         v[bi] = torch.randn((Hk, L, D), generator=_torch_gen(dev, seed, _P_V, bi), device=dev,
                             dtype=torch.float32).to(dt)
     return DecodeInputs(spec, seed, q.to(dt), k, v, budget, hot, u)
+
+
+@dataclass
+class PagedKV:
+    k_pages: torch.Tensor  # [Hkv, pages_per_head, page_size, D]
+    v_pages: torch.Tensor
+    table: torch.Tensor  # int32 [b, Hkv, max_pages]: physical page of each logical page
+    page_size: int
+    kv_len: int
+
+
+def make_paged(k: torch.Tensor, v: torch.Tensor, page_size: int, seed: int, spare_pages: int = 3) -> PagedKV:
+    """The same cache scattered into per-KV-head page pools: logical page p of
+    sequence b goes to a physical page drawn by a seeded permutation of the head's
+    pool (``spare_pages`` pages of the pool stay unused, holding zeros).  Rows of
+    a last page past the cache end are zero.  Pure data movement."""
+    b, hk, L, D = k.shape
+    mp = -(-L // page_size)
+    pph = b * mp + spare_pages
+    dev = k.device
+    table = torch.empty((b, hk, mp), dtype=torch.int32)
+    pools = []
+    for x in (k, v):
+        pool = torch.zeros((hk, pph, page_size, D), dtype=x.dtype, device=dev)
+        pools.append(pool)
+    for j in range(hk):
+        perm = torch.from_numpy(_rng(seed, _P_PAGES, j).permutation(pph)[:b * mp].astype(np.int64))
+        table[:, j, :] = perm.view(b, mp).to(torch.int32)
+        idx = perm.to(dev)
+        for x, pool in zip((k, v), pools):
+            rows = torch.zeros((b, mp * page_size, D), dtype=x.dtype, device=dev)
+            rows[:, :L] = x[:, j]
+            pool[j].index_copy_(0, idx, rows.view(b * mp, page_size, D))
+            del rows
+    return PagedKV(pools[0], pools[1], table.to(dev), page_size, L)
 
 
 def to_numpy(t: torch.Tensor) -> np.ndarray:

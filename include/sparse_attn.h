@@ -261,6 +261,49 @@ sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* 
                                 int32_t kmax, int32_t out_f32, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- paged KV */
+
+/* A decode KV cache held in pages of page_size tokens, each KV head with its
+ * own pool of physical pages: the page-based KV substrate that partitions of
+ * any granularity map onto, with physical pages per attention head ("Unifying
+ * Sparse Attention with Hierarchical Memory for Scalable Long-Context LLM
+ * Serving" (Spin), §2.A partition abstraction and §2.B per-head physical
+ * pages).
+ *   K (and V) pool of KV head j: pages_per_head * page_size rows of head_dim
+ *   elements starting at k + j * desc->k_stride[1]; row r (token r % page_size
+ *   of physical page r / page_size) at + r * desc->k_stride[2].
+ *   desc->k_stride[0] / v_stride[0] are not used.
+ *   table [dev] int32 [batch][n_kv_heads][max_pages]: physical page (index into
+ *   that KV head's pool) of logical page p = token / page_size of sequence b.
+ * page_size is a multiple of 64, so every selection block (16, 32 or 64 tokens)
+ * lies in one page; max_pages >= ceil(kv_len / page_size); one pool spans
+ * < 2 GiB.  Entries outside [0, pages_per_head) read as zero keys and values.
+ * Rows of a page past the cache end must hold finite values (they get
+ * probability zero).  Owned by the caller, read only. */
+typedef struct {
+  const int32_t* table;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t pages_per_head;
+} sa_kv_pages;
+
+/* sa_pool_keys_decode over a paged K cache (bf16 or fp32): the same pooled-key
+ * cache, bit for bit, as the contiguous cache holding the same tokens. */
+sa_status sa_pool_keys_decode_paged(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                                    const void* k_pages, const sa_kv_pages* pages, float* k_pooled,
+                                    void* stream);
+
+/* sa_sparse_attn_decode over a paged bf16 cache: the same results, bit for bit,
+ * as over the contiguous cache holding the same tokens (the same arithmetic in
+ * the same order; only the row addresses differ).  Workspace as
+ * sa_decode_workspace_size.  fp32 caches return SA_ERR_UNSUPPORTED. */
+sa_status sa_sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                                      const void* q, const void* k_pages, const void* v_pages,
+                                      const sa_kv_pages* pages, void* o, float* lse,
+                                      const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
+                                      int32_t out_f32, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

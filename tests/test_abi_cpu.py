@@ -258,3 +258,71 @@ def test_device_calls_fail_cleanly_without_gpu():
     st = lib.sa_sparse_attn_prefill(ctypes.byref(d), ctypes.c_void_p(3), fake, fake, fake, None, fake, fake, 16,
                                     None, None, 0, 0, None, 0, None)
     assert st == SA.SA_ERR_INVALID_ARG  # misaligned q
+
+
+def _paged_call(page_size=128, max_pages=8, pages_per_head=20, dtype="bf16", table=True, pages_null=False,
+                L=1000):
+    """Return the status of sa_sparse_attn_decode_paged on fake device pointers."""
+    import torch
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qd = torch.empty((2, 4, 128), dtype=dt, device="meta")
+    kp = torch.empty((2, 4, 128, 128), dtype=dt, device="meta")  # the pool shape only sets the strides
+    d = SA.make_paged_decode_desc(qd, kp, kp, L)
+    b = SA.make_budgets({"min_blocks": [2] * 4, "ratio_q16": [0] * 4, "n_sink": [1] * 4, "n_local": [1] * 4,
+                        "granularity": [64] * 4})
+    pg = SA.sa_kv_pages()
+    pg.table = (1 << 20) if table else None
+    pg.page_size, pg.max_pages, pg.pages_per_head = page_size, max_pages, pages_per_head
+    fake = ctypes.c_void_p(1 << 20)
+    st = SA._lib.sa_sparse_attn_decode_paged(ctypes.byref(d), b, fake, fake, fake,
+                                             None if pages_null else ctypes.byref(pg), fake, None, fake, fake, 2, 0,
+                                             fake, 1 << 40, None)
+    _paged_call.last_error = SA._lib.sa_last_error().decode()
+    st2 = SA._lib.sa_pool_keys_decode_paged(ctypes.byref(d), b, fake, None if pages_null else ctypes.byref(pg),
+                                            fake, None)
+    return st, st2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(page_size=96), SA.SA_ERR_INVALID_ARG),       # not a multiple of 64
+    (dict(page_size=0), SA.SA_ERR_INVALID_ARG),
+    (dict(max_pages=7), SA.SA_ERR_INVALID_ARG),        # 7 pages of 128 < 1000 tokens
+    (dict(pages_per_head=0), SA.SA_ERR_INVALID_ARG),
+    (dict(table=False), SA.SA_ERR_INVALID_ARG),
+    (dict(pages_null=True), SA.SA_ERR_INVALID_ARG),
+    (dict(page_size=1 << 16, max_pages=1, pages_per_head=1 << 8), SA.SA_ERR_UNSUPPORTED),  # pool of 4 GiB
+])
+def test_paged_arguments_rejected(kw, code):
+    st, st2 = _paged_call(**kw)
+    assert st == code, _paged_call.last_error
+    assert st2 == code
+
+
+def test_paged_decode_fp32_unsupported_and_valid_call_reaches_device_check():
+    import torch
+    st, st2 = _paged_call(dtype="f32")
+    assert st == SA.SA_ERR_UNSUPPORTED and "bf16" in _paged_call.last_error
+    st, st2 = _paged_call()
+    if not torch.cuda.is_available():
+        assert st in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP) and st2 in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
+
+
+def test_paged_pool_builder_scatters_exactly():
+    """The seeded page pools hold every cache row at the page the table names,
+    zero rows past the cache end, and a permutation of pages per KV head."""
+    import torch
+    spec = W.DECODE_128K.with_(batch=2, kv_len=1000)
+    inp = W.make_decode(spec, 3)
+    pk = W.make_paged(inp.k, inp.v, 128, 5)
+    b, hk, L, D = inp.k.shape
+    tab = pk.table.numpy()
+    for j in range(hk):
+        flat = tab[:, j].reshape(-1)
+        assert len(set(flat.tolist())) == flat.size and flat.min() >= 0 and flat.max() < pk.k_pages.shape[1]
+    back_k = torch.stack([torch.stack([pk.k_pages[j, torch.from_numpy(tab[bi, j]).long()].reshape(-1, D)[:L]
+                                       for j in range(hk)]) for bi in range(b)])
+    back_v = torch.stack([torch.stack([pk.v_pages[j, torch.from_numpy(tab[bi, j]).long()].reshape(-1, D)[:L]
+                                       for j in range(hk)]) for bi in range(b)])
+    assert torch.equal(back_k, inp.k) and torch.equal(back_v, inp.v)
+    last = pk.k_pages[0, int(tab[0, 0, -1])]
+    assert torch.count_nonzero(last[L % 128:]) == 0
