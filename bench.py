@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also time the offline budget calibration (block attention mass on the GPU, recovery "
+                         "table and max-min shifting on the host) on the 32K prefill workload")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the decode step over the same cache held in 128-token pages")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -91,6 +94,41 @@ def traffic_from_profiles():
     if rec.get("kernel_source_sha256") != h:
         return None
     return rec.get("bytes_per_launch")
+
+
+def calibration_timing(dev, stream):
+    """Offline budget calibration on the 32K Llama-shaped layer: the block
+    attention mass (two dense causal Q K^T passes) on the GPU, then the
+    recovery table and the max-min shift to a mean ratio of 1/8 on the host."""
+    import numpy as np
+    import torch
+    from head_heterogeneous_block_amd import sparse_attn as SA
+    from head_heterogeneous_block_amd import workloads as W
+    spec = W.LLAMA_32K
+    inp = W.make_prefill(spec, W.seed_of(spec), device=dev)
+    d = SA.make_prefill_desc(inp.q, inp.k, inp.v, inp.q, 128)
+    nb = spec.n_blocks
+    mass = torch.empty((spec.batch, spec.n_q_heads, nb, nb), dtype=torch.float32, device=dev)
+    run = lambda: SA.sa_block_attention_mass(d, inp.q, inp.k, mass)  # noqa: E731
+    run()
+    ms = timed(run, stream, 3)[0]
+    flops = 2 * 2.0 * spec.n_q_heads * spec.head_dim * sum(min(128, spec.seq_len - 128 * m) * (128 * m + 64.5)
+                                                           for m in range(nb))
+    host = mass.cpu().numpy()
+    H = spec.n_q_heads
+    bud = {"min_blocks": [2] * H, "ratio_q16": [0] * H, "n_sink": [1] * H, "n_local": [1] * H}
+    step = 1024
+    t0 = time.perf_counter()
+    rec = SA.sa_budget_recovery(host, bud, step)
+    t1 = time.perf_counter()
+    ratios = SA.sa_budget_shift(rec, step, H * 8192)
+    t2 = time.perf_counter()
+    rmin = float(min(rec[h, ratios[h] // step - 1] for h in range(H)))
+    return {"workload": spec.name, "mass_ms": ms, "mass_qk_tflops": flops / (ms * 1e-3) / 1e12,
+            "recovery_table_host_ms": (t1 - t0) * 1e3, "shift_host_ms": (t2 - t1) * 1e3, "step_q16": step,
+            "mean_ratio": 0.125, "lowest_recovery_equal_split": float(rec[:, 8192 // step - 1].min()),
+            "lowest_recovery_shifted": rmin,
+            "ratio_range": [int(np.min(ratios)), int(np.max(ratios))]}
 
 
 def cpu_baseline_prefill(inp, block_idx, block_cnt, tiles_per_head=96, select_heads=(0, 4, 8, 12, 16, 20, 24, 28)):
@@ -378,6 +416,8 @@ def main():
         "cpu_baseline_decode": cpu_dec,
         "ablation": ablation,
     }
+    if args.calibrate:
+        out["calibration"] = calibration_timing(dev, stream)
     print(json.dumps(out))
 
 

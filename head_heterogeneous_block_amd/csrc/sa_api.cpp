@@ -421,7 +421,7 @@ static sa_status pool_decode_into(const sa_attn_desc* d, const sa_head_budget* b
                                   hipStream_t st, const sa_kv_pages* pages = nullptr) {
   size_t off = 0;
   for (int g : decode_pools(d, b)) {
-    sa::PoolParams pp;
+    sa::PoolParams pp{};
     pp.x = k;
     pp.s0 = d->k_stride[0];
     pp.s1 = d->k_stride[1];
@@ -523,7 +523,7 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
   const int D = desc->head_dim;
   const int G = desc->n_q_heads / desc->n_kv_heads;
   hipError_t e;
-  sa::TopkParams tp;
+  sa::TopkParams tp{};
   std::memset(&tp, 0, sizeof tp);
   tp.idx = block_idx;
   tp.cnt = block_cnt;
@@ -536,7 +536,7 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
     float* qp = reinterpret_cast<float*>(ws + w.qpool);
     float* kp = reinterpret_cast<float*>(ws + w.kpool);
     float* sc = reinterpret_cast<float*>(ws + w.scores);
-    sa::PoolParams pp;
+    sa::PoolParams pp{};
     pp.g = desc->block_size;
     pp.nb = nb;
     pp.T = desc->q_len;
@@ -555,7 +555,7 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
     pp.out = kp;
     pp.heads = desc->n_kv_heads;
     if ((e = sa::launch_pool(pp, desc->dtype, D, desc->batch, st)) != hipSuccess) return hip_fail(e, "pool K");
-    sa::PrefillScoreParams sp;
+    sa::PrefillScoreParams sp{};
     sp.qp = qp;
     sp.kp = kp;
     sp.s = sc;
@@ -582,7 +582,7 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
   float* sc = reinterpret_cast<float*>(ws + w.scores);
   const std::vector<int> pools = decode_pools(desc, budgets);
   if (pools.size() > 4) return fail(SA_ERR_UNSUPPORTED, "more than 4 granularities");
-  sa::DecodeScoreParams dp;
+  sa::DecodeScoreParams dp{};
   std::memset(&dp, 0, sizeof dp);
   dp.q = q;
   dp.qs0 = desc->q_stride[0];
@@ -672,7 +672,7 @@ sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const 
       return fail(SA_ERR_UNSUPPORTED, "one (batch, KV head) slice of K or V must span < 2 GiB");
   }
   if ((s = check_device())) return s;
-  sa::PrefillParams p;
+  sa::PrefillParams p{};
   p.q = q;
   p.k = k;
   p.v = v;
@@ -754,7 +754,7 @@ static sa_status decode_impl(const sa_attn_desc* desc, const sa_head_budget* bud
   float* part_o = reinterpret_cast<float*>(ws + w.part_o);
   float* part_ml = reinterpret_cast<float*>(ws + w.part_ml);
   hipError_t e;
-  sa::DecodePlanParams pp;
+  sa::DecodePlanParams pp{};
   pp.block_idx = block_idx;
   pp.block_cnt = block_cnt;
   pp.kmax = kmax;
@@ -768,7 +768,7 @@ static sa_status decode_impl(const sa_attn_desc* desc, const sa_head_budget* bud
   pp.n_union = n_union;
   pp.heads = make_table(desc, budgets, false);
   if ((e = sa::launch_decode_plan(pp, desc->batch, st)) != hipSuccess) return hip_fail(e, "decode plan");
-  sa::DecodeAttnParams ap;
+  sa::DecodeAttnParams ap{};
   ap.q = q;
   ap.qs0 = desc->q_stride[0];
   ap.qs1 = desc->q_stride[1];
@@ -795,7 +795,7 @@ static sa_status decode_impl(const sa_attn_desc* desc, const sa_head_budget* bud
   ap.part_ml = part_ml;
   if ((e = sa::launch_decode_attn(ap, desc->dtype, desc->head_dim, desc->batch, st)) != hipSuccess)
     return hip_fail(e, "decode attention");
-  sa::DecodeCombineParams cp;
+  sa::DecodeCombineParams cp{};
   cp.part_o = part_o;
   cp.part_ml = part_ml;
   cp.n_union = n_union;
@@ -811,6 +811,114 @@ static sa_status decode_impl(const sa_attn_desc* desc, const sa_head_budget* bud
   cp.out_f32 = out_f32 ? 1 : 0;
   if ((e = sa::launch_decode_combine(cp, desc->dtype, desc->head_dim, desc->batch, st)) != hipSuccess)
     return hip_fail(e, "decode combine");
+  return ok();
+}
+
+sa_status sa_block_attention_mass(const sa_attn_desc* desc, const void* q, const void* k, float* mass,
+                                  void* stream) {
+  sa_status s = check_desc(desc, true);
+  if (s) return s;
+  if (desc->dtype != SA_BF16 || desc->block_size != 128)
+    return fail(SA_ERR_UNSUPPORTED, "block attention mass needs bf16 inputs and block_size 128");
+  if (!q || !k || !mass) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(mass) & 3))
+    return fail(SA_ERR_INVALID_ARG, "q and k must be 16-byte aligned, mass 4-byte aligned");
+  if ((s = check_device())) return s;
+  sa::MassParams p{};
+  p.q = q;
+  p.k = k;
+  p.qs0 = desc->q_stride[0];
+  p.qs1 = desc->q_stride[1];
+  p.qs2 = desc->q_stride[2];
+  p.ks0 = desc->k_stride[0];
+  p.ks1 = desc->k_stride[1];
+  p.ks2 = desc->k_stride[2];
+  p.mass = mass;
+  p.Hq = desc->n_q_heads;
+  p.G = desc->n_q_heads / desc->n_kv_heads;
+  p.S = desc->q_len;
+  p.NB = int(cdiv(desc->q_len, 128));
+  p.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+  const hipError_t e = sa::launch_block_mass(p, desc->head_dim, desc->batch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "block attention mass");
+  return ok();
+}
+
+sa_status sa_budget_recovery(const float* mass, int32_t batch, int32_t n_heads, int32_t n_blocks,
+                             const sa_head_budget* budgets, int32_t step_q16, double* recovery) {
+  if (!mass || !budgets || !recovery) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (batch < 1 || n_heads < 1 || n_blocks < 1) return fail(SA_ERR_INVALID_ARG, "batch, n_heads, n_blocks must be >= 1");
+  if (step_q16 < 1 || 65536 % step_q16) return fail(SA_ERR_INVALID_ARG, "step_q16 %d must divide 65536", step_q16);
+  for (int32_t h = 0; h < n_heads; ++h) {
+    const sa_head_budget& b = budgets[h];
+    if (b.n_sink < 0 || b.n_local < 0 || b.min_blocks < b.n_sink + b.n_local || b.min_blocks < 1)
+      return fail(SA_ERR_INVALID_ARG, "head %d: need min_blocks >= max(1, n_sink + n_local)", h);
+  }
+  const int32_t n_grid = 65536 / step_q16;
+  std::vector<int32_t> order, rank(n_blocks);
+  std::vector<char> forced(n_blocks);
+  for (int32_t h = 0; h < n_heads; ++h) {
+    const sa_head_budget& bud = budgets[h];
+    std::vector<double> acc(n_grid, 0.0);
+    for (int32_t bi = 0; bi < batch; ++bi) {
+      for (int32_t m = 0; m < n_blocks; ++m) {
+        const float* w = mass + (((int64_t)bi * n_heads + h) * n_blocks + m) * n_blocks;
+        const int32_t nc = m + 1;
+        // ranking: the forced blocks, then the others heaviest first, ties to the lowest index
+        order.clear();
+        int32_t n_forced = 0;
+        for (int32_t n = 0; n < nc; ++n) {
+          forced[n] = n < bud.n_sink || n >= nc - bud.n_local;
+          if (forced[n]) {
+            order.push_back(n);
+            ++n_forced;
+          }
+        }
+        for (int32_t n = 0; n < nc; ++n)
+          if (!forced[n]) order.push_back(n);
+        std::stable_sort(order.begin() + n_forced, order.end(),
+                         [&](int32_t a, int32_t b) { return double(w[a]) > double(w[b]); });
+        for (int32_t r = 0; r < nc; ++r) rank[order[r]] = r;
+        double total = 0.0;
+        for (int32_t n = 0; n < nc; ++n) total += double(w[n]);
+        for (int32_t i = 0; i < n_grid; ++i) {
+          const int32_t kk = sa::budget_blocks(nc, bud.min_blocks, uint32_t((i + 1) * step_q16));
+          double kept = 0.0;
+          for (int32_t n = 0; n < nc; ++n)
+            if (rank[n] < kk) kept += double(w[n]);
+          acc[i] += total > 0.0 ? kept / total : 1.0;
+        }
+      }
+    }
+    for (int32_t i = 0; i < n_grid; ++i) recovery[(int64_t)h * n_grid + i] = acc[i] / (double(batch) * n_blocks);
+  }
+  return ok();
+}
+
+sa_status sa_budget_shift(const double* recovery, int32_t n_heads, int32_t step_q16, int64_t total_q16,
+                          uint32_t* ratio_q16) {
+  if (!recovery || !ratio_q16) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (n_heads < 1) return fail(SA_ERR_INVALID_ARG, "n_heads must be >= 1");
+  if (step_q16 < 1 || 65536 % step_q16) return fail(SA_ERR_INVALID_ARG, "step_q16 %d must divide 65536", step_q16);
+  const int64_t per = total_q16 / n_heads;
+  if (per * n_heads != total_q16 || per % step_q16 || per < step_q16 || per > 65536)
+    return fail(SA_ERR_INVALID_ARG, "total_q16 must be n_heads times a whole number of steps in [step, 65536]");
+  const int32_t n_grid = 65536 / step_q16;
+  auto rec = [&](int32_t h, int32_t i) { return recovery[(int64_t)h * n_grid + i]; };
+  std::vector<int32_t> idx(n_heads, int32_t(per / step_q16) - 1);
+  while (true) {
+    int32_t b = -1;
+    for (int32_t h = 0; h < n_heads; ++h)
+      if (idx[h] + 1 < n_grid && (b < 0 || rec(h, idx[h]) < rec(b, idx[b]))) b = h;
+    if (b < 0) break;
+    int32_t a = -1;
+    for (int32_t h = 0; h < n_heads; ++h)
+      if (h != b && idx[h] >= 1 && (a < 0 || rec(h, idx[h] - 1) > rec(a, idx[a] - 1))) a = h;
+    if (a < 0 || !(rec(a, idx[a] - 1) > rec(b, idx[b]))) break;
+    --idx[a];
+    ++idx[b];
+  }
+  for (int32_t h = 0; h < n_heads; ++h) ratio_q16[h] = uint32_t((idx[h] + 1) * step_q16);
   return ok();
 }
 

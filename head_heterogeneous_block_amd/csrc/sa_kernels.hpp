@@ -23,8 +23,8 @@ struct HeadTable {
 // token rows; page_table[(b * heads + h) * max_pages + p] is the physical page
 // (in head h's pool) of logical page p of sequence b.
 struct PageTable {
-  const int32_t* table;  // nullptr: contiguous cache
-  int page_size, max_pages, pages_per_head;
+  const int32_t* table = nullptr;  // nullptr: contiguous cache
+  int page_size = 0, max_pages = 0, pages_per_head = 0;
 };
 
 struct PoolParams {
@@ -145,5 +145,17 @@ struct DecodeCombineParams {
   int out_f32;
 };
 hipError_t launch_decode_combine(const DecodeCombineParams& p, int dtype, int D, int batch, hipStream_t stream);
+
+// ---------------------------------------------------------------- calibration
+struct MassParams {
+  const void* q;  // bf16 [batch][Hq][S][D] (strided)
+  const void* k;  // bf16 [batch][Hkv][S][D] (strided)
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2;
+  float* mass;    // [batch][Hq][NB][NB] fp32
+  int Hq, G, S, NB;
+  float scale_log2;
+};
+// block size 128; D 64 or 128
+hipError_t launch_block_mass(const MassParams& p, int D, int batch, hipStream_t stream);
 
 }  // namespace sa

@@ -490,6 +490,9 @@ hipError_t topk_launch(const TopkParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_pool(const PoolParams& p, int dtype, int D, int batch, hipStream_t stream) {
+  if (p.pages.table && (p.pages.page_size < p.g || p.pages.page_size % p.g || p.pages.max_pages < 1 ||
+                        p.pages.pages_per_head < 1))
+    return hipErrorInvalidValue;
   dim3 grid((p.nb + p.blocks_per_wg - 1) / p.blocks_per_wg, p.heads, batch);
   if (dtype == 0 && D == 128) hipLaunchKernelGGL((pool_kernel<bf16_t, 128>), grid, dim3(256), 0, stream, p);
   else if (dtype == 0 && D == 64) hipLaunchKernelGGL((pool_kernel<bf16_t, 64>), grid, dim3(256), 0, stream, p);

@@ -36,6 +36,7 @@ EXPORTED = [
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_decode_workspace_size", "sa_sparse_attn_decode",
     "sa_pool_keys_decode_paged", "sa_sparse_attn_decode_paged",
+    "sa_block_attention_mass", "sa_budget_recovery", "sa_budget_shift",
 ]
 
 
@@ -97,6 +98,12 @@ _SIG = {
     "sa_sparse_attn_decode_paged": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, ctypes.POINTER(sa_kv_pages), _P,
                                                      _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P,
                                                      ctypes.c_size_t, _P]),
+    "sa_block_attention_mass": (ctypes.c_int32, [_descp, _P, _P, _P, _P]),
+    "sa_budget_recovery": (ctypes.c_int32, [ctypes.POINTER(ctypes.c_float), ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, _budp, ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_double)]),
+    "sa_budget_shift": (ctypes.c_int32, [ctypes.POINTER(ctypes.c_double), ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int64, ctypes.POINTER(ctypes.c_uint32)]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -344,6 +351,31 @@ def sa_sparse_attn_decode_paged(desc: sa_attn_desc, budgets, q, k_pages, v_pages
                                             ctypes.byref(pages), _ptr(o), _ptr(lse), _ptr(block_idx),
                                             _ptr(block_cnt), kmax, 1 if out_f32 else 0, _ptr(workspace),
                                             workspace.numel(), _stream(q)))
+
+
+def sa_block_attention_mass(desc: sa_attn_desc, q: torch.Tensor, k: torch.Tensor, mass: torch.Tensor) -> None:
+    _check(_lib.sa_block_attention_mass(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(mass), _stream(q)))
+
+
+def sa_budget_recovery(mass: np.ndarray, budget: dict, step_q16: int) -> np.ndarray:
+    """Host recovery table ``[H, 65536 // step_q16]`` from a host fp32 mass
+    array ``[b, H, NB, NB]``."""
+    m = np.ascontiguousarray(mass, dtype=np.float32)
+    b, H, nb, _ = m.shape
+    rec = np.zeros((H, 65536 // step_q16), dtype=np.float64)
+    _check(_lib.sa_budget_recovery(m.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), b, H, nb,
+                                   make_budgets(budget), step_q16,
+                                   rec.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    return rec
+
+
+def sa_budget_shift(recovery: np.ndarray, step_q16: int, total_q16: int) -> np.ndarray:
+    """Max-min shifted ratios (uint32 ``[H]``, units 2^-16) from a recovery table."""
+    rec = np.ascontiguousarray(recovery, dtype=np.float64)
+    out = np.zeros(rec.shape[0], dtype=np.uint32)
+    _check(_lib.sa_budget_shift(rec.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), rec.shape[0], step_q16,
+                                int(total_q16), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))))
+    return out
 
 
 # ---------------------------------------------------------------- conveniences

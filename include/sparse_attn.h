@@ -261,6 +261,46 @@ sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* 
                                 int32_t kmax, int32_t out_f32, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- calibration */
+
+/* Offline calibration of per-head budgets: each head gets the budget that keeps
+ * a share of its attention weight, and budget is shifted from heads that need
+ * little to heads that need much with the total fixed, maximising the lowest
+ * head's share ("S-HPLB: Efficient LLM Attention Serving via Sparsity-Aware
+ * Head Parallelism Load Balance", Italian summary §2.A, Chinese summary §2.1). */
+
+/* Attention mass per block pair: mass[b][h][m][n] = sum over the query rows t
+ * of block m of head h of their exact causal softmax probabilities
+ * softmax(scale q_t k^T) on the keys of block n (n <= m), zero for n > m.
+ * Row m sums to the number of query rows in block m.  Prefill descriptor
+ * (q_len == kv_len), bf16, block_size 128.  q, k [dev]; mass [dev] fp32
+ * [batch][n_q_heads][n_blocks][n_blocks], written completely.  Costs two
+ * passes of dense causal Q K^T: meant for calibration inputs, not the path. */
+sa_status sa_block_attention_mass(const sa_attn_desc* desc, const void* q, const void* k, float* mass,
+                                  void* stream);
+
+/* Recovery table (host, synchronous): recovery[h][i] = mean over (sequence b,
+ * query block m) of the share of row mass[b][h][m][0..m] kept by the row's best
+ * selection at ratio r = (i+1) * step_q16: the forced blocks (budgets[h].n_sink
+ * first, n_local last) plus the heaviest others (ties to the lowest index), k
+ * blocks in all by the budget rule with budgets[h].min_blocks.  Kept and total
+ * mass are summed in ascending block order in double.  mass [host] fp32
+ * [batch][n_heads][n_blocks][n_blocks] (from sa_block_attention_mass);
+ * recovery [host] double [n_heads][65536 / step_q16]; step_q16 divides 65536.
+ * The ratio and granularity fields of budgets are not used. */
+sa_status sa_budget_recovery(const float* mass, int32_t batch, int32_t n_heads, int32_t n_blocks,
+                             const sa_head_budget* budgets, int32_t step_q16, double* recovery);
+
+/* Max-min budget shifting (host, synchronous) on a recovery table: every head
+ * starts at total_q16 / n_heads (a whole number of steps); while the head with
+ * the lowest recovery (lowest index on ties) can grow and another head can give
+ * one step and still stay strictly above it (the one that stays highest, lowest
+ * index on ties), one step moves.  For tables that grow with the ratio this
+ * reaches the largest possible lowest recovery.  ratio_q16 [host] [n_heads]:
+ * the shifted ratios, summing to total_q16. */
+sa_status sa_budget_shift(const double* recovery, int32_t n_heads, int32_t step_q16, int64_t total_q16,
+                          uint32_t* ratio_q16);
+
 /* ---------------------------------------------------------------- paged KV */
 
 /* A decode KV cache held in pages of page_size tokens, each KV head with its

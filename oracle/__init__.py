@@ -26,3 +26,12 @@ from .block_sparse import (  # noqa: F401
     lpt_schedule,
     brute_force_makespan,
 )
+from .calibration import (  # noqa: F401
+    block_attention_mass,
+    row_recovery,
+    head_recovery,
+    recovery_table,
+    needed_ratio,
+    maxmin_shift,
+    brute_force_maxmin,
+)

@@ -1,0 +1,138 @@
+"""Pins of the calibration oracle (block attention mass, head recovery, max-min
+budget shifting) and the library's host calibration against it.
+
+Mass: every row of softmax probabilities sums to one, so row m of the block
+mass sums to the query rows of block m; with Q = 0 every visible key of row t
+has probability 1/(t+1), a closed form; and the block sums of
+torch's fp64 softmax agree.  Recovery: a full budget keeps everything, a budget
+of the forced blocks keeps exactly them, and the best selection is the best of
+all block subsets.  Shifting: on tables that grow with the ratio, the lowest
+recovery it reaches is the largest that any allocation of the total reaches.
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+SA = pytest.importorskip("head_heterogeneous_block_amd.sparse_attn", reason="library not built")
+
+
+def _qk(seed, b=1, H=2, Hk=1, S=300, D=16, scale=1.0):
+    r = np.random.default_rng(seed)
+    q = (scale * r.standard_normal((b, H, S, D))).astype(np.float32)
+    k = (scale * r.standard_normal((b, Hk, S, D))).astype(np.float32)
+    return q, k
+
+
+def test_mass_rows_sum_to_row_count():
+    q, k = _qk(1, S=300)
+    W = O.block_attention_mass(q, k, 64)
+    rows = np.array([min(64, 300 - 64 * m) for m in range(5)], dtype=np.float64)
+    np.testing.assert_allclose(W.sum(axis=3), np.broadcast_to(rows, W.shape[:3]), rtol=0, atol=1e-12)
+    assert np.all(np.triu(W[0, 0], 1) == 0)
+
+
+def test_mass_uniform_attention_closed_form():
+    q, k = _qk(2, S=200)
+    q[:] = 0.0
+    W = O.block_attention_mass(q, k, 32)
+    nb = 7
+    for m in range(nb):
+        for n in range(m + 1):
+            want = 0.0
+            for t in range(32 * m, min(200, 32 * m + 32)):
+                seen = max(0, min(t, 32 * n + 31) - 32 * n + 1)
+                want += seen / (t + 1)
+            assert abs(W[0, 0, m, n] - want) < 1e-12
+
+
+def test_mass_matches_torch_softmax_block_sums():
+    q, k = _qk(3, H=4, Hk=2, S=256, D=32)
+    W = O.block_attention_mass(q, k, 64)
+    qt, kt = torch.from_numpy(q).double(), torch.from_numpy(k).double()
+    z = qt @ kt.repeat_interleave(2, dim=1).transpose(-1, -2) / math.sqrt(32)
+    z = z.masked_fill(~torch.tril(torch.ones(256, 256, dtype=torch.bool)), float("-inf"))
+    p = torch.softmax(z, dim=-1).numpy()
+    ref = p.reshape(1, 4, 4, 64, 4, 64).sum(axis=(3, 5))
+    np.testing.assert_allclose(W, ref, rtol=0, atol=1e-12)
+
+
+def test_recovery_full_budget_and_forced_only():
+    q, k = _qk(4, S=320, scale=2.0)
+    W = O.block_attention_mass(q, k, 64)
+    assert O.head_recovery(W[:, 0], 65536, 2, 1, 1) == 1.0
+    got = O.head_recovery(W[:, 0], 1, 2, 1, 1)  # tiny ratio: only the sink and the diagonal
+    want = np.mean([1.0] + [(W[0, 0, m, 0] + W[0, 0, m, m]) / W[0, 0, m, :m + 1].sum() for m in range(1, 5)])
+    assert abs(got - want) < 1e-14
+
+
+def test_row_recovery_is_the_best_subset():
+    r = np.random.default_rng(5)
+    for trial in range(30):
+        n = int(r.integers(3, 9))
+        w = r.random(n) ** 3
+        if trial % 5 == 0:
+            w[r.integers(0, n, 2)] = w[0]  # ties
+        for kk in range(2, n + 1):
+            best = 0.0
+            for sub in itertools.combinations(range(1, n - 1), kk - 2):
+                best = max(best, w[0] + w[n - 1] + sum(w[list(sub)]))
+            assert abs(O.row_recovery(w, kk, 1, 1) * w.sum() - best) < 1e-12
+
+
+def _monotone_tables(seed, H, n_grid):
+    r = np.random.default_rng(seed)
+    steps = r.random((H, n_grid)) * (r.random((H, n_grid)) < 0.7)
+    rec = np.cumsum(steps, axis=1)
+    return rec / rec[:, -1:].clip(min=1e-9) * r.uniform(0.8, 1.0, (H, 1))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_maxmin_shift_reaches_the_brute_force_optimum(seed):
+    H, n_grid, step = 3 + seed % 2, 8, 8192
+    rec = _monotone_tables(seed, H, n_grid)
+    for per_units in (1, 2, 4):
+        total = H * per_units * step
+        got = O.maxmin_shift(rec, total, step)
+        assert sum(got) == total and all(step <= x <= 65536 for x in got)
+        got_min = min(rec[h, got[h] // step - 1] for h in range(H))
+        assert got_min == O.brute_force_maxmin(rec, total, step)
+        assert got_min >= rec[:, per_units - 1].min()  # never below the equal split
+
+
+def test_needed_ratio():
+    rec = np.array([0.2, 0.5, 0.89, 0.9, 0.95])
+    assert O.needed_ratio(rec, 0.9, 4096) == 4 * 4096
+    assert O.needed_ratio(rec, 0.99, 4096) == 5 * 4096
+
+
+def _budget(H, min_blocks=2):
+    return {"min_blocks": [min_blocks] * H, "ratio_q16": [0] * H, "n_sink": [1] * H, "n_local": [1] * H}
+
+
+def test_host_recovery_and_shift_match_oracle_bitwise():
+    q, k = _qk(6, b=2, H=4, Hk=2, S=512, D=32, scale=1.5)
+    W32 = O.block_attention_mass(q, k, 64).astype(np.float32)
+    bud = _budget(4)
+    step = 4096
+    got = SA.sa_budget_recovery(W32, bud, step)
+    want = O.recovery_table(W32.astype(np.float64), bud, step)
+    assert np.array_equal(got, want)
+    for per in (step, 4 * step, 8 * step):
+        r_host = SA.sa_budget_shift(got, step, 4 * per)
+        assert r_host.tolist() == O.maxmin_shift(want, 4 * per, step)
+
+
+def test_host_calibration_rejects_bad_arguments():
+    rec = np.ones((3, 16))
+    with pytest.raises(SA.SaError):
+        SA.sa_budget_shift(rec, 4096, 3 * 4096 + 1)  # not a whole number of steps per head
+    with pytest.raises(SA.SaError):
+        SA.sa_budget_shift(rec, 5000, 3 * 5000)  # step does not divide 2^16
+    with pytest.raises(SA.SaError):
+        SA.sa_budget_recovery(np.ones((1, 2, 3, 3), np.float32), _budget(2, min_blocks=1), 4096)
