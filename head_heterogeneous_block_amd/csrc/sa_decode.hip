@@ -70,7 +70,9 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodePlanPar
 #pragma unroll
       for (int gi = 0; gi < kGM; ++gi) {
         const int b = b0 + r * kPlanThreads + tid;
-        if (b >= cnt[gi] || nv[r][gi] < 0) continue;
+        // out-of-range indices (n >= n_atoms can never be a block of the cache)
+        // are skipped before n * apb could overflow
+        if (b >= cnt[gi] || nv[r][gi] < 0 || nv[r][gi] >= p.n_atoms) continue;
         const int a = nv[r][gi] * apb[gi];
         const int na = min(apb[gi], p.n_atoms - a);
         if (na > 0) atomicOr(&bits[gi * n_words + (a >> 5)], ((na >= 32 ? 0u : (1u << na)) - 1u) << (a & 31));
