@@ -310,3 +310,47 @@ def test_decode_full_size_sampled():
     plan.attend(inp.q, inp.k, inp.v, o2)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
+
+
+# ---------------------------------------------------------------- degenerate budgets
+
+
+def test_prefill_full_budget_is_dense_causal_attention():
+    """A ratio of 1 keeps every causal block: the selection is 0..m for every
+    row and the output is dense causal attention (torch's fp64 SDPA on the CPU,
+    K/V repeated over the GQA group), ragged tail included."""
+    spec = W.LLAMA_32K.with_(seq_len=2048 + 100, n_q_heads=8, n_kv_heads=2)
+    inp = W.make_prefill(spec, 61, device=DEV)
+    inp.budget["ratio_q16"][:] = 65536
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=64, queue=True)
+    nb = spec.n_blocks
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    for m in range(nb):
+        assert np.all(gcnt[:, :, m] == m + 1)
+        assert np.all(gidx[:, :, m, :m + 1] == np.arange(m + 1))
+    q, k, v = (torch.from_numpy(O.to_f64(x)) for x in to_host(inp))
+    G = spec.n_q_heads // spec.n_kv_heads
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k.repeat_interleave(G, 1), v.repeat_interleave(G, 1),
+                                                           is_causal=True).numpy()
+    err = max_abs(o.cpu().numpy(), ref)
+    _say("full budget: max abs err vs dense causal attention", err)
+    assert err <= TOL_BF16
+
+
+def test_prefill_minimal_budget_keeps_sink_and_diagonal():
+    """A budget of two blocks keeps exactly the sink and the diagonal block."""
+    spec = W.LLAMA_32K.with_(seq_len=1536, n_q_heads=4, n_kv_heads=1)
+    inp = W.make_prefill(spec, 62, device=DEV)
+    inp.budget["ratio_q16"][:] = 0
+    inp.budget["min_blocks"][:] = 2
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=16, queue=True)
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert np.all(gcnt[:, :, 0] == 1) and np.all(gidx[:, :, 0, 0] == 0)
+    for m in range(1, spec.n_blocks):
+        assert np.all(gcnt[:, :, m] == 2)
+        assert np.all(gidx[:, :, m, 0] == 0) and np.all(gidx[:, :, m, 1] == m)
+    q, k, v = to_host(inp)
+    ro, rl = O.attention_prefill_gather(q, k, v, gidx, gcnt, spec.block)
+    err = max_abs(o.cpu().numpy(), ro)
+    _say("minimal budget: max abs err", err)
+    assert err <= TOL_BF16
