@@ -54,11 +54,16 @@ def parse():
     return ap.parse_args()
 
 
-def timed(fn, stream, reps):
-    """Median / mean milliseconds of fn() with events on `stream`."""
+def timed(fn, stream, reps, scrub=None):
+    """Median / mean milliseconds of fn() with events on `stream`.  With
+    ``scrub`` (a tensor), it is overwritten before every repetition, outside
+    the timed region, so the caches (L2 and the 256 MB MALL) hold none of the
+    inputs when fn starts."""
     import torch
     ts = []
     for _ in range(reps):
+        if scrub is not None:
+            scrub.fill_(1)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -263,15 +268,18 @@ def main():
 
     reps = max(args.steps, 5)
     res = {}
+    scrub = torch.empty(512 << 18, dtype=torch.float32, device=dev)  # 512 MiB, twice the MALL
     if args.only in ("prefill", "all"):
         res["sel_ms"] = timed(sel, stream, reps)[0]
         att_med, att_mean, _ = timed(att, stream, reps)
         res["att_ms"] = att_med
         res["att_mean_ms"] = att_mean
+        res["att_scrub_ms"] = timed(att, stream, reps, scrub)[0]
     if args.only in ("decode", "all"):
         res["dsel_ms"] = timed(dsel, stream, reps)[0]
         res["datt_ms"] = timed(datt, stream, reps)[0]
         res["dstep_ms"] = timed(lambda: (dsel(), datt()), stream, reps)[0]
+        res["dstep_scrub_ms"] = timed(lambda: (dsel(), datt()), stream, reps, scrub)[0]
         if not args.no_paged:
             # the same decode step over the cache scattered into per-KV-head
             # pools of 128-token pages (the pools are built once, untimed)
@@ -400,10 +408,12 @@ def main():
                    "global_batch": 1, "seq_len": pspec.seq_len, "parallelism": "single GPU",
                    "schedule": f"work queue: {n_bins} workgroups, tiles longest first per (sequence, KV head)"},
         "prefill": {"select_ms": res.get("sel_ms"), "attention_ms": res.get("att_ms"),
+                    "attention_ms_scrubbed": res.get("att_scrub_ms"),
                     "attended_tflops": tflops, "attended_flops": flops,
                     "mfma_frac": roofline["frac"], "schedule_host_ms": lpt_ms},
         "decode": {"select_ms": res.get("dsel_ms"), "attention_ms": res.get("datt_ms"),
-                   "step_ms": res.get("dstep_ms"), "bytes": dbytes, "step_gbps": dgbps,
+                   "step_ms": res.get("dstep_ms"), "step_ms_scrubbed": res.get("dstep_scrub_ms"),
+                   "bytes": dbytes, "step_gbps": dgbps,
                    "hbm_frac": dgbps / (M.PEAK_HBM_BYTES / 1e9) if dgbps else None,
                    "kv_gbps_attention_kernel": kv_gbps},
         "decode_paged": None if "paged_step_ms" not in res else {
