@@ -346,6 +346,13 @@ def main():
         cont.n_bins = n_bins
         ablation["contiguous_bins_ms"] = timed(lambda: cont.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
         ablation["queue_lpt_grouped_ms"] = res["att_ms"]
+        # the queue grouped by query head (heaviest head first) instead of by KV head
+        byhead = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
+                                queue_group="head")
+        byhead.block_idx = plan.block_idx
+        byhead.block_cnt = plan.block_cnt
+        ablation["queue_lpt_by_query_head_ms"] = timed(lambda: byhead.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+        del byhead
         # the same queue in plain longest-first order (no grouping by KV head)
         flat = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True)
         flat.block_idx = plan.block_idx

@@ -395,7 +395,7 @@ class PrefillPlan:
 
     def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
                  kernel_variant: int = 0, bin_order: str = "index", xcd_groups: int = 0, xcd_chunk: int = 64,
-                 queue: bool = False):
+                 queue: bool = False, queue_group: str = "kv"):
         self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_prefill_block_counts(self.desc, self.budgets)
@@ -412,9 +412,21 @@ class PrefillPlan:
         if queue:
             if n_bins < 1:
                 raise ValueError("the work queue needs n_bins >= 1 workgroups")
-            # item = (b * Hq + h) * NB + m, grouped by (b, KV head) = (b * Hq + h) // G
+            # item = (b * Hq + h) * NB + m
             G = q.shape[1] // k.shape[1]
-            group = (np.arange(self.counts.size, dtype=np.int64) // self.nb // G).astype(np.int32)
+            bh = np.arange(self.counts.size, dtype=np.int64) // self.nb
+            if queue_group == "kv":
+                # grouped by (b, KV head) = (b * Hq + h) // G
+                group = (bh // G).astype(np.int32)
+            elif queue_group == "head":
+                # grouped by (b, query head), the heads with the largest total
+                # load first, so the lightest head's short tiles end the queue
+                tot = self.counts.reshape(-1, self.nb).sum(axis=1)
+                rank = np.empty(tot.size, dtype=np.int64)
+                rank[np.argsort(-tot, kind="stable")] = np.arange(tot.size)
+                group = rank[bh].astype(np.int32)
+            else:
+                raise ValueError(f"queue_group {queue_group!r}")
             order = sa_lpt_queue_order(self.counts.reshape(-1), group)
             self.bin_load = None
             self.bin_offsets = None
