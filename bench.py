@@ -225,8 +225,8 @@ def main():
     print(f"[bench] prefill inputs {pspec.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     n_bins = n_cu * args.bins_per_cu
     t0 = time.perf_counter()
-    # work queue: n_bins persistent workgroups take the tiles longest first
-    # inside each (sequence, KV head) group
+    # work queue: n_bins persistent workgroups take the tiles in load tiers,
+    # heaviest tier first, grouped by (sequence, KV head) inside a tier
     plan = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True)
     lpt_ms = (time.perf_counter() - t0) * 1e3
     o = torch.empty_like(pin.q)
@@ -345,7 +345,13 @@ def main():
         cont.items_by_bin = torch.arange(n_t, dtype=torch.int32, device=dev)
         cont.n_bins = n_bins
         ablation["contiguous_bins_ms"] = timed(lambda: cont.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
-        ablation["queue_lpt_grouped_ms"] = res["att_ms"]
+        ablation["queue_lpt_kv_tiers_ms"] = res["att_ms"]
+        grouped = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
+                                 queue_group="kv")
+        grouped.block_idx = plan.block_idx
+        grouped.block_cnt = plan.block_cnt
+        ablation["queue_lpt_grouped_ms"] = timed(lambda: grouped.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+        del grouped
         # the queue grouped by query head (heaviest head first) instead of by KV head
         byhead = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
                                 queue_group="head")
@@ -413,7 +419,7 @@ def main():
                                f"Hkv={pspec.n_kv_heads}, D={pspec.head_dim}, block={pspec.block}) + decode "
                                f"{dspec.name} (batch={dspec.batch}, L={dspec.kv_len})",
                    "global_batch": 1, "seq_len": pspec.seq_len, "parallelism": "single GPU",
-                   "schedule": f"work queue: {n_bins} workgroups, tiles longest first per (sequence, KV head)"},
+                   "schedule": f"work queue: {n_bins} workgroups, tiles in load tiers (quarter octave) heaviest first, grouped by (sequence, KV head) within a tier"},
         "prefill": {"select_ms": res.get("sel_ms"), "attention_ms": res.get("att_ms"),
                     "attention_ms_scrubbed": res.get("att_scrub_ms"),
                     "attended_tflops": tflops, "attended_flops": flops,

@@ -391,11 +391,15 @@ class PrefillPlan:
     (sa_lpt_schedule_grouped): chunks of ``xcd_chunk`` query blocks of one
     (sequence, KV head) onto ``xcd_groups`` cache partitions, then LPT inside.
     ``queue``: instead of fixed bins, the ``n_bins`` workgroups take the tiles
-    longest first from a shared counter (the greedy rule applied online)."""
+    longest first from a shared counter (the greedy rule applied online).
+    ``queue_group`` orders the queue: "kv_tiers" (default) in load tiers of a
+    quarter octave, heaviest first, grouped by (sequence, KV head) inside a
+    tier; "kv" grouped by (sequence, KV head) only; "head" grouped by query
+    head, heaviest head first; "flat" plain longest first."""
 
     def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
                  kernel_variant: int = 0, bin_order: str = "index", xcd_groups: int = 0, xcd_chunk: int = 64,
-                 queue: bool = False, queue_group: str = "kv"):
+                 queue: bool = False, queue_group: str = "kv_tiers"):
         self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_prefill_block_counts(self.desc, self.budgets)
@@ -418,6 +422,16 @@ class PrefillPlan:
             if queue_group == "kv":
                 # grouped by (b, KV head) = (b * Hq + h) // G
                 group = (bh // G).astype(np.int32)
+            elif queue_group == "kv_tiers":
+                # load tiers of a quarter octave, heaviest tier first, grouped by
+                # (b, KV head) inside a tier: the longest tiles still open the
+                # queue (the greedy tail) and tiles in flight share a KV head
+                ld = self.counts.reshape(-1).astype(np.float64)
+                tier = np.floor(np.log2(np.maximum(ld, 1.0)) * 4.0).astype(np.int64)
+                n_kv = int(bh.max() // G) + 1
+                group = ((tier.max() - tier) * n_kv + bh // G).astype(np.int32)
+            elif queue_group == "flat":
+                group = None
             elif queue_group == "head":
                 # grouped by (b, query head), the heads with the largest total
                 # load first, so the lightest head's short tiles end the queue

@@ -123,7 +123,8 @@ def test_prefill_schedules_bitwise_equal():
     # work queue with one worker, some, and more workers than tiles (each
     # queue plan attends twice: the counter is reset by every call)
     for kw in (dict(xcd_groups=8, xcd_chunk=4), dict(bin_order="lpt"), dict(queue=True),
-               dict(queue=True, n_bins=1), dict(queue=True, n_bins=5000)):
+               dict(queue=True, n_bins=1), dict(queue=True, n_bins=5000), dict(queue=True, queue_group="kv"),
+               dict(queue=True, queue_group="flat"), dict(queue=True, queue_group="head")):
         _say("schedule", kw)
         kw = dict(kw)
         nb = kw.pop("n_bins", 64)
