@@ -484,8 +484,8 @@ class DecodePlan:
     """Descriptor, budgets, kmax, index buffers and workspaces for one decode
     shape; ``pool`` builds the pooled-key cache once per KV cache."""
 
-    def __init__(self, q, k, v, budget: dict, out_f32: bool = False):
-        self.desc = make_decode_desc(q, k, v, q)
+    def __init__(self, q, k, v, budget: dict, out_f32: bool = False, desc: Optional[sa_attn_desc] = None):
+        self.desc = desc if desc is not None else make_decode_desc(q, k, v, q)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_decode_block_counts(self.desc, self.budgets)
         self.out_f32 = out_f32
@@ -515,19 +515,10 @@ class PagedDecodePlan(DecodePlan):
     the pooled-key cache built by ``pool``, as for a contiguous cache."""
 
     def __init__(self, q, k_pages, v_pages, table, kv_len: int, budget: dict, out_f32: bool = False):
-        self.desc = make_paged_decode_desc(q, k_pages, v_pages, kv_len)
+        super().__init__(q, k_pages, v_pages, budget, out_f32,
+                         desc=make_paged_decode_desc(q, k_pages, v_pages, kv_len))
         self.pages = make_pages(table, k_pages.shape[2], k_pages.shape[1])
         self.table = table  # keeps the table alive while the plan holds its address
-        self.budgets = make_budgets(budget)
-        self.counts, self.kmax = sa_decode_block_counts(self.desc, self.budgets)
-        self.out_f32 = out_f32
-        dev = q.device
-        self.block_idx = torch.empty((q.shape[0], q.shape[1], self.kmax), dtype=torch.int32, device=dev)
-        self.block_cnt = torch.empty((q.shape[0], q.shape[1]), dtype=torch.int32, device=dev)
-        self.k_pooled = torch.empty(max(sa_decode_pooled_size(self.desc, self.budgets) // 4, 4),
-                                    dtype=torch.float32, device=dev)
-        self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
-        self.attn_ws = _workspace(sa_decode_workspace_size(self.desc, self.budgets, self.kmax), dev)
 
     def pool(self, k_pages) -> None:
         sa_pool_keys_decode_paged(self.desc, self.budgets, k_pages, self.pages, self.k_pooled)
