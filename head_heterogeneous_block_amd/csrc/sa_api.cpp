@@ -368,6 +368,31 @@ sa_status sa_lpt_queue_order(const int64_t* loads, const int32_t* group_of_item,
   return ok();
 }
 
+sa_status sa_lpt_queue_order_tiered(const int64_t* loads, const int32_t* group_of_item, int32_t n_items,
+                                    int32_t tiers_per_octave, int32_t* order) {
+  if (n_items < 0) return fail(SA_ERR_INVALID_ARG, "n_items < 0");
+  if (tiers_per_octave != 1 && tiers_per_octave != 2 && tiers_per_octave != 4)
+    return fail(SA_ERR_INVALID_ARG, "tiers_per_octave %d (1, 2 or 4)", tiers_per_octave);
+  if (n_items > 0 && (!loads || !order)) return fail(SA_ERR_INVALID_ARG, "loads or order is NULL");
+  std::vector<int32_t> tier(n_items);
+  for (int32_t i = 0; i < n_items; ++i) {
+    if (loads[i] < 0 || loads[i] >= (1 << 15)) return fail(SA_ERR_INVALID_ARG, "load %lld at item %d outside [0, 2^15)",
+                                                          (long long)loads[i], i);
+    uint64_t p = 1;
+    const uint64_t x = uint64_t(std::max<int64_t>(loads[i], 1));
+    for (int32_t t = 0; t < tiers_per_octave; ++t) p *= x;  // < 2^60
+    tier[i] = 63 - __builtin_clzll(p);                          // floor(log2(x^t))
+    order[i] = i;
+  }
+  const auto group = [&](int32_t i) { return group_of_item ? group_of_item[i] : 0; };
+  std::stable_sort(order, order + n_items, [&](int32_t a, int32_t b) {
+    if (tier[a] != tier[b]) return tier[a] > tier[b];
+    if (group(a) != group(b)) return group(a) < group(b);
+    return loads[a] > loads[b];
+  });
+  return ok();
+}
+
 sa_status sa_prefill_block_counts(const sa_attn_desc* desc, const sa_head_budget* budgets, int32_t* counts,
                                   int32_t* kmax) {
   sa_status s = check_desc(desc, true);

@@ -31,7 +31,7 @@ MAX_HEADS = 128
 
 EXPORTED = [
     "sa_version", "sa_last_error", "sa_lpt_schedule", "sa_lpt_schedule_grouped", "sa_lpt_order_bins",
-    "sa_lpt_queue_order",
+    "sa_lpt_queue_order", "sa_lpt_queue_order_tiered",
     "sa_prefill_block_counts", "sa_decode_block_counts",
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_decode_workspace_size", "sa_sparse_attn_decode",
@@ -79,6 +79,7 @@ _SIG = {
     "sa_lpt_schedule": (ctypes.c_int32, [_i64p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
     "sa_lpt_order_bins": (ctypes.c_int32, [_i32p, ctypes.c_int32, _i32p]),
     "sa_lpt_queue_order": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, _i32p]),
+    "sa_lpt_queue_order_tiered": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p]),
     "sa_lpt_schedule_grouped": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
     "sa_prefill_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
@@ -255,6 +256,18 @@ def sa_lpt_order_bins(bin_offsets: np.ndarray, items_by_bin: np.ndarray) -> np.n
     return items
 
 
+def sa_lpt_queue_order_tiered(loads: Sequence[int], group_of_item: Optional[Sequence[int]] = None,
+                              tiers_per_octave: int = 4) -> np.ndarray:
+    """Item order for the work queue in load tiers (see the C header)."""
+    ld = np.ascontiguousarray(loads, dtype=np.int64)
+    n = ld.size
+    gp = None if group_of_item is None else np.ascontiguousarray(group_of_item, dtype=np.int32)
+    order = np.zeros(n, dtype=np.int32)
+    _check(_lib.sa_lpt_queue_order_tiered(ld.ctypes.data_as(_i64p), gp.ctypes.data_as(_i32p) if gp is not None
+                                          else None, n, tiers_per_octave, order.ctypes.data_as(_i32p)))
+    return order
+
+
 def sa_lpt_queue_order(loads: Sequence[int], group_of_item: Optional[Sequence[int]] = None) -> np.ndarray:
     """Item order for the work queue: groups ascending, largest load first inside a group."""
     ld = np.ascontiguousarray(loads, dtype=np.int64)
@@ -426,10 +439,7 @@ class PrefillPlan:
                 # load tiers of a quarter octave, heaviest tier first, grouped by
                 # (b, KV head) inside a tier: the longest tiles still open the
                 # queue (the greedy tail) and tiles in flight share a KV head
-                ld = self.counts.reshape(-1).astype(np.float64)
-                tier = np.floor(np.log2(np.maximum(ld, 1.0)) * 4.0).astype(np.int64)
-                n_kv = int(bh.max() // G) + 1
-                group = ((tier.max() - tier) * n_kv + bh // G).astype(np.int32)
+                group = (bh // G).astype(np.int32)
             elif queue_group == "flat":
                 group = None
             elif queue_group == "head":
@@ -441,7 +451,10 @@ class PrefillPlan:
                 group = rank[bh].astype(np.int32)
             else:
                 raise ValueError(f"queue_group {queue_group!r}")
-            order = sa_lpt_queue_order(self.counts.reshape(-1), group)
+            if queue_group == "kv_tiers":
+                order = sa_lpt_queue_order_tiered(self.counts.reshape(-1), group, 4)
+            else:
+                order = sa_lpt_queue_order(self.counts.reshape(-1), group)
             self.bin_load = None
             self.bin_offsets = None
             self.items_by_bin = torch.from_numpy(order).to(dev)

@@ -173,6 +173,20 @@ sa_status sa_lpt_order_bins(const int32_t* bin_offsets, int32_t n_bins, int32_t*
 sa_status sa_lpt_queue_order(const int64_t* loads, const int32_t* group_of_item, int32_t n_items,
                              int32_t* order);
 
+/* The work-queue order in load tiers (host, synchronous): items by tier
+ * t(load) = floor(tiers_per_octave * log2(max(load, 1))) descending, then group
+ * ascending, then load descending, then item index.  The tier is computed
+ * exactly in integers (the bit length of max(load, 1)^tiers_per_octave, minus
+ * one).  The longest items still open the queue, as the greedy rule needs for
+ * its tail, while items of one group run together inside a tier.
+ *   loads[n_items]          [host] int64 in [0, 2^15)
+ *   group_of_item[n_items]  [host] int32, may be NULL (one group)
+ *   tiers_per_octave        1, 2 or 4
+ *   order[n_items]          [host] out: item indices in queue order
+ * Loads outside [0, 2^15) or another tiers_per_octave are SA_ERR_INVALID_ARG. */
+sa_status sa_lpt_queue_order_tiered(const int64_t* loads, const int32_t* group_of_item, int32_t n_items,
+                                    int32_t tiers_per_octave, int32_t* order);
+
 /* Blocks kept per prefill row, from the budget rule alone (no data needed):
  * counts[b][h][m] for m < ceil(q_len/block_size) ([host] out, int32), and the
  * maximum over all rows in *kmax ([host] out, may be NULL).  These are the

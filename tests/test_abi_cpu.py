@@ -326,3 +326,25 @@ def test_paged_pool_builder_scatters_exactly():
     assert torch.equal(back_k, inp.k) and torch.equal(back_v, inp.v)
     last = pk.k_pages[0, int(tab[0, 0, -1])]
     assert torch.count_nonzero(last[L % 128:]) == 0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_lpt_queue_order_tiered(seed):
+    """Tiers floor(t log2 k) exact in integers (bit length of k^t, minus one),
+    heaviest tier first, then group, then load, then index: against a plain
+    sort with the same key."""
+    r = np.random.default_rng(seed)
+    n = 700
+    loads = r.integers(0, 300, n)
+    loads[:5] = [1, 2, 4, 8, 0]  # exact powers of two sit at tier boundaries
+    groups = r.integers(0, 6, n).astype(np.int32)
+    for t in (1, 2, 4):
+        tier = [int(max(int(x), 1) ** t).bit_length() - 1 for x in loads]
+        want = sorted(range(n), key=lambda i: (-tier[i], int(groups[i]), -int(loads[i]), i))
+        assert SA.sa_lpt_queue_order_tiered(loads, groups, t).tolist() == want
+    want = sorted(range(n), key=lambda i: (-(int(max(int(loads[i]), 1) ** 4).bit_length() - 1), -int(loads[i]), i))
+    assert SA.sa_lpt_queue_order_tiered(loads, None, 4).tolist() == want
+    with pytest.raises(SA.SaError):
+        SA.sa_lpt_queue_order_tiered(loads, groups, 3)
+    with pytest.raises(SA.SaError):
+        SA.sa_lpt_queue_order_tiered(np.array([1 << 15]), None, 4)
