@@ -12,7 +12,11 @@ namespace sa {
 namespace prefill {
 
 constexpr int kKS = 64;       // keys per step
-constexpr float kLazy = 8.f;  // log2 headroom before the running max is raised
+// log2 headroom before the running max is raised (P <= 2^kLazy).  A smaller
+// headroom raises the max more often: measured with one key holding most of a
+// row's weight, the output error falls from 0.014 (8) to 0.005 (0) while the
+// 128K layer takes up to 3.7% longer; 8 keeps the benchmark error near 3e-3.
+constexpr float kLazy = 8.f;
 
 // swap bits 2 and 3 of a key index (an involution)
 __device__ __forceinline__ int perm_key(int k) { return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1); }
