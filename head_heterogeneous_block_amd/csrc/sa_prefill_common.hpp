@@ -12,10 +12,11 @@ namespace sa {
 namespace prefill {
 
 constexpr int kKS = 64;       // keys per step
-// log2 headroom before the running max is raised (P <= 2^kLazy).  A smaller
-// headroom raises the max more often: measured with one key holding most of a
-// row's weight, the output error falls from 0.014 (8) to 0.005 (0) while the
-// 128K layer takes up to 3.7% longer; 8 keeps the benchmark error near 3e-3.
+// log2 headroom before the running max is raised (P <= 2^kLazy).  P is
+// rounded to bf16 (relative error up to 2^-8); with a headroom the largest P of
+// a row is not 1 and is rounded too, which shows when one key holds most of a
+// row's weight (output error 0.014 at headroom 8, 0.005 at 0, for up to 3.7%
+// more time on the 128K layer); 8 keeps the benchmark error near 3e-3.
 constexpr float kLazy = 8.f;
 
 // swap bits 2 and 3 of a key index (an involution)

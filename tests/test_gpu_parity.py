@@ -364,10 +364,10 @@ def test_prefill_and_decode_with_wide_logits():
     """Q scaled by 6 spreads each row's logits over tens of units, so the lazily
     raised running maximum moves inside tiles (rescaling O and l) and most
     probabilities underflow.  The normaliser must stay exact (lse within 1e-4:
-    the max-raising logic); the output is held to two bf16 rounding units of
-    its largest terms, 2^-8 max|v| (P is rounded to bf16 for the P V MFMAs, and
-    with one key holding most of a row's weight that rounding no longer
-    averages out), or 1e-2, whichever is larger."""
+    the max-raising logic); the output is held to the bound of rounding P to
+    bf16 for the P V MFMAs, 2^-8 max|v| (8 significant bits: with one key
+    holding most of a row's weight the rounding of its P no longer averages
+    out), or 1e-2, whichever is larger."""
     spec = W.LLAMA_32K.with_(seq_len=2048 + 64, n_q_heads=8, n_kv_heads=2)
     inp = W.make_prefill(spec, 71, device=DEV)
     inp.q = (inp.q.float() * 6.0).to(inp.q.dtype)
