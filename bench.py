@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--prefill-workload", default="llama3.1-8b-prefill-128k")
     ap.add_argument("--decode-workload", default="llama3.1-8b-decode-128k-b16")
     ap.add_argument("--bins-per-cu", type=int, default=2)
+    ap.add_argument("--queues", type=int, default=8,
+                    help="partitions of the prefill work queue (8: one per XCD; 1: one queue)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
@@ -227,7 +229,8 @@ def main():
     t0 = time.perf_counter()
     # work queue: n_bins persistent workgroups take the tiles in load tiers,
     # heaviest tier first, grouped by (sequence, KV head) inside a tier
-    plan = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True)
+    plan = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
+                          queues=args.queues)
     lpt_ms = (time.perf_counter() - t0) * 1e3
     o = torch.empty_like(pin.q)
     sel = lambda: plan.select(pin.q, pin.k)  # noqa: E731
@@ -345,13 +348,21 @@ def main():
         cont.items_by_bin = torch.arange(n_t, dtype=torch.int32, device=dev)
         cont.n_bins = n_bins
         ablation["contiguous_bins_ms"] = timed(lambda: cont.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
-        ablation["queue_lpt_kv_tiers_ms"] = res["att_ms"]
+        ablation["queue_xcd_partitions_ms" if args.queues > 1 else "queue_lpt_kv_tiers_ms"] = res["att_ms"]
         grouped = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
                                  queue_group="kv")
         grouped.block_idx = plan.block_idx
         grouped.block_cnt = plan.block_cnt
         ablation["queue_lpt_grouped_ms"] = timed(lambda: grouped.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
         del grouped
+        # the other of: one queue in load tiers / the same cut into one partition per XCD
+        other = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
+                               queues=1 if args.queues > 1 else 8)
+        other.block_idx = plan.block_idx
+        other.block_cnt = plan.block_cnt
+        ablation["queue_lpt_kv_tiers_ms" if args.queues > 1 else "queue_xcd_partitions_ms"] = timed(
+            lambda: other.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+        del other
         # the queue grouped by query head (heaviest head first) instead of by KV head
         byhead = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
                                 queue_group="head")
@@ -360,7 +371,7 @@ def main():
         ablation["queue_lpt_by_query_head_ms"] = timed(lambda: byhead.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
         del byhead
         # the same queue in plain longest-first order (no grouping by KV head)
-        flat = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True)
+        flat = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True, queues=1)
         flat.block_idx = plan.block_idx
         flat.block_cnt = plan.block_cnt
         flat.items_by_bin = torch.from_numpy(SA.sa_lpt_queue_order(plan.counts.reshape(-1))).to(dev)
@@ -419,7 +430,8 @@ def main():
                                f"Hkv={pspec.n_kv_heads}, D={pspec.head_dim}, block={pspec.block}) + decode "
                                f"{dspec.name} (batch={dspec.batch}, L={dspec.kv_len})",
                    "global_batch": 1, "seq_len": pspec.seq_len, "parallelism": "single GPU",
-                   "schedule": f"work queue: {n_bins} workgroups, tiles in load tiers (quarter octave) heaviest first, grouped by (sequence, KV head) within a tier"},
+                   "schedule": f"work queue: {n_bins} workgroups, tiles in load tiers (quarter octave) heaviest first, grouped by (sequence, KV head) within a tier"
+                   + (f"; cut into {args.queues} partitions (one per XCD) of (load tier, sequence, KV head) runs placed by LPT, workgroup w starting on partition w mod {args.queues} and moving on when it is empty" if args.queues > 1 else "")},
         "prefill": {"select_ms": res.get("sel_ms"), "attention_ms": res.get("att_ms"),
                     "attention_ms_scrubbed": res.get("att_scrub_ms"),
                     "attended_tflops": tflops, "attended_flops": flops,

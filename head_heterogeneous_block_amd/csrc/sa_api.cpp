@@ -212,6 +212,7 @@ DecodeSelectWs decode_select_ws(const sa_attn_desc* d, const sa_head_budget* b, 
 
 constexpr int kChunkAtoms = 40;  // atoms per decode attention wave: about one full round of waves at 128K
 constexpr int kAtomPad = 16;  // tokens an atom may reach past the cache end
+constexpr int kMaxQueues = sa::PrefillParams::kMaxQueues;  // work-queue partitions (one per XCD on MI355X)
 
 struct DecodeAttnWs {
   size_t atoms, n_union, part_o, part_ml, total;
@@ -390,6 +391,57 @@ sa_status sa_lpt_queue_order_tiered(const int64_t* loads, const int32_t* group_o
     if (group(a) != group(b)) return group(a) < group(b);
     return loads[a] > loads[b];
   });
+  return ok();
+}
+
+sa_status sa_lpt_queue_partition(const int64_t* loads, const int32_t* group_of_item, int32_t n_items,
+                                 int32_t n_groups, int32_t n_queues, int32_t tiers_per_octave, int32_t chunk_items,
+                                 int32_t* order, int32_t* queue_offsets) {
+  if (n_items < 0 || n_groups < 1) return fail(SA_ERR_INVALID_ARG, "n_items < 0 or n_groups < 1");
+  if (n_queues < 1 || n_queues > kMaxQueues)
+    return fail(SA_ERR_INVALID_ARG, "n_queues %d outside [1, %d]", n_queues, kMaxQueues);
+  if (chunk_items < 0) return fail(SA_ERR_INVALID_ARG, "chunk_items must be >= 0");
+  if (chunk_items == 0) chunk_items = std::max<int32_t>(n_items, 1);  // no limit
+  if (!queue_offsets || (n_items > 0 && (!loads || !group_of_item || !order)))
+    return fail(SA_ERR_INVALID_ARG, "NULL array");
+  for (int32_t i = 0; i < n_items; ++i)
+    if (group_of_item[i] < 0 || group_of_item[i] >= n_groups)
+      return fail(SA_ERR_INVALID_ARG, "group %d of item %d outside [0, %d)", group_of_item[i], i, n_groups);
+  // the tiered order (validates the loads and tiers_per_octave)
+  std::vector<int32_t> tiered(n_items);
+  sa_status st = sa_lpt_queue_order_tiered(loads, group_of_item, n_items, tiers_per_octave, tiered.data());
+  if (st) return st;
+  const auto tier_of = [&](int32_t i) {
+    uint64_t p = 1;
+    const uint64_t x = uint64_t(std::max<int64_t>(loads[i], 1));
+    for (int32_t t = 0; t < tiers_per_octave; ++t) p *= x;
+    return 63 - __builtin_clzll(p);
+  };
+  // units: runs of the tiered order with one (tier, group), cut every chunk_items items
+  std::vector<int32_t> unit_of_pos(n_items);
+  std::vector<int64_t> uload;
+  for (int32_t pos = 0, run = 0; pos < n_items; ++pos) {
+    const int32_t i = tiered[pos];
+    const bool same = pos > 0 && group_of_item[tiered[pos - 1]] == group_of_item[i] &&
+                      tier_of(tiered[pos - 1]) == tier_of(i);
+    run = same ? run + 1 : 0;
+    if (!same || run % chunk_items == 0) uload.push_back(0);
+    unit_of_pos[pos] = int32_t(uload.size()) - 1;
+    uload.back() += loads[i];
+  }
+  // units onto queues by the greedy rule on their loads
+  const int32_t n_units = int32_t(uload.size());
+  std::vector<int32_t> queue_of_unit(n_units), uoff(n_queues + 1), uitems(n_units);
+  if (n_units > 0 &&
+      (st = sa_lpt_schedule(uload.data(), n_units, n_queues, queue_of_unit.data(), uoff.data(), uitems.data(), nullptr)))
+    return st;
+  // every queue keeps the tiered order of its items
+  std::vector<int32_t> count(n_queues, 0);
+  for (int32_t pos = 0; pos < n_items; ++pos) count[queue_of_unit[unit_of_pos[pos]]] += 1;
+  queue_offsets[0] = 0;
+  for (int32_t q = 0; q < n_queues; ++q) queue_offsets[q + 1] = queue_offsets[q] + count[q];
+  std::vector<int32_t> fill(queue_offsets, queue_offsets + n_queues);
+  for (int32_t pos = 0; pos < n_items; ++pos) order[fill[queue_of_unit[unit_of_pos[pos]]]++] = tiered[pos];
   return ok();
 }
 
@@ -670,10 +722,11 @@ size_t sa_prefill_workspace_size(const sa_attn_desc* desc, int32_t kmax, int32_t
   return 256;  // the work-queue counter
 }
 
-sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
-                                 float* lse, const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
-                                 const int32_t* bin_offsets, const int32_t* items_by_bin, int32_t n_bins,
-                                 int32_t out_f32, void* workspace, size_t workspace_bytes, void* stream) {
+static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
+                              float* lse, const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
+                              const int32_t* bin_offsets, const int32_t* items_by_bin, int32_t n_bins,
+                              const int32_t* queue_offsets, int32_t n_queues, int32_t out_f32, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   sa_status s = check_desc(desc, true);
   if (s) return s;
   if (!q || !k || !v || !o || !block_idx || !block_cnt) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
@@ -683,13 +736,19 @@ sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const 
   if (bin_offsets && !items_by_bin) return fail(SA_ERR_INVALID_ARG, "bin_offsets without items_by_bin");
   if (items_by_bin && n_bins < 1) return fail(SA_ERR_INVALID_ARG, "n_bins must be >= 1");
   const bool queue = items_by_bin && !bin_offsets;
-  if (queue && (!workspace || workspace_bytes < 4 || (reinterpret_cast<uintptr_t>(workspace) & 3)))
-    return fail(SA_ERR_INVALID_ARG, "the work queue needs a 4-byte aligned workspace of >= 4 bytes");
+  if (queue && (!workspace || workspace_bytes < size_t(4) * n_queues || (reinterpret_cast<uintptr_t>(workspace) & 3)))
+    return fail(SA_ERR_INVALID_ARG, "the work queue needs a 4-byte aligned workspace of >= %d bytes", 4 * n_queues);
   if (desc->batch >= 32768 || desc->n_kv_heads >= 65536)
     return fail(SA_ERR_UNSUPPORTED, "batch must be < 32768 and n_kv_heads < 65536");
   const int64_t nb = cdiv(desc->q_len, desc->block_size);
   const int64_t n_tiles = int64_t(desc->batch) * desc->n_q_heads * nb;
   if (n_tiles > (1ll << 30)) return fail(SA_ERR_UNSUPPORTED, "too many tiles");
+  if (queue_offsets) {
+    if (queue_offsets[0] != 0 || queue_offsets[n_queues] != n_tiles)
+      return fail(SA_ERR_INVALID_ARG, "queue_offsets must run from 0 to the tile count %lld", (long long)n_tiles);
+    for (int32_t i = 0; i < n_queues; ++i)
+      if (queue_offsets[i + 1] < queue_offsets[i]) return fail(SA_ERR_INVALID_ARG, "queue_offsets must not decrease");
+  }
   {
     const int64_t es = elem_size(desc->dtype);
     if (int64_t(desc->kv_len + 256) * desc->k_stride[2] * es >= (1ll << 31) ||
@@ -728,10 +787,32 @@ sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const 
   p.scale_log2 = scale_of(desc) * 1.4426950408889634f;
   p.out_f32 = out_f32 ? 1 : 0;
   p.queue = queue ? static_cast<int*>(workspace) : nullptr;
+  p.n_queues = n_queues;
+  for (int32_t i = 0; i <= n_queues; ++i) p.qoff[i] = queue_offsets ? queue_offsets[i] : (i ? int(n_tiles) : 0);
   const int grid = items_by_bin ? n_bins : int(n_tiles);
   hipError_t e = sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, grid, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
   return ok();
+}
+
+sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
+                                 const int32_t* bin_offsets, const int32_t* items_by_bin, int32_t n_bins,
+                                 int32_t out_f32, void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, bin_offsets, items_by_bin, n_bins, nullptr,
+                      1, out_f32, workspace, workspace_bytes, stream);
+}
+
+sa_status sa_sparse_attn_prefill_queues(const sa_attn_desc* desc, const void* q, const void* k, const void* v,
+                                        void* o, float* lse, const int32_t* block_idx, const int32_t* block_cnt,
+                                        int32_t kmax, const int32_t* queue_offsets, int32_t n_queues,
+                                        const int32_t* order, int32_t n_workgroups, int32_t out_f32, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  if (n_queues < 1 || n_queues > kMaxQueues)
+    return fail(SA_ERR_INVALID_ARG, "n_queues %d outside [1, %d]", n_queues, kMaxQueues);
+  if (!queue_offsets || !order) return fail(SA_ERR_INVALID_ARG, "queue_offsets or order is NULL");
+  return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, nullptr, order, n_workgroups, queue_offsets,
+                      n_queues, out_f32, workspace, workspace_bytes, stream);
 }
 
 size_t sa_decode_workspace_size(const sa_attn_desc* desc, const sa_head_budget* budgets, int32_t kmax) {

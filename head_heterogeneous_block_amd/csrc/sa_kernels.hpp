@@ -97,7 +97,14 @@ struct PrefillParams {
   int Hq, G, S, NB, n_tiles;
   float scale_log2;
   int out_f32;
-  int* queue;  // work-queue counter (nullable): items_by_bin is then one global order
+  int* queue;  // work-queue counters (nullable): items_by_bin is then one global order
+  // Work-queue partitions: positions [qoff[i], qoff[i+1]) of items_by_bin form
+  // queue i, counted by queue[i]; workgroup w starts on queue w % n_queues and
+  // moves to the next queue when its own is empty.  One queue: n_queues = 1,
+  // qoff = {0, n_tiles}.
+  static constexpr int kMaxQueues = 16;
+  int n_queues = 1;
+  int qoff[kMaxQueues + 1] = {};
 };
 // workgroup of B/32 waves, 32 queries each; grid = persistent bins, queue
 // workers or tiles

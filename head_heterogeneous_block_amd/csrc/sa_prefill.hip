@@ -63,20 +63,48 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int col = lane & 31;   // MFMA column (query) / A-row (key, d) index
   const int half = lane >> 5;  // MFMA k-half
 
-  // Work queue (p.queue set): the workgroups take the items of one global
-  // list in order, each claiming its next item from the counter when it starts
-  // the current one, so faster compute units simply take more items.  Wave 0
-  // makes the claims and hands each to the other waves through LDS.
+  // Work queue (p.queue set): the workgroups take the items of a global list
+  // in order, each claiming its next item from a counter when it starts the
+  // current one, so faster compute units simply take more items.  The list may
+  // be cut into partitions, one counter each (one per XCD, so that the
+  // workgroups of an XCD share its L2): a workgroup starts on partition
+  // blockIdx.x % n_queues and, once that is empty, moves on to the following
+  // ones in turn; after trying every partition it is done.  Wave 0 makes the
+  // claims and hands each to the other waves through LDS; its partition and
+  // the partitions left to try sit in LDS (q_state), out of the registers of
+  // the main loop.
   __shared__ int q_slot;
-  int q_pend = 0;  // wave 0, lane 0: the claim in flight
+  __shared__ int q_state[2];  // wave 0: current partition, partitions left
+  int q_pend = 0;             // wave 0, lane 0: the claim in flight
   auto claim = [&]() {
-    if (wave == 0 && lane == 0) q_pend = atomicAdd(COLD(queue), 1);
+    if (wave == 0 && lane == 0 && q_state[1] > 0) q_pend = atomicAdd(COLD(queue) + q_state[0], 1);
   };
+  // position in items_by_bin of the claim in flight (n_tiles: none left)
   auto take_claim = [&]() -> int {
     __syncthreads();  // every wave has read the previous claim
     if (wave == 0) {
-      const int v = __builtin_amdgcn_readfirstlane(q_pend);
-      if (lane == 0) q_slot = v;
+      const int n_tiles = COLD(n_tiles), nq = COLD(n_queues);
+      int qc = __builtin_amdgcn_readfirstlane(q_state[0]);
+      int left = __builtin_amdgcn_readfirstlane(q_state[1]);
+      int v = __builtin_amdgcn_readfirstlane(q_pend);
+      int pos = n_tiles;
+      while (left > 0) {  // at most n_queues rounds per workgroup in all
+        const int beg = min(max(kernel_arg<int>(offsetof(PrefillParams, qoff) + 4 * qc), 0), n_tiles);
+        const int end = min(max(kernel_arg<int>(offsetof(PrefillParams, qoff) + 4 * qc + 4), beg), n_tiles);
+        if (v < end - beg) {
+          pos = beg + v;
+          break;
+        }
+        if (--left == 0) break;
+        qc = qc + 1 == nq ? 0 : qc + 1;
+        if (lane == 0) q_pend = atomicAdd(COLD(queue) + qc, 1);
+        v = __builtin_amdgcn_readfirstlane(q_pend);
+      }
+      if (lane == 0) {
+        q_slot = pos;
+        q_state[0] = qc;
+        q_state[1] = left;
+      }
     }
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(q_slot);
@@ -85,6 +113,10 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
   int it_beg, it_end;
   if (qmode) {
+    if (wave == 0 && lane == 0) {
+      q_state[0] = blockIdx.x % p.n_queues;
+      q_state[1] = p.n_queues;
+    }
     claim();
     it_beg = take_claim();
     claim();
@@ -536,8 +568,8 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
 }
 
-__global__ void queue_reset_kernel(int* counter) {
-  if (threadIdx.x == 0) *counter = 0;
+__global__ void queue_reset_kernel(int* counters, int n) {
+  if ((int)threadIdx.x < n) counters[threadIdx.x] = 0;
 }
 
 template <typename T, int D, int B>
@@ -551,7 +583,8 @@ hipError_t launch_t(const PrefillParams& p, int grid, hipStream_t stream) {
 hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int grid, hipStream_t stream) {
   if (p.queue) {
     // a kernel, not a memset, so that the call can be captured in a graph
-    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, stream, p.queue);
+    if (p.n_queues < 1 || p.n_queues > PrefillParams::kMaxQueues) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(queue_reset_kernel, dim3(1), dim3(64), 0, stream, p.queue, p.n_queues);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

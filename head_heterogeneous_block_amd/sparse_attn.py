@@ -31,10 +31,11 @@ MAX_HEADS = 128
 
 EXPORTED = [
     "sa_version", "sa_last_error", "sa_lpt_schedule", "sa_lpt_schedule_grouped", "sa_lpt_order_bins",
-    "sa_lpt_queue_order", "sa_lpt_queue_order_tiered",
+    "sa_lpt_queue_order", "sa_lpt_queue_order_tiered", "sa_lpt_queue_partition",
     "sa_prefill_block_counts", "sa_decode_block_counts",
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
-    "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_decode_workspace_size", "sa_sparse_attn_decode",
+    "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_sparse_attn_prefill_queues",
+    "sa_decode_workspace_size", "sa_sparse_attn_decode",
     "sa_pool_keys_decode_paged", "sa_sparse_attn_decode_paged",
     "sa_block_attention_mass", "sa_budget_recovery", "sa_budget_shift",
 ]
@@ -80,6 +81,8 @@ _SIG = {
     "sa_lpt_order_bins": (ctypes.c_int32, [_i32p, ctypes.c_int32, _i32p]),
     "sa_lpt_queue_order": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, _i32p]),
     "sa_lpt_queue_order_tiered": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, ctypes.c_int32, _i32p]),
+    "sa_lpt_queue_partition": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_int32, _i32p, _i32p]),
     "sa_lpt_schedule_grouped": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                  ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
     "sa_prefill_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
@@ -92,6 +95,9 @@ _SIG = {
     "sa_prefill_workspace_size": (ctypes.c_size_t, [_descp, ctypes.c_int32, ctypes.c_int32]),
     "sa_sparse_attn_prefill": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
                                                 ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+    "sa_sparse_attn_prefill_queues": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _i32p,
+                                                       ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P,
+                                                       ctypes.c_size_t, _P]),
     "sa_decode_workspace_size": (ctypes.c_size_t, [_descp, _budp, ctypes.c_int32]),
     "sa_sparse_attn_decode": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                ctypes.c_int32, _P, ctypes.c_size_t, _P]),
@@ -268,6 +274,23 @@ def sa_lpt_queue_order_tiered(loads: Sequence[int], group_of_item: Optional[Sequ
     return order
 
 
+def sa_lpt_queue_partition(loads: Sequence[int], group_of_item: Sequence[int], n_groups: int, n_queues: int,
+                           tiers_per_octave: int = 4, chunk_items: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Work queue cut into ``n_queues`` partitions of (tier, group) units of at
+    most ``chunk_items`` items, 0 = no limit (see the C header): returns
+    (order, queue_offsets)."""
+    ld = np.ascontiguousarray(loads, dtype=np.int64)
+    gp = np.ascontiguousarray(group_of_item, dtype=np.int32)
+    if gp.size != ld.size:
+        raise ValueError("group_of_item must have one entry per item")
+    order = np.zeros(ld.size, dtype=np.int32)
+    off = np.zeros(max(n_queues, 0) + 1, dtype=np.int32)
+    _check(_lib.sa_lpt_queue_partition(ld.ctypes.data_as(_i64p), gp.ctypes.data_as(_i32p), ld.size, n_groups,
+                                       n_queues, tiers_per_octave, chunk_items, order.ctypes.data_as(_i32p),
+                                       off.ctypes.data_as(_i32p)))
+    return order, off
+
+
 def sa_lpt_queue_order(loads: Sequence[int], group_of_item: Optional[Sequence[int]] = None) -> np.ndarray:
     """Item order for the work queue: groups ascending, largest load first inside a group."""
     ld = np.ascontiguousarray(loads, dtype=np.int64)
@@ -344,6 +367,17 @@ def sa_sparse_attn_prefill(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block
                                        0 if ws is None else ws.numel(), _stream(q)))
 
 
+def sa_sparse_attn_prefill_queues(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
+                                  queue_offsets: np.ndarray, order, n_workgroups: int, out_f32: bool = False,
+                                  workspace: Optional[torch.Tensor] = None) -> None:
+    off = np.ascontiguousarray(queue_offsets, dtype=np.int32)
+    ws = workspace
+    _check(_lib.sa_sparse_attn_prefill_queues(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                              _ptr(block_idx), _ptr(block_cnt), kmax, off.ctypes.data_as(_i32p),
+                                              off.size - 1, _ptr(order), n_workgroups, 1 if out_f32 else 0,
+                                              _ptr(ws), 0 if ws is None else ws.numel(), _stream(q)))
+
+
 def sa_sparse_attn_decode(desc: sa_attn_desc, budgets, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
                           workspace: torch.Tensor, out_f32: bool = False) -> None:
     _check(_lib.sa_sparse_attn_decode(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -408,11 +442,15 @@ class PrefillPlan:
     ``queue_group`` orders the queue: "kv_tiers" (default) in load tiers of a
     quarter octave, heaviest first, grouped by (sequence, KV head) inside a
     tier; "kv" grouped by (sequence, KV head) only; "head" grouped by query
-    head, heaviest head first; "flat" plain longest first."""
+    head, heaviest head first; "flat" plain longest first.  ``queues`` > 1
+    (default 8, one per XCD of MI355X) cuts the "kv_tiers" queue into that many
+    partitions (sa_lpt_queue_partition): runs of one (load tier, sequence, KV
+    head), of at most ``queue_chunk`` tiles (0: no limit), placed by LPT, each
+    partition in the tiered order; other ``queue_group`` orders use one queue."""
 
     def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
                  kernel_variant: int = 0, bin_order: str = "index", xcd_groups: int = 0, xcd_chunk: int = 64,
-                 queue: bool = False, queue_group: str = "kv_tiers"):
+                 queue: bool = False, queue_group: str = "kv_tiers", queues: int = 8, queue_chunk: int = 0):
         self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_prefill_block_counts(self.desc, self.budgets)
@@ -426,6 +464,7 @@ class PrefillPlan:
         self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
         self.attn_ws = _workspace(sa_prefill_workspace_size(self.desc, self.kmax, n_bins), dev)
         self.queue = queue
+        self.queue_offsets = None
         if queue:
             if n_bins < 1:
                 raise ValueError("the work queue needs n_bins >= 1 workgroups")
@@ -451,7 +490,11 @@ class PrefillPlan:
                 group = rank[bh].astype(np.int32)
             else:
                 raise ValueError(f"queue_group {queue_group!r}")
-            if queue_group == "kv_tiers":
+            if queues > 1 and queue_group == "kv_tiers":
+                n_groups = q.shape[0] * k.shape[1]
+                order, self.queue_offsets = sa_lpt_queue_partition(self.counts.reshape(-1), group, n_groups, queues,
+                                                                   4, queue_chunk)
+            elif queue_group == "kv_tiers":
                 order = sa_lpt_queue_order_tiered(self.counts.reshape(-1), group, 4)
             else:
                 order = sa_lpt_queue_order(self.counts.reshape(-1), group)
@@ -489,6 +532,11 @@ class PrefillPlan:
                          self.select_ws)
 
     def attend(self, q, k, v, o, lse=None) -> None:
+        if self.queue and self.queue_offsets is not None:
+            sa_sparse_attn_prefill_queues(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
+                                          self.queue_offsets, self.items_by_bin, self.n_bins, self.out_f32,
+                                          self.attn_ws)
+            return
         sa_sparse_attn_prefill(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
                                self.bin_offsets, self.items_by_bin, self.n_bins, self.out_f32, self.attn_ws)
 

@@ -187,6 +187,32 @@ sa_status sa_lpt_queue_order(const int64_t* loads, const int32_t* group_of_item,
 sa_status sa_lpt_queue_order_tiered(const int64_t* loads, const int32_t* group_of_item, int32_t n_items,
                                     int32_t tiers_per_octave, int32_t* order);
 
+/* The work queue cut into partitions, one per cache domain (host,
+ * synchronous).  MI355X has 8 XCDs, each with its own L2, and workgroup w of a
+ * launch runs on XCD w mod 8; with one partition per XCD, the workgroups of an
+ * XCD take the tiles placed on it, so the key and value blocks they gather are
+ * shared through that XCD's L2.  The tiered order of sa_lpt_queue_order_tiered
+ * is cut into units: runs of items of one (load tier, group), at most
+ * chunk_items long (0: no limit).  Whole groups would keep the longest tiles of
+ * a heavy group on one XCD, where they cannot all start at once; units of one
+ * tier spread them over the XCDs while the workgroups of an XCD still work on
+ * one group at a time.  The units go onto the partitions by the greedy longest-processing-time
+ * rule of the S-HPLB pages (§2.B, §2.2) on their loads (least loaded partition
+ * first, lower index on ties); inside a partition the items keep the tiered
+ * order.  A workgroup whose partition is empty moves to the next ones in turn
+ * (sa_sparse_attn_prefill_queues), so the tail is balanced across the chip.
+ *   loads[n_items]               [host] int64 in [0, 2^15)
+ *   group_of_item[n_items]       [host] int32 in [0, n_groups)
+ *   n_queues                     1 .. 16
+ *   tiers_per_octave             1, 2 or 4
+ *   chunk_items                  items per unit at most, 0 = no limit
+ *   order[n_items]               [host] out: items, partition after partition
+ *   queue_offsets[n_queues + 1]  [host] out: partition i is order[off[i] .. off[i+1])
+ * Out-of-range groups, loads or sizes are SA_ERR_INVALID_ARG. */
+sa_status sa_lpt_queue_partition(const int64_t* loads, const int32_t* group_of_item, int32_t n_items,
+                                 int32_t n_groups, int32_t n_queues, int32_t tiers_per_octave,
+                                 int32_t chunk_items, int32_t* order, int32_t* queue_offsets);
+
 /* Blocks kept per prefill row, from the budget rule alone (no data needed):
  * counts[b][h][m] for m < ceil(q_len/block_size) ([host] out, int32), and the
  * maximum over all rows in *kmax ([host] out, may be NULL).  These are the
@@ -259,6 +285,25 @@ sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const 
                                  const int32_t* bin_offsets, const int32_t* items_by_bin,
                                  int32_t n_bins, int32_t out_f32, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/* sa_sparse_attn_prefill on a work queue cut into n_queues partitions (from
+ * sa_lpt_queue_partition): n_workgroups persistent workgroups, workgroup w
+ * starting on partition w mod n_queues and moving on to the following
+ * partitions once its own is empty; every workgroup has tried every partition
+ * before it ends.  n_queues = 1 is the single queue of sa_sparse_attn_prefill.
+ *   queue_offsets[n_queues + 1]  [host] 0 = off[0] <= ... <= off[n_queues] = tiles
+ *   order[tiles]                 [dev] every tile exactly once
+ *   workspace                    [dev] >= 4 * n_queues bytes (the counters), reset
+ *                                by the call on the stream; calls sharing it must
+ *                                not overlap
+ * Bad offsets, n_queues outside [1, 16] or n_workgroups < 1 are
+ * SA_ERR_INVALID_ARG; otherwise as sa_sparse_attn_prefill. */
+sa_status sa_sparse_attn_prefill_queues(const sa_attn_desc* desc, const void* q, const void* k,
+                                        const void* v, void* o, float* lse, const int32_t* block_idx,
+                                        const int32_t* block_cnt, int32_t kmax,
+                                        const int32_t* queue_offsets, int32_t n_queues,
+                                        const int32_t* order, int32_t n_workgroups, int32_t out_f32,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 size_t sa_decode_workspace_size(const sa_attn_desc* desc, const sa_head_budget* budgets,
                                 int32_t kmax);

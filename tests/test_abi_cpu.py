@@ -348,3 +348,72 @@ def test_lpt_queue_order_tiered(seed):
         SA.sa_lpt_queue_order_tiered(loads, groups, 3)
     with pytest.raises(SA.SaError):
         SA.sa_lpt_queue_order_tiered(np.array([1 << 15]), None, 4)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_lpt_queue_partition(seed):
+    """Partitioned queue: the tiered order (tier, group, load, index) cut into
+    runs of one (tier, group) of at most chunk items, the runs placed by the
+    oracle's greedy LPT on their loads, each partition keeping the tiered order,
+    partitions concatenated with their offsets."""
+    r = np.random.default_rng(200 + seed)
+    n_groups = int(r.integers(1, 20))
+    n_queues = int(r.integers(1, 17))
+    chunk = [1, 3, 64, 0][seed % 4]
+    n = int(r.integers(0, 900))
+    loads = r.integers(0, 300, n)
+    groups = r.integers(0, n_groups, n).astype(np.int32)
+    order, off = SA.sa_lpt_queue_partition(loads, groups, n_groups, n_queues, 4, chunk)
+    chunk = chunk or n + 1  # 0: no limit
+    tier = [int(max(int(x), 1) ** 4).bit_length() - 1 for x in loads]
+    seq = sorted(range(n), key=lambda i: (-tier[i], int(groups[i]), -int(loads[i]), i))
+    units, unit_load = [], []
+    for p, i in enumerate(seq):
+        prev = seq[p - 1] if p else None
+        if prev is None or (tier[prev], groups[prev]) != (tier[i], groups[i]) or len(units[-1]) == chunk:
+            units.append([])
+            unit_load.append(0)
+        units[-1].append(i)
+        unit_load[-1] += int(loads[i])
+    q_of_u, _, _, _ = O.lpt_schedule(unit_load, n_queues) if units else ([], None, None, None)
+    rank = {i: p for p, i in enumerate(seq)}
+    want, want_off = [], [0]
+    for qq in range(n_queues):
+        want += sorted((i for u, items in enumerate(units) if q_of_u[u] == qq for i in items), key=rank.get)
+        want_off.append(len(want))
+    assert order.tolist() == want and off.tolist() == want_off
+    with pytest.raises(SA.SaError):
+        SA.sa_lpt_queue_partition(loads, groups, n_groups, 17)
+    with pytest.raises(SA.SaError):
+        SA.sa_lpt_queue_partition(loads, groups, n_groups, n_queues, 4, -1)
+    if n:
+        bad = groups.copy()
+        bad[0] = n_groups
+        with pytest.raises(SA.SaError):
+            SA.sa_lpt_queue_partition(loads, bad, n_groups, n_queues)
+
+
+def test_prefill_queues_validation():
+    """The partitioned prefill queue rejects bad partitions before any launch;
+    valid ones reach the device check."""
+    import torch
+    d = _desc()
+    fake = ctypes.c_void_p(1 << 20)
+    lib = SA._lib
+    counts, _ = SA.sa_prefill_block_counts(d, _bud())
+    tiles = counts.size
+
+    def call(off, nq=None, nwg=8, ws=256):
+        a = np.ascontiguousarray(off, dtype=np.int32)
+        return lib.sa_sparse_attn_prefill_queues(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 16,
+                                                 a.ctypes.data_as(SA._i32p), a.size - 1 if nq is None else nq,
+                                                 fake, nwg, 0, fake, ws, None)
+
+    assert call([0, tiles // 2, tiles + 1]) == SA.SA_ERR_INVALID_ARG  # does not end at the tile count
+    assert call([1, tiles]) == SA.SA_ERR_INVALID_ARG                  # does not start at 0
+    assert call([0, tiles // 2 + 1, tiles // 2, tiles]) == SA.SA_ERR_INVALID_ARG  # decreasing
+    assert call([0] * 18 + [tiles]) == SA.SA_ERR_INVALID_ARG          # 18 partitions
+    assert call([0, tiles], nwg=0) == SA.SA_ERR_INVALID_ARG
+    assert call([0, 3, tiles], ws=4) == SA.SA_ERR_INVALID_ARG         # 2 counters need 8 bytes
+    if not torch.cuda.is_available():
+        assert call([0, 3, tiles]) in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)

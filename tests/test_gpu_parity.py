@@ -77,13 +77,15 @@ PREFILL_SHAPES = [
 
 
 @pytest.mark.parametrize("name,over", PREFILL_SHAPES, ids=[s[0] for s in PREFILL_SHAPES])
-@pytest.mark.parametrize("sched", ["natural", "bins37", "queue23"])
+@pytest.mark.parametrize("sched", ["natural", "bins37", "queue23", "queue23x1"])
 def test_prefill_bf16_all_rows(name, over, sched):
     spec = W.LLAMA_32K.with_(**over)
     inp = W.make_prefill(spec, 77, device=DEV)
     _say("case:", name, "schedule", sched)
-    n_bins = {"natural": 0, "bins37": 37, "queue23": 23}[sched]
-    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins, queue=sched.startswith("queue"))
+    n_bins = {"natural": 0, "bins37": 37, "queue23": 23, "queue23x1": 23}[sched]
+    # queue23: the queue cut into 8 partitions (the default); queue23x1: one queue
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins, queue=sched.startswith("queue"),
+                                         queues=1 if sched.endswith("x1") else 8)
     q, k, v = to_host(inp)
     oidx, ocnt, scores = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, return_scores=True)
     gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
@@ -121,10 +123,15 @@ def test_prefill_schedules_bitwise_equal():
         outs.append((o, lse))
     # two-level (cache-partition) placement, assignment-order bins, and the
     # work queue with one worker, some, and more workers than tiles (each
-    # queue plan attends twice: the counter is reset by every call)
+    # queue plan attends twice: the counters are reset by every call); the
+    # queue cut into partitions (2 KV groups here, so most partitions are
+    # empty), one worker walking all 16 of them, more workers than tiles
     for kw in (dict(xcd_groups=8, xcd_chunk=4), dict(bin_order="lpt"), dict(queue=True),
                dict(queue=True, n_bins=1), dict(queue=True, n_bins=5000), dict(queue=True, queue_group="kv"),
-               dict(queue=True, queue_group="flat"), dict(queue=True, queue_group="head")):
+               dict(queue=True, queue_group="flat"), dict(queue=True, queue_group="head"),
+               dict(queue=True, queues=1), dict(queue=True, queues=1, n_bins=1), dict(queue=True, queue_chunk=3),
+               dict(queue=True, queues=3, n_bins=5), dict(queue=True, queues=16, n_bins=1),
+               dict(queue=True, queues=16, n_bins=5000), dict(queue=True, queues=2, n_bins=2)):
         _say("schedule", kw)
         kw = dict(kw)
         nb = kw.pop("n_bins", 64)
@@ -148,7 +155,7 @@ def test_prefill_full_size_sampled(spec):
     _say("case: full-size workload", spec.name)
     inp = W.make_prefill(spec, W.seed_of(spec), device=DEV)
     n_bins = 512
-    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins)
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins, queue=True)  # the benchmark's launch
     gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
     np.testing.assert_array_equal(gcnt, plan.counts)
     G = spec.group
