@@ -34,4 +34,7 @@ from .calibration import (  # noqa: F401
     needed_ratio,
     maxmin_shift,
     brute_force_maxmin,
+    output_deviation,
+    deviation_table,
+    needed_ratio_deviation,
 )

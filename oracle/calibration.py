@@ -13,7 +13,12 @@ shifting) and Chinese summary §2.1 (relative sparsity is stable per head; all
 heads start with equal budgets and budget moves iteratively from high-sparsity
 heads to low-sparsity heads with the total unchanged).
 
-Readings where the pages are silent (kept with the design notes as R32-R35):
+The output-aware variant follows "Fluxion" (Italian summary, Intuizioni Chiave 1
+and Componenti di Sistema): a budget judged by how far the head's attention
+output moves from dense attention, not by the attention weight it keeps (the
+sink blocks hold much weight and little value norm).
+
+Readings where the pages are silent (kept with the design notes as R32-R35, R37):
   R32  the "attention weight" of a key block for a query block is the sum, over
        the query rows of the block, of their exact causal softmax probabilities
        on the block's keys;
@@ -29,9 +34,19 @@ Readings where the pages are silent (kept with the design notes as R32-R35):
        lowest recovery (lowest index on ties) receives one step from the head
        whose recovery stays highest after giving it (lowest index on ties),
        while that donor would still stay strictly above the receiver; heads
-       stay within [step, 2^16].
+       stay within [step, 2^16];
+  R37  the output deviation of head h at a budget is the relative Frobenius
+       distance sqrt(sum (o_sparse - o_dense)^2) / sqrt(sum o_dense^2) over all
+       sequences, query rows and channels of that head, o_dense being causal
+       attention over every key; the head's relative contribution (its share of
+       the layer output after the output projection) needs the projection
+       weights and is left out.
 
-Parity status: block_attention_mass is pinned by its row-sum identity, the
+Parity status: output_deviation is pinned by the split of dense attention
+into the selected and the dropped keys (o_dense - o_sparse = w_out * (o_out -
+o_sparse), w_out the dropped keys' softmax weight, from two separate
+softmaxes), by zero at the full budget and for constant values, and by a
+hand-computed two-key case; block_attention_mass is pinned by its row-sum identity, the
 uniform-attention closed form and the full-attention softmax of
 ``torch.nn.functional.scaled_dot_product_attention``; head_recovery by its
 full-budget and forced-only values and by brute force over block subsets;
@@ -45,7 +60,7 @@ from typing import Mapping, Sequence
 
 import numpy as np
 
-from .block_sparse import budget_blocks, select_row, to_f64
+from .block_sparse import attention_prefill_gather, budget_blocks, select_blocks_prefill, select_row, to_f64
 
 
 def block_attention_mass(q, k, block: int, scale: float | None = None) -> np.ndarray:
@@ -175,3 +190,50 @@ def brute_force_maxmin(rec: np.ndarray, total_q16: int, step_q16: int) -> float:
 
     walk(0, units, [])
     return best
+
+
+def output_deviation(o_sparse, o_dense) -> np.ndarray:
+    """dev[h] = ||o_sparse[:, h] - o_dense[:, h]||_F / ||o_dense[:, h]||_F over
+    every sequence, row and channel of head h (R37); arrays ``[b, Hq, S, D]``."""
+    a, r = to_f64(o_sparse), to_f64(o_dense)
+    H = a.shape[1]
+    dev = np.zeros(H)
+    for h in range(H):
+        num = 0.0
+        den = 0.0
+        for bi in range(a.shape[0]):
+            d = a[bi, h] - r[bi, h]
+            num += float(np.sum(d * d))
+            den += float(np.sum(r[bi, h] * r[bi, h]))
+        dev[h] = math.sqrt(num) / math.sqrt(den) if den > 0 else 0.0
+    return dev
+
+
+def deviation_table(q, k, v, budget: Mapping[str, Sequence[int]], block: int, step_q16: int) -> np.ndarray:
+    """dev[h, i]: output deviation of head h when every head runs at ratio
+    (i + 1) * step (R34, R37), the blocks chosen by the path's own selection
+    (pooled scores, per-head top-k with the sink and local blocks), against
+    causal attention over every key (ratio 1 keeps every block)."""
+    n_grid = 65536 // step_q16
+    H = q.shape[1]
+    full = dict(budget)
+    full["ratio_q16"] = [65536] * H
+    idx, cnt = select_blocks_prefill(q, k, full, block)
+    o_dense, _ = attention_prefill_gather(q, k, v, idx, cnt, block)
+    dev = np.zeros((H, n_grid))
+    for i in range(n_grid):
+        b = dict(budget)
+        b["ratio_q16"] = [(i + 1) * step_q16] * H
+        idx, cnt = select_blocks_prefill(q, k, b, block)
+        o, _ = attention_prefill_gather(q, k, v, idx, cnt, block)
+        dev[:, i] = output_deviation(o, o_dense)
+    return dev
+
+
+def needed_ratio_deviation(dev_h: Sequence[float], max_dev: float, step_q16: int) -> int:
+    """Smallest grid ratio whose output deviation is at most ``max_dev`` (R37)."""
+    for i, d in enumerate(dev_h):
+        if d <= max_dev:
+            return (i + 1) * step_q16
+    return len(dev_h) * step_q16
+

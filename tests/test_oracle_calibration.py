@@ -136,3 +136,82 @@ def test_host_calibration_rejects_bad_arguments():
         SA.sa_budget_shift(rec, 5000, 3 * 5000)  # step does not divide 2^16
     with pytest.raises(SA.SaError):
         SA.sa_budget_recovery(np.ones((1, 2, 3, 3), np.float32), _budget(2, min_blocks=1), 4096)
+
+
+# ---------------------------------------------------------------- output deviation (R37)
+
+
+def _budget(H, ratio, block):
+    return {"min_blocks": [2] * H, "ratio_q16": [ratio] * H, "n_sink": [1] * H, "n_local": [1] * H,
+            "granularity": [block] * H}
+
+
+def _qkv(seed, b=2, H=4, Hk=2, S=512, D=16):
+    r = np.random.default_rng(seed)
+    q = r.standard_normal((b, H, S, D)).astype(np.float32)
+    k = r.standard_normal((b, Hk, S, D)).astype(np.float32)
+    v = r.standard_normal((b, Hk, S, D)).astype(np.float32)
+    return q, k, v
+
+
+def test_output_deviation_hand_values():
+    """Relative Frobenius distance, pooled over sequences: one sequence 4/3;
+    two sequences (differences 4 and 0, reference norms 3 and 4) 4/5, not the
+    mean of 4/3 and 0."""
+    a = np.array([[[[3.0, 4.0]]]])
+    r = np.array([[[[3.0, 0.0]]]])
+    assert O.output_deviation(a, r)[0] == pytest.approx(4.0 / 3.0, abs=1e-15)
+    a2 = np.array([[[[3.0, 4.0]]], [[[0.0, 4.0]]]])
+    r2 = np.array([[[[3.0, 0.0]]], [[[0.0, 4.0]]]])
+    assert O.output_deviation(a2, r2)[0] == pytest.approx(0.8, abs=1e-15)
+    assert O.needed_ratio_deviation([0.5, 0.2, 0.05, 0.01], 0.1, 4096) == 3 * 4096
+    assert O.needed_ratio_deviation([0.5, 0.2], 0.01, 4096) == 2 * 4096
+
+
+def test_output_deviation_split_identity():
+    """Dense attention splits over the kept and the dropped keys: with w the
+    dropped keys' softmax weight (from the two log-sum-exps),
+    o_dense = (1 - w) o_kept + w o_dropped, so o_dense - o_kept = w (o_dropped -
+    o_kept).  The deviation the table reports must equal the one built from
+    this split, computed from separate softmaxes over disjoint key sets."""
+    q, k, v = _qkv(11)
+    block, step = 64, 16384
+    dev = O.deviation_table(q, k, v, _budget(4, 0, block), block, step)
+    assert dev.shape == (4, 4)
+    nb = 512 // block
+    for i in range(4):
+        ratio = (i + 1) * step
+        idx, cnt = O.select_blocks_prefill(q, k, _budget(4, ratio, block), block)
+        o_kept, l_kept = O.attention_prefill_gather(q, k, v, idx, cnt, block)
+        # the dropped causal blocks of every tile
+        comp = np.full((2, 4, nb, nb), -1, dtype=np.int32)
+        ccnt = np.zeros((2, 4, nb), dtype=np.int32)
+        for bi in range(2):
+            for h in range(4):
+                for m in range(nb):
+                    rest = sorted(set(range(m + 1)) - set(idx[bi, h, m, :cnt[bi, h, m]].tolist()))
+                    comp[bi, h, m, :len(rest)] = rest
+                    ccnt[bi, h, m] = len(rest)
+        some = [(bi, h, m) for bi in range(2) for h in range(4) for m in range(nb) if ccnt[bi, h, m]]
+        o_out, l_out = O.attention_prefill_gather(q, k, v, comp, ccnt, block, tiles=some)
+        o_out = np.nan_to_num(o_out)  # tiles with nothing dropped (left NaN): weight 0
+        with np.errstate(invalid="ignore"):
+            w = np.where(np.isfinite(l_out), 1.0 / (1.0 + np.exp(l_kept - l_out)), 0.0)[..., None]
+        diff = w * (o_out - o_kept)
+        dense = (1.0 - w) * o_kept + w * o_out
+        want = [math.sqrt(np.sum(diff[:, h] ** 2)) / math.sqrt(np.sum(dense[:, h] ** 2)) for h in range(4)]
+        np.testing.assert_allclose(dev[:, i], want, rtol=1e-10, atol=1e-14)
+    assert np.all(dev[:, -1] == 0.0)  # ratio 1 keeps every block
+    assert np.all(dev[:, 0] > 0.05)   # a quarter of the blocks moves the output
+
+
+def test_output_deviation_zero_cases():
+    """Constant values: every softmax average is that constant, so no budget
+    moves the output; the full budget alone on random values: zero."""
+    q, k, v = _qkv(12, b=1, H=2, Hk=1, S=256)
+    v[:] = 0.75
+    dev = O.deviation_table(q, k, v, _budget(2, 0, 64), 64, 16384)
+    assert np.all(np.abs(dev) < 1e-14)
+    q, k, v = _qkv(13, b=1, H=2, Hk=1, S=256)
+    dev1 = O.deviation_table(q, k, v, _budget(2, 0, 64), 64, 65536)
+    assert dev1.shape == (2, 1) and np.all(dev1 == 0.0)
