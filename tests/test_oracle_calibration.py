@@ -141,7 +141,7 @@ def test_host_calibration_rejects_bad_arguments():
 # ---------------------------------------------------------------- output deviation (R37)
 
 
-def _budget(H, ratio, block):
+def _dev_budget(H, ratio, block):
     return {"min_blocks": [2] * H, "ratio_q16": [ratio] * H, "n_sink": [1] * H, "n_local": [1] * H,
             "granularity": [block] * H}
 
@@ -176,12 +176,12 @@ def test_output_deviation_split_identity():
     this split, computed from separate softmaxes over disjoint key sets."""
     q, k, v = _qkv(11)
     block, step = 64, 16384
-    dev = O.deviation_table(q, k, v, _budget(4, 0, block), block, step)
+    dev = O.deviation_table(q, k, v, _dev_budget(4, 0, block), block, step)
     assert dev.shape == (4, 4)
     nb = 512 // block
     for i in range(4):
         ratio = (i + 1) * step
-        idx, cnt = O.select_blocks_prefill(q, k, _budget(4, ratio, block), block)
+        idx, cnt = O.select_blocks_prefill(q, k, _dev_budget(4, ratio, block), block)
         o_kept, l_kept = O.attention_prefill_gather(q, k, v, idx, cnt, block)
         # the dropped causal blocks of every tile
         comp = np.full((2, 4, nb, nb), -1, dtype=np.int32)
@@ -210,8 +210,8 @@ def test_output_deviation_zero_cases():
     moves the output; the full budget alone on random values: zero."""
     q, k, v = _qkv(12, b=1, H=2, Hk=1, S=256)
     v[:] = 0.75
-    dev = O.deviation_table(q, k, v, _budget(2, 0, 64), 64, 16384)
+    dev = O.deviation_table(q, k, v, _dev_budget(2, 0, 64), 64, 16384)
     assert np.all(np.abs(dev) < 1e-14)
     q, k, v = _qkv(13, b=1, H=2, Hk=1, S=256)
-    dev1 = O.deviation_table(q, k, v, _budget(2, 0, 64), 64, 65536)
+    dev1 = O.deviation_table(q, k, v, _dev_budget(2, 0, 64), 64, 65536)
     assert dev1.shape == (2, 1) and np.all(dev1 == 0.0)
