@@ -950,6 +950,32 @@ sa_status sa_block_attention_mass(const sa_attn_desc* desc, const void* q, const
   return ok();
 }
 
+sa_status sa_output_deviation(const sa_attn_desc* desc, const float* o_approx, const float* o_ref, double* dev,
+                              void* stream) {
+  sa_status s = check_desc(desc, true);
+  if (s) return s;
+  if (!o_approx || !o_ref || !dev) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned16(o_approx) || !aligned16(o_ref) || (reinterpret_cast<uintptr_t>(dev) & 7))
+    return fail(SA_ERR_INVALID_ARG, "o_approx and o_ref must be 16-byte aligned, dev 8-byte aligned");
+  if (desc->head_dim % 4 || desc->o_stride[0] % 4 || desc->o_stride[1] % 4 || desc->o_stride[2] % 4)
+    return fail(SA_ERR_INVALID_ARG, "head_dim and the o strides must be multiples of 4 elements");
+  if ((s = check_device())) return s;
+  sa::DeviationParams p{};
+  p.a = o_approx;
+  p.r = o_ref;
+  p.s0 = desc->o_stride[0];
+  p.s1 = desc->o_stride[1];
+  p.s2 = desc->o_stride[2];
+  p.batch = desc->batch;
+  p.Hq = desc->n_q_heads;
+  p.S = desc->q_len;
+  p.D = desc->head_dim;
+  p.dev = dev;
+  const hipError_t e = sa::launch_output_deviation(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "output deviation");
+  return ok();
+}
+
 sa_status sa_budget_recovery(const float* mass, int32_t batch, int32_t n_heads, int32_t n_blocks,
                              const sa_head_budget* budgets, int32_t step_q16, double* recovery) {
   if (!mass || !budgets || !recovery) return fail(SA_ERR_INVALID_ARG, "NULL pointer");

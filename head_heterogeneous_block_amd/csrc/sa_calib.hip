@@ -138,7 +138,52 @@ __global__ __launch_bounds__(256) void block_mass_kernel(MassParams p) {
   for (int n = m + 1 + tid; n < p.NB; n += 256) out[n] = 0.f;
 }
 
+// Output deviation of query head h = blockIdx.x: sqrt(sum (a - r)^2) /
+// sqrt(sum r^2) over every sequence, row and channel of the head, the output
+// moved by a budget against dense attention ("Fluxion", Italian summary,
+// Intuizioni Chiave 1).  Each thread sums a fixed share of the 16-byte chunks
+// in double; the workgroup reduces in a fixed tree order (bitwise reproducible).
+__global__ __launch_bounds__(256) void output_deviation_kernel(DeviationParams p) {
+  __shared__ double red[2][256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int cpr = p.D / 4;  // 16-byte chunks per row
+  const int64_t per_seq = (int64_t)p.S * cpr;
+  double num = 0.0, den = 0.0;
+  for (int bi = 0; bi < p.batch; ++bi) {
+    const float* ab = p.a + bi * p.s0 + h * p.s1;
+    const float* rb = p.r + bi * p.s0 + h * p.s1;
+    for (int64_t c = tid; c < per_seq; c += 256) {
+      const int64_t row = c / cpr;
+      const int col = int(c % cpr) * 4;
+      const f32x4 av = *reinterpret_cast<const f32x4*>(ab + row * p.s2 + col);
+      const f32x4 rv = *reinterpret_cast<const f32x4*>(rb + row * p.s2 + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double d = (double)av[e] - (double)rv[e];
+        num += d * d;
+        den += (double)rv[e] * (double)rv[e];
+      }
+    }
+  }
+  red[0][tid] = num;
+  red[1][tid] = den;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) {
+      red[0][tid] += red[0][tid + w];
+      red[1][tid] += red[1][tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) p.dev[h] = red[1][0] > 0.0 ? sqrt(red[0][0]) / sqrt(red[1][0]) : 0.0;
+}
+
 }  // namespace
+
+hipError_t launch_output_deviation(const DeviationParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(output_deviation_kernel, dim3(p.Hq), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_block_mass(const MassParams& p, int D, int batch, hipStream_t stream) {
   dim3 grid(p.NB, p.Hq, batch);

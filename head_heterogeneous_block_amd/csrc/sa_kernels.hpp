@@ -165,4 +165,14 @@ struct MassParams {
 // block size 128; D 64 or 128
 hipError_t launch_block_mass(const MassParams& p, int D, int batch, hipStream_t stream);
 
+struct DeviationParams {
+  const float* a;  // fp32 [batch][Hq][S][D] (strided, D contiguous)
+  const float* r;  // same layout
+  int64_t s0, s1, s2;
+  int batch, Hq, S, D;
+  double* dev;     // [Hq]
+};
+// one workgroup per query head
+hipError_t launch_output_deviation(const DeviationParams& p, hipStream_t stream);
+
 }  // namespace sa

@@ -37,7 +37,7 @@ EXPORTED = [
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_sparse_attn_prefill_queues",
     "sa_decode_workspace_size", "sa_sparse_attn_decode",
     "sa_pool_keys_decode_paged", "sa_sparse_attn_decode_paged",
-    "sa_block_attention_mass", "sa_budget_recovery", "sa_budget_shift",
+    "sa_block_attention_mass", "sa_budget_recovery", "sa_budget_shift", "sa_output_deviation",
 ]
 
 
@@ -109,6 +109,7 @@ _SIG = {
     "sa_budget_recovery": (ctypes.c_int32, [ctypes.POINTER(ctypes.c_float), ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, _budp, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_double)]),
+    "sa_output_deviation": (ctypes.c_int32, [_descp, _P, _P, _P, _P]),
     "sa_budget_shift": (ctypes.c_int32, [ctypes.POINTER(ctypes.c_double), ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int64, ctypes.POINTER(ctypes.c_uint32)]),
 }
@@ -414,6 +415,41 @@ def sa_budget_recovery(mass: np.ndarray, budget: dict, step_q16: int) -> np.ndar
                                    make_budgets(budget), step_q16,
                                    rec.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
     return rec
+
+
+def sa_output_deviation(desc: sa_attn_desc, o_approx: torch.Tensor, o_ref: torch.Tensor, dev: torch.Tensor) -> None:
+    """dev [n_q_heads] float64 on the device: relative output distance per head."""
+    if dev.dtype != torch.float64 or dev.numel() < desc.n_q_heads:
+        raise ValueError("dev must be a float64 tensor of n_q_heads entries")
+    _check(_lib.sa_output_deviation(ctypes.byref(desc), _ptr(o_approx), _ptr(o_ref), _ptr(dev), _stream(o_ref)))
+
+
+def deviation_table(q, k, v, budget: dict, block: int, step_q16: int, n_bins: int = 512) -> np.ndarray:
+    """dev[h, i]: output deviation of head h when every head runs at ratio
+    (i + 1) * step_q16, against ratio 1 (every block), each output from the
+    library's selection and prefill attention (fp32 out), each deviation from
+    sa_output_deviation."""
+    H = q.shape[1]
+    n_grid = 65536 // step_q16
+    if n_grid * step_q16 != 65536:
+        raise ValueError("step_q16 must divide 65536")
+
+    def run(ratio):
+        b = dict(budget)
+        b["ratio_q16"] = [ratio] * H
+        plan = PrefillPlan(q, k, v, b, block, n_bins=n_bins, out_f32=True, queue=True)
+        o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        plan.select(q, k)
+        plan.attend(q, k, v, o)
+        return plan, o
+
+    plan, o_ref = run(65536)
+    dev = torch.empty((n_grid, H), dtype=torch.float64, device=q.device)
+    for i in range(n_grid):
+        _, o = run((i + 1) * step_q16)
+        sa_output_deviation(plan.desc, o, o_ref, dev[i])
+    torch.cuda.synchronize(q.device)
+    return dev.cpu().numpy().T.copy()
 
 
 def sa_budget_shift(recovery: np.ndarray, step_q16: int, total_q16: int) -> np.ndarray:

@@ -350,6 +350,23 @@ sa_status sa_block_attention_mass(const sa_attn_desc* desc, const void* q, const
 sa_status sa_budget_recovery(const float* mass, int32_t batch, int32_t n_heads, int32_t n_blocks,
                              const sa_head_budget* budgets, int32_t step_q16, double* recovery);
 
+/* Output deviation per query head, the output-aware budget criterion of
+ * "Fluxion" (Italian summary, Intuizioni Chiave 1: a budget judged by how far
+ * it moves the head's attention output, not by the attention weight it keeps):
+ *   dev[h] = sqrt(sum (o_approx - o_ref)^2) / sqrt(sum o_ref^2)
+ * over every sequence, query row and channel of head h, summed in double in a
+ * fixed order (bitwise reproducible); 0 where o_ref is all zero.  o_approx is
+ * typically sa_sparse_attn_prefill's fp32 output (out_f32) at a candidate
+ * budget and o_ref the same at ratio 1 (every block).  Over a grid of ratios
+ * this gives a quality table (1 - dev) for sa_budget_shift.
+ *   o_approx, o_ref [dev] fp32 with desc's o layout (o_stride, q_len rows,
+ *                   head_dim contiguous), 16-byte aligned; head_dim and the
+ *                   strides multiples of 4
+ *   dev             [dev] double [n_q_heads]
+ * One workgroup per head: an offline calibration step, not the path. */
+sa_status sa_output_deviation(const sa_attn_desc* desc, const float* o_approx, const float* o_ref,
+                              double* dev, void* stream);
+
 /* Max-min budget shifting (host, synchronous) on a recovery table: every head
  * starts at total_q16 / n_heads (a whole number of steps); while the head with
  * the lowest recovery (lowest index on ties) can grow and another head can give

@@ -417,3 +417,20 @@ def test_prefill_queues_validation():
     assert call([0, 3, tiles], ws=4) == SA.SA_ERR_INVALID_ARG         # 2 counters need 8 bytes
     if not torch.cuda.is_available():
         assert call([0, 3, tiles]) in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
+
+
+def test_output_deviation_validation():
+    """sa_output_deviation rejects NULL and misaligned pointers before any
+    launch; valid ones reach the device check."""
+    import torch
+    d = _desc()
+    lib = SA._lib
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.sa_output_deviation(ctypes.byref(d), None, fake, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_output_deviation(ctypes.byref(d), ctypes.c_void_p((1 << 20) + 4), fake, fake,
+                                   None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_output_deviation(ctypes.byref(d), fake, fake, ctypes.c_void_p((1 << 20) + 4),
+                                   None) == SA.SA_ERR_INVALID_ARG
+    if not torch.cuda.is_available():
+        assert lib.sa_output_deviation(ctypes.byref(d), fake, fake, fake, None) in (SA.SA_ERR_NO_DEVICE,
+                                                                                     SA.SA_ERR_HIP)
