@@ -131,11 +131,26 @@ def calibration_timing(dev, stream):
     ratios = SA.sa_budget_shift(rec, step, H * 8192)
     t2 = time.perf_counter()
     rmin = float(min(rec[h, ratios[h] // step - 1] for h in range(H)))
+    # the output-aware variant: each head's output deviation from dense
+    # attention on a grid of 16 ratios (the path's own prefill at each ratio)
+    dstep = 4096
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    dev_tab = SA.deviation_table(inp.q, inp.k, inp.v, bud | {"granularity": [128] * H}, spec.block, dstep)
+    t4 = time.perf_counter()
+    # quality for the shift: 1 - deviation, as its running best along the grid
+    # (a larger budget can swap one block for another and move the output a
+    # little more; the shift is defined on tables that do not decrease)
+    dshift = SA.sa_budget_shift(np.maximum.accumulate(1.0 - dev_tab, axis=1), dstep, H * 8192)
     return {"workload": spec.name, "mass_ms": ms, "mass_qk_tflops": flops / (ms * 1e-3) / 1e12,
             "recovery_table_host_ms": (t1 - t0) * 1e3, "shift_host_ms": (t2 - t1) * 1e3, "step_q16": step,
             "mean_ratio": 0.125, "lowest_recovery_equal_split": float(rec[:, 8192 // step - 1].min()),
             "lowest_recovery_shifted": rmin,
-            "ratio_range": [int(np.min(ratios)), int(np.max(ratios))]}
+            "ratio_range": [int(np.min(ratios)), int(np.max(ratios))],
+            "deviation_table_ms": (t4 - t3) * 1e3, "deviation_step_q16": dstep,
+            "deviation_at_mean_ratio": [float(dev_tab[:, 8192 // dstep - 1].min()),
+                                        float(dev_tab[:, 8192 // dstep - 1].max())],
+            "deviation_shift_ratio_range": [int(np.min(dshift)), int(np.max(dshift))]}
 
 
 def cpu_baseline_prefill(inp, block_idx, block_cnt, tiles_per_head=96, select_heads=(0, 4, 8, 12, 16, 20, 24, 28)):
