@@ -38,12 +38,15 @@ def _bud_sub(budget, heads):
 # ---------------------------------------------------------------- prefill, all rows
 
 
-@pytest.mark.parametrize("schedule", ["natural", "lpt"])
+@pytest.mark.parametrize("schedule", ["natural", "lpt", "queue"])
 def test_prefill_config0_fp32_all_rows(schedule):
     spec = W.TINY_F32
     inp = W.make_prefill(spec, W.seed_of(W.TINY_F32), device=DEV)
     _say("case: config0 fp32", schedule)
-    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=8 if schedule == "lpt" else 0)
+    # queue: 3 workgroups over the queue in 8 XCD partitions (one KV group,
+    # so seven partitions are empty and every workgroup walks them)
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins={"natural": 0, "lpt": 8, "queue": 3}[schedule],
+                                         queue=schedule == "queue")
     q, k, v = to_host(inp)
     oidx, ocnt, scores = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, return_scores=True)
     gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
