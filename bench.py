@@ -77,6 +77,11 @@ def timed(fn, stream, reps, scrub=None):
     return ts[len(ts) // 2], sum(ts) / len(ts), ts
 
 
+def pct(ts, q):
+    """q-quantile of sorted samples (nearest rank)."""
+    return ts[min(len(ts) - 1, max(0, int(round(q * (len(ts) - 1)))))]
+
+
 PREFILL_KERNEL_SOURCES = ("sa_prefill.hip", "sa_prefill_common.hpp", "sa_device.hpp")
 
 
@@ -288,15 +293,20 @@ def main():
     res = {}
     scrub = torch.empty(512 << 18, dtype=torch.float32, device=dev)  # 512 MiB, twice the MALL
     if args.only in ("prefill", "all"):
-        res["sel_ms"] = timed(sel, stream, reps)[0]
-        att_med, att_mean, _ = timed(att, stream, reps)
+        sel_med, _, sel_ts = timed(sel, stream, reps)
+        res["sel_ms"] = sel_med
+        res["sel_p10_p90_ms"] = [pct(sel_ts, 0.1), pct(sel_ts, 0.9)]
+        att_med, att_mean, att_ts = timed(att, stream, reps)
         res["att_ms"] = att_med
         res["att_mean_ms"] = att_mean
+        res["att_p10_p90_ms"] = [pct(att_ts, 0.1), pct(att_ts, 0.9)]
         res["att_scrub_ms"] = timed(att, stream, reps, scrub)[0]
     if args.only in ("decode", "all"):
         res["dsel_ms"] = timed(dsel, stream, reps)[0]
         res["datt_ms"] = timed(datt, stream, reps)[0]
-        res["dstep_ms"] = timed(lambda: (dsel(), datt()), stream, reps)[0]
+        dmed, _, dts = timed(lambda: (dsel(), datt()), stream, reps)
+        res["dstep_ms"] = dmed
+        res["dstep_p10_p90_ms"] = [pct(dts, 0.1), pct(dts, 0.9)]
         res["dstep_scrub_ms"] = timed(lambda: (dsel(), datt()), stream, reps, scrub)[0]
         if not args.no_paged:
             # the same decode step over the cache scattered into per-KV-head
@@ -316,9 +326,11 @@ def main():
             del pk, pplan
             torch.cuda.empty_cache()
 
-    bidx = plan.block_idx.cpu().numpy()
-    bcnt = plan.block_cnt.cpu().numpy()
-    flops = M.prefill_flops(bidx, bcnt, pspec.seq_len, pspec.block, pspec.head_dim)
+    flops = None
+    if args.only in ("prefill", "all"):  # the block table is filled only when the prefill ran
+        bidx = plan.block_idx.cpu().numpy()
+        bcnt = plan.block_cnt.cpu().numpy()
+        flops = M.prefill_flops(bidx, bcnt, pspec.seq_len, pspec.block, pspec.head_dim)
     dbytes = {"total": 0}
     if args.only in ("decode", "all"):
         dbidx = dplan.block_idx.cpu().numpy()
@@ -414,14 +426,15 @@ def main():
     cpu = None
     cpu_dec = None
     if not args.no_cpu_baseline and args.only in ("prefill", "all"):
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:  # noqa: BLE001
-            cores = len(os.sched_getaffinity(0))
-        cpu_ms, spent, desc = cpu_baseline_prefill(pin, bidx, bcnt)
-        cpu = {"value": cpu_ms, "unit": "ms/layer", "cores": int(cores), "kind": "oracle",
-               "sample": f"fp64 oracle on {pspec.name}: {desc}; {spent:.1f} s of CPU work"}
+        # the host cores this process may run on; the BLAS pool (the oracle's
+        # matrix products) is set to that many threads
+        cores = len(os.sched_getaffinity(0))
+        from threadpoolctl import threadpool_info, threadpool_limits
+        with threadpool_limits(limits=cores):
+            blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+            cpu_ms, spent, desc = cpu_baseline_prefill(pin, bidx, bcnt)
+        cpu = {"value": cpu_ms, "unit": "ms/layer", "cores": int(cores), "blas_threads": int(blas),
+               "kind": "oracle", "sample": f"fp64 oracle on {pspec.name}: {desc}; {spent:.1f} s of CPU work"}
         print(f"[bench] cpu baseline (prefill) {spent:.1f} s", file=sys.stderr, flush=True)
         if args.only == "all":
             dms, dspent = cpu_baseline_decode(din, dbidx, dbcnt)
@@ -447,12 +460,14 @@ def main():
                    "global_batch": 1, "seq_len": pspec.seq_len, "parallelism": "single GPU",
                    "schedule": f"work queue: {n_bins} workgroups, tiles in load tiers (quarter octave) heaviest first, grouped by (sequence, KV head) within a tier"
                    + (f"; cut into {args.queues} partitions (one per XCD) of (load tier, sequence, KV head) runs placed by LPT, workgroup w starting on partition w mod {args.queues} and moving on when it is empty" if args.queues > 1 else "")},
-        "prefill": {"select_ms": res.get("sel_ms"), "attention_ms": res.get("att_ms"),
+        "prefill": {"select_ms": res.get("sel_ms"), "select_p10_p90_ms": res.get("sel_p10_p90_ms"),
+                    "attention_ms": res.get("att_ms"), "attention_p10_p90_ms": res.get("att_p10_p90_ms"),
                     "attention_ms_scrubbed": res.get("att_scrub_ms"),
                     "attended_tflops": tflops, "attended_flops": flops,
                     "mfma_frac": roofline["frac"], "schedule_host_ms": lpt_ms},
         "decode": {"select_ms": res.get("dsel_ms"), "attention_ms": res.get("datt_ms"),
-                   "step_ms": res.get("dstep_ms"), "step_ms_scrubbed": res.get("dstep_scrub_ms"),
+                   "step_ms": res.get("dstep_ms"), "step_p10_p90_ms": res.get("dstep_p10_p90_ms"),
+                   "step_ms_scrubbed": res.get("dstep_scrub_ms"),
                    "bytes": dbytes, "step_gbps": dgbps,
                    "hbm_frac": dgbps / (M.PEAK_HBM_BYTES / 1e9) if dgbps else None,
                    "kv_gbps_attention_kernel": kv_gbps},

@@ -238,7 +238,7 @@ DecodeAttnWs decode_attn_ws(const sa_attn_desc* d, const sa_head_budget* b) {
   w.n_union = align256(bk * w.max_union * 4);
   w.part_o = w.n_union + align256(bk * 4);
   w.part_ml = w.part_o + align256(bk * w.n_chunks * G * d->head_dim * 4);
-  w.total = w.part_ml + align256(bk * w.n_chunks * G * 2 * 4);
+  w.total = w.part_ml + align256(bk * w.n_chunks * G * sa::kPartMl * 4);
   return w;
 }
 

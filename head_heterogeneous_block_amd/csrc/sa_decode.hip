@@ -286,9 +286,10 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeAttnParams p) {
       l += sm[w][gi][1] * f;
     }
     p.part_o[(pbase + gi) * D + d] = acc;
-    if (d == 0) {
-      p.part_ml[(pbase + gi) * 2 + 0] = mx;
-      p.part_ml[(pbase + gi) * 2 + 1] = l;
+    if (d == 0) {  // fp32 probabilities: nothing is rounded
+      p.part_ml[(pbase + gi) * kPartMl + 0] = mx;
+      p.part_ml[(pbase + gi) * kPartMl + 1] = l;
+      p.part_ml[(pbase + gi) * kPartMl + 2] = l;
     }
   }
 }
@@ -407,7 +408,9 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
   f32x4 oacc[C::kDT];
 #pragma unroll
   for (int t = 0; t < C::kDT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_part = 0.f;
+  // l_part sums the probabilities as bf16-rounded for the P V MFMAs (the
+  // normaliser of o); l_lse the same before rounding (for lse only)
+  float m_run = kNegInf, l_part = 0.f, l_lse = 0.f;
   const float c2 = p.scale_log2;
 
   auto step = [&](auto S, int i) {
@@ -444,6 +447,7 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
       const float m_new = raise ? mt : m_run;
       const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 when raised from -inf
       l_part *= alpha;
+      l_lse *= alpha;
 #pragma unroll
       for (int t = 0; t < C::kDT; ++t) oacc[t] *= alpha;
       m_run = m_new;
@@ -452,8 +456,9 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
     float pr[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], c2, -m_use));
-    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    l_lse += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const uint32_t pk0 = pack_bf16x2(pr[0], pr[1]), pk1 = pack_bf16x2(pr[2], pr[3]);
+    l_part += (bf16_lo(pk0) + bf16_hi(pk0)) + (bf16_lo(pk1) + bf16_hi(pk1));
     const v4i16 pb = __builtin_bit_cast(v4i16, uint2{pk0, pk1});
     // V^T fragments: source lane (group qg, index jj) points at V row
     // 4 qg + jj / 4, columns 16 t + 4 (jj % 4) .. +3; the lane receives
@@ -485,34 +490,37 @@ __global__ __launch_bounds__(64) void decode_attn_mfma_kernel(DecodeAttnParams p
   // partial state of this chunk: heads col < G; lane (col, qg) holds
   // d = 16 t + 4 qg .. +3
   const float l = sum_xor32(sum_xor16(l_part));
+  const float lx = sum_xor32(sum_xor16(l_lse));
   if (col < p.G) {
     const int64_t r = (((int64_t)bi * p.Hkv + j) * p.n_chunks + c) * p.G + col;
 #pragma unroll
     for (int t = 0; t < C::kDT; ++t) *reinterpret_cast<f32x4*>(p.part_o + r * D + 16 * t + 4 * qg) = oacc[t];
     if (qg == 0) {
-      p.part_ml[r * 2 + 0] = m_run;
-      p.part_ml[r * 2 + 1] = l;
+      p.part_ml[r * kPartMl + 0] = m_run;
+      p.part_ml[r * kPartMl + 1] = l;
+      p.part_ml[r * kPartMl + 2] = lx;
     }
   }
 }
 
 // ---------------------------------------------------------------- combine
 // Fixed-order merge of the chunk partials of one (batch, query head):
-// o = sum_c w_c o_c / sum_c w_c l_c with w_c = 2^(m_c - max_c m_c).  The
+// o = sum_c w_c o_c / sum_c w_c l_c with w_c = 2^(m_c - max_c m_c), l_c the
+// chunk's sum of the probabilities as applied to V; lse from the unrounded sums.  The
 // weights of up to D chunks at a time go through LDS, so the loop over chunks
 // issues independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeCombineParams p, int dtype) {
   constexpr int kW = D / 64;  // waves
   __shared__ float w_s[D + 16];  // 16 words of slack for the 16-wide unrolled reads
-  __shared__ float red[kW];
+  __shared__ float red[kW], red2[kW];
   const int h = blockIdx.x, bi = blockIdx.y;
   const int j = h / p.G, gi = h % p.G;
   const int d = threadIdx.x, lane = d & 63, wv = d >> 6;
   const int nu = p.n_union[(int64_t)bi * p.Hkv + j];
   const int nch = (nu + p.chunk_atoms - 1) / p.chunk_atoms;
   const int64_t base = ((int64_t)bi * p.Hkv + j) * p.n_chunks;
-  auto ml = [&](int c, int k) { return p.part_ml[((base + c) * p.G + gi) * 2 + k]; };
+  auto ml = [&](int c, int k) { return p.part_ml[((base + c) * p.G + gi) * kPartMl + k]; };
   float mx = kNegInf;
   for (int c = d; c < nch; c += D) mx = fmaxf(mx, ml(c, 0));
   mx = wave_max(mx);
@@ -521,11 +529,12 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeCombineParams p
 #pragma unroll
   for (int i = 0; i < kW; ++i) mx = fmaxf(mx, red[i]);
   const float mu = mx == kNegInf ? 0.f : mx;
-  float acc = 0.f, lp = 0.f;
+  float acc = 0.f, lp = 0.f, lq = 0.f;
   for (int c0 = 0; c0 < nch; c0 += D) {
     const int c = c0 + d;
     const float w = c < nch ? __builtin_amdgcn_exp2f(ml(c, 0) - mu) : 0.f;
     lp += c < nch ? w * ml(c, 1) : 0.f;
+    lq += c < nch ? w * ml(c, 2) : 0.f;
     __syncthreads();
     w_s[d] = w;
     __syncthreads();
@@ -542,17 +551,24 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeCombineParams p
     }
   }
   lp = wave_sum(lp);
+  lq = wave_sum(lq);
   __syncthreads();
-  if (lane == 0) red[wv] = lp;
+  if (lane == 0) {
+    red[wv] = lp;
+    red2[wv] = lq;
+  }
   __syncthreads();
-  float l = 0.f;
+  float l = 0.f, lx = 0.f;
 #pragma unroll
-  for (int i = 0; i < kW; ++i) l += red[i];
+  for (int i = 0; i < kW; ++i) {
+    l += red[i];
+    lx += red2[i];
+  }
   const float o = l > 0.f ? acc / l : 0.f;
   const int64_t oi = bi * p.os0 + h * p.os1 + d;
   if (p.out_f32 || dtype == 1) reinterpret_cast<float*>(p.o)[oi] = o;
   else reinterpret_cast<bf16_t*>(p.o)[oi] = bf16_t(pack_bf16x2(o, 0.f) & 0xffffu);
-  if (p.lse && d == 0) p.lse[(int64_t)bi * p.Hq + h] = l > 0.f ? (mx + __log2f(l)) * kLn2 : kNegInf;
+  if (p.lse && d == 0) p.lse[(int64_t)bi * p.Hq + h] = lx > 0.f ? (mx + __log2f(lx)) * kLn2 : kNegInf;
 }
 
 }  // namespace

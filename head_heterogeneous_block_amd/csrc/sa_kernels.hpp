@@ -124,6 +124,10 @@ struct DecodePlanParams {
 };
 hipError_t launch_decode_plan(const DecodePlanParams& p, int batch, hipStream_t stream);
 
+// Per chunk partial of one head: running max (log2 domain), the sum of the
+// probabilities as they weighted the V rows (bf16-rounded for bf16 inputs: the
+// normaliser of o), and the same sum before rounding (for lse).
+constexpr int kPartMl = 3;
 struct DecodeAttnParams {
   const void* q;
   int64_t qs0, qs1;
@@ -137,7 +141,7 @@ struct DecodeAttnParams {
   float scale_log2;
   PageTable pages;  // paged: k, v are the pools (head stride ks1 / vs1, row stride ks2 / vs2)
   float* part_o;    // [batch][Hkv][n_chunks][G][D]
-  float* part_ml;   // [batch][Hkv][n_chunks][G][2]  (max in log2 domain, sum)
+  float* part_ml;   // [batch][Hkv][n_chunks][G][kPartMl]
 };
 hipError_t launch_decode_attn(const DecodeAttnParams& p, int dtype, int D, int batch, hipStream_t stream);
 

@@ -50,7 +50,7 @@ namespace {
 
 using namespace prefill;
 
-template <typename T, int D, int B>
+template <typename T, int D, int B, bool kLse>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
   using C = Cfg<T, D, B>;
   __shared__ __attribute__((aligned(1024))) char smem[C::kLds];
@@ -298,7 +298,10 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // ---------------------------------------------------------------- tile state
   u32x4 qf[C::kDG];  // Q^T fragments of the wave's 32 queries
   f32x16 oacc[C::kDT];
-  float m_run = kNegInf, l_run = 0.f;
+  // l_run: sum of the probabilities exactly as the P V MFMAs weight the V rows
+  // (bf16-rounded for bf16 inputs), so O / l_run is a convex combination of V
+  // rows with those weights; l_lse: the same sum before rounding, for lse only.
+  float m_run = kNegInf, l_run = 0.f, l_lse = 0.f;
   int t_bh = 0, t_m = 0;  // tile being accumulated
 
   auto start_tile = [&](const Step& s) {
@@ -317,6 +320,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     }
     m_run = kNegInf;
     l_run = 0.f;
+    l_lse = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt) oacc[dt] = f32x16{};
   };
@@ -326,6 +330,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int bi = t_bh / Hq, h = t_bh % Hq;
     const float l = sum_xor32(l_run);
     const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float lx = kLse && C::kBf16 ? sum_xor32(l_lse) : l;
     const int qrow = t_m * B + wave * 32 + col;
     if (qrow < S) {
       const int64_t orow = bi * COLD(os0) + h * COLD(os1) + (int64_t)qrow * COLD(os2);
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         }
       }
       float* const lse = COLD(lse);
-      if (lse && half == 0) lse[(int64_t)t_bh * S + qrow] = l > 0.f ? (m_run + __log2f(l)) * kLn2 : kNegInf;
+      if (kLse && half == 0) lse[(int64_t)t_bh * S + qrow] = lx > 0.f ? (m_run + __log2f(lx)) * kLn2 : kNegInf;
     }
   };
 
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       // fetching or advancing its cursor, so the MFMA pipe stays fed
       __builtin_amdgcn_s_setprio(1);
       u32x4 pf[4];
-      float ps0 = 0.f, ps1 = 0.f;
+      float ps0 = 0.f, ps1 = 0.f, px0 = 0.f, px1 = 0.f;
 #pragma unroll
       for (int dg = 0; dg < C::kDG; ++dg) {
 #pragma unroll
@@ -425,12 +430,18 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           const int i = (kc & 1) * 8 + 2 * w;
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][i], c2, -m_use));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][i + 1], c2, -m_use));
-          pf[kc][w] = pack_bf16x2(p0, p1);
-          ps0 += p0;
-          ps1 += p1;
+          const uint32_t pk = pack_bf16x2(p0, p1);
+          pf[kc][w] = pk;
+          ps0 += bf16_lo(pk);
+          ps1 += bf16_hi(pk);
+          if constexpr (kLse) {
+            px0 += p0;
+            px1 += p1;
+          }
         }
       }
       l_run += ps0 + ps1;
+      if constexpr (kLse) l_lse += px0 + px1;
       // O^T += V^T P^T.  A fragments by transposed LDS reads: 16-lane group G
       // covers d = 32 dt + 16 (G % 2) + lane % 16 and keys 16 kc + 8 (G / 2) +
       // 4 r + 0..3; source lane j of the group points at V row k0 + j / 4,
@@ -547,6 +558,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         const float m_new = raise ? mx : m_run;
         const float alpha = raise ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;  // 0 when m_run = -inf
         l_run *= alpha;
+        if constexpr (kLse) l_lse *= alpha;
 #pragma unroll
         for (int dt = 0; dt < C::kDT; ++dt) oacc[dt] *= alpha;
         m_run = m_new;
@@ -574,7 +586,8 @@ __global__ void queue_reset_kernel(int* counters, int n) {
 
 template <typename T, int D, int B>
 hipError_t launch_t(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<T, D, B>), dim3(grid), dim3(2 * B), 0, stream, p);
+  if (p.lse) hipLaunchKernelGGL((prefill_kernel<T, D, B, true>), dim3(grid), dim3(2 * B), 0, stream, p);
+  else hipLaunchKernelGGL((prefill_kernel<T, D, B, false>), dim3(grid), dim3(2 * B), 0, stream, p);
   return hipGetLastError();
 }
 

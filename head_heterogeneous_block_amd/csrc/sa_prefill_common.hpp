@@ -13,10 +13,13 @@ namespace prefill {
 
 constexpr int kKS = 64;       // keys per step
 // log2 headroom before the running max is raised (P <= 2^kLazy).  P is
-// rounded to bf16 (relative error up to 2^-8); with a headroom the largest P of
-// a row is not 1 and is rounded too, which shows when one key holds most of a
-// row's weight (output error 0.014 at headroom 8, 0.005 at 0, for up to 3.7%
-// more time on the 128K layer); 8 keeps the benchmark error near 3e-3.
+// rounded to bf16 for the P V MFMAs (relative error up to 2^-8), and the
+// normaliser sums those same rounded values, so the output is an exact convex
+// combination of the V rows under slightly perturbed weights whatever the
+// headroom: the largest P of a row being rounded too no longer biases it.  (A
+// normaliser over the unrounded P left an error of up to 2^-8 of the dominant
+// key's V row when one key held most of a row's weight.)  A large headroom
+// keeps the rescaling of O rare.
 constexpr float kLazy = 8.f;
 
 // swap bits 2 and 3 of a key index (an involution)

@@ -363,8 +363,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   uint32_t before;
   block_scan<NT>((n_tie << 16) | n_gt, before, red);
   const uint32_t gt_before = before & 0xffffu, ties_before = before >> 16;
-  const uint32_t my_ties = ties_before >= ties_wanted ? 0u : min(n_tie, ties_wanted - ties_before);
-  uint32_t pos = gt_before + min(ties_before, ties_wanted);
+  // ties kept at lower indices, and how many of this thread's ties are kept.
+  // Written without a guarded subtraction: ROCm 7.2's clang hoisted the
+  // subtraction of a "ties_before >= ties_wanted ? 0 : ties_wanted -
+  // ties_before" form out of its guard with its no-wrap flag and then folded
+  // min(ties_before, ties_wanted) to ties_before, which misplaced a kept block
+  // that had more ties than ties_wanted before it (rows with exact ties).
+  const uint32_t taken_before = min(ties_before, ties_wanted);
+  const uint32_t my_ties = min(n_tie, ties_wanted - taken_before);
+  uint32_t pos = gt_before + taken_before;
   uint32_t t_used = 0;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {

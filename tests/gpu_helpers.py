@@ -28,7 +28,14 @@ def gap_scale(a: float, b: float, row_max: float) -> float:
 
 
 def check_row(gpu_sel, ora_sel, scores, k, forced):
-    """Returns True if the row was pinned (exact match required), False if exempt."""
+    """Checks one selected row.  Returns 1 if the row was pinned by its score gap
+    (exact match required), 2 if pinned by an exact tie (exact match required:
+    ties go to the lowest block index), 0 if exempt (near tie: validity only).
+
+    An exact tie is a row whose last kept and best dropped candidates have equal
+    fp64 oracle scores (-0 and +0 compare equal), with every other candidate more
+    than the gap away from that value, so the choice inside the tied set is
+    decided by the tie rule alone."""
     gpu_sel = [int(x) for x in gpu_sel]
     ora_sel = [int(x) for x in ora_sel]
     assert len(gpu_sel) == k, (len(gpu_sel), k)
@@ -39,26 +46,38 @@ def check_row(gpu_sel, ora_sel, scores, k, forced):
     dropped = [n for n in cand if n not in set(ora_sel)]
     if not kept or not dropped:
         assert gpu_sel == ora_sel
-        return True
+        return 1
     row_max = float(np.max(np.abs(scores[cand])))
     last_kept = min(scores[n] for n in kept)
     best_drop = max(scores[n] for n in dropped)
     scale = gap_scale(last_kept, best_drop, row_max)
     if last_kept - best_drop > GAP * scale:
         assert gpu_sel == ora_sel, (gpu_sel, ora_sel)
-        return True
+        return 1
+    if last_kept == best_drop:
+        others = [scores[n] for n in cand if scores[n] != last_kept]
+        if all(abs(x - last_kept) > GAP * scale for x in others):
+            assert gpu_sel == ora_sel, ("exact tie", gpu_sel, ora_sel)
+            return 2
     assert fs <= set(gpu_sel)
     gkept = [n for n in gpu_sel if n not in fs]
     gdrop = [n for n in cand if n not in set(gpu_sel)]
     if gkept and gdrop:
         assert min(scores[n] for n in gkept) >= max(scores[n] for n in gdrop) - GAP * scale
-    return False
+    return 0
 
 
 def check_prefill_selection(gpu_idx, gpu_cnt, ora_idx, ora_cnt, scores, budget, heads=None):
     """Compare [b, H, NB, kmax] tables; ``heads`` maps local head -> budget head."""
     b, H, nb = gpu_cnt.shape
-    pinned = exempt = 0
+    kinds = count_rows_prefill(gpu_idx, gpu_cnt, ora_idx, ora_cnt, scores, budget, heads)
+    return kinds[1] + kinds[2], kinds[0]
+
+
+def count_rows_prefill(gpu_idx, gpu_cnt, ora_idx, ora_cnt, scores, budget, heads=None):
+    """check_row over every row; returns counts of [exempt, gap-pinned, tie-pinned]."""
+    b, H, nb = gpu_cnt.shape
+    kinds = [0, 0, 0]
     np.testing.assert_array_equal(gpu_cnt, ora_cnt)
     for bi in range(b):
         for h in range(H):
@@ -67,11 +86,8 @@ def check_prefill_selection(gpu_idx, gpu_cnt, ora_idx, ora_cnt, scores, budget, 
                 c = int(ora_cnt[bi, h, m])
                 assert np.all(gpu_idx[bi, h, m, c:] == -1)
                 F = O.forced_blocks(m + 1, int(budget["n_sink"][hb]), int(budget["n_local"][hb]))
-                if check_row(gpu_idx[bi, h, m, :c], ora_idx[bi, h, m, :c], scores[bi, h, m, : m + 1], c, F):
-                    pinned += 1
-                else:
-                    exempt += 1
-    return pinned, exempt
+                kinds[check_row(gpu_idx[bi, h, m, :c], ora_idx[bi, h, m, :c], scores[bi, h, m, : m + 1], c, F)] += 1
+    return kinds
 
 
 def prefill_gpu(inp: W.PrefillInputs, n_bins: int = 0, out_f32: bool = True, with_lse: bool = True,

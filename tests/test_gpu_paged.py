@@ -88,7 +88,7 @@ def test_paged_decode_bitwise_and_oracle(page_size, L):
             c = int(ocnt[bi, h])
             assert int(gcnt[bi, h]) == c
             F = O.forced_blocks(-(-L // g), int(inp.budget["n_sink"][h]), int(inp.budget["n_local"][h]))
-            pinned += check_row(gidx[bi, h, :c], oidx[bi, h, :c], sc[bi, h], c, F)
+            pinned += bool(check_row(gidx[bi, h, :c], oidx[bi, h, :c], sc[bi, h], c, F))
     ro, rl = O.decode_attention(q, k, v, gidx, gcnt, inp.budget["granularity"])
     err, lerr = max_abs(op.cpu().numpy(), ro), max_abs(lp.cpu().numpy(), rl)
     _say("pinned", pinned, "max abs err o", err, "lse", lerr)

@@ -370,36 +370,47 @@ def test_prefill_minimal_budget_keeps_sink_and_diagonal():
 # ---------------------------------------------------------------- wide logits
 
 
-def test_prefill_and_decode_with_wide_logits():
-    """Q scaled by 6 spreads each row's logits over tens of units, so the lazily
-    raised running maximum moves inside tiles (rescaling O and l) and most
-    probabilities underflow.  The normaliser must stay exact (lse within 1e-4:
-    the max-raising logic); the output is held to the bound of rounding P to
-    bf16 for the P V MFMAs, 2^-8 max|v| (8 significant bits: with one key
-    holding most of a row's weight the rounding of its P no longer averages
-    out), or 1e-2, whichever is larger."""
+@pytest.mark.parametrize("qmul", [3.0, 4.0, 6.0])
+def test_prefill_with_wide_logits(qmul):
+    """Q scaled by 3-6 makes each row's softmax sharp: one key often holds most
+    of a row's weight and the lazily raised running maximum moves inside tiles
+    (rescaling O and l).  Output within 1e-2 and lse within 1e-4 of the oracle,
+    like every other bf16 case.  The probabilities are rounded to bf16 for the
+    P V MFMAs, and the normaliser sums those same rounded values, so the output
+    stays a convex combination of V rows; lse comes from the unrounded sum."""
     spec = W.LLAMA_32K.with_(seq_len=2048 + 64, n_q_heads=8, n_kv_heads=2)
     inp = W.make_prefill(spec, 71, device=DEV)
-    inp.q = (inp.q.float() * 6.0).to(inp.q.dtype)
+    inp.q = (inp.q.float() * qmul).to(inp.q.dtype)
+    _say("case: prefill wide logits, Q x", qmul)
     idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=32, queue=True)
     q, k, v = to_host(inp)
     gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
     ro, rl = O.attention_prefill_gather(q, k, v, gidx, gcnt, spec.block)
     err, lerr = max_abs(o.cpu().numpy(), ro), max_abs(lse.cpu().numpy(), rl)
-    vmax = float(np.abs(O.to_f64(v)).max())
     _say("prefill wide logits: max abs err o", err, "lse", lerr, "lse range", float(rl.min()), float(rl.max()))
     assert lerr <= 1e-4
-    assert err <= max(TOL_BF16, 2.0 ** -8 * vmax)
+    assert err <= TOL_BF16
+    # the same tiles without lse (the kernel variant that keeps one sum)
+    o2 = torch.empty_like(o)
+    plan.attend(inp.q, inp.k, inp.v, o2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o)
 
+
+@pytest.mark.parametrize("qmul", [3.0, 4.0, 6.0])
+def test_decode_with_wide_logits(qmul):
+    """Decode with Q scaled by 3-6 (sharp softmax): output within 1e-2, lse
+    within 1e-4 of the oracle.  The chunk partials carry both the rounded-P sum
+    (normaliser of o) and the unrounded one (lse)."""
     dspec = W.DECODE_128K.with_(batch=2, kv_len=4096 + 24, tok_lo=256, tok_hi=1024, stream_local=8)
     din = W.make_decode(dspec, 72, device=DEV)
-    din.q = (din.q.float() * 6.0).to(din.q.dtype)
+    din.q = (din.q.float() * qmul).to(din.q.dtype)
+    _say("case: decode wide logits, Q x", qmul)
     dplan, do, dl = _decode_gpu(din)
     gidx, gcnt = dplan.block_idx.cpu().numpy(), dplan.block_cnt.cpu().numpy()
     qd, kd, vd = W.to_numpy(din.q), W.to_numpy(din.k), W.to_numpy(din.v)
     ro, rl = O.decode_attention(qd, kd, vd, gidx, gcnt, din.budget["granularity"])
     err, lerr = max_abs(do.cpu().numpy(), ro), max_abs(dl.cpu().numpy(), rl)
-    vmax = float(np.abs(O.to_f64(vd)).max())
     _say("decode wide logits: max abs err o", err, "lse", lerr)
     assert lerr <= 1e-4
-    assert err <= max(TOL_BF16, 2.0 ** -8 * vmax)
+    assert err <= TOL_BF16

@@ -1,5 +1,6 @@
 """Pins of the calibration oracle (block attention mass, head recovery, max-min
-budget shifting) and the library's host calibration against it.
+budget shifting).  They need no built library: the host library's calibration
+is checked against this oracle in test_abi_calibration.py.
 
 Mass: every row of softmax probabilities sums to one, so row m of the block
 mass sums to the query rows of block m; with Q = 0 every visible key of row t
@@ -18,9 +19,6 @@ import pytest
 import torch
 
 import oracle as O
-
-SA = pytest.importorskip("head_heterogeneous_block_amd.sparse_attn", reason="library not built")
-
 
 def _qk(seed, b=1, H=2, Hk=1, S=300, D=16, scale=1.0):
     r = np.random.default_rng(seed)
@@ -113,29 +111,6 @@ def test_needed_ratio():
 
 def _budget(H, min_blocks=2):
     return {"min_blocks": [min_blocks] * H, "ratio_q16": [0] * H, "n_sink": [1] * H, "n_local": [1] * H}
-
-
-def test_host_recovery_and_shift_match_oracle_bitwise():
-    q, k = _qk(6, b=2, H=4, Hk=2, S=512, D=32, scale=1.5)
-    W32 = O.block_attention_mass(q, k, 64).astype(np.float32)
-    bud = _budget(4)
-    step = 4096
-    got = SA.sa_budget_recovery(W32, bud, step)
-    want = O.recovery_table(W32.astype(np.float64), bud, step)
-    assert np.array_equal(got, want)
-    for per in (step, 4 * step, 8 * step):
-        r_host = SA.sa_budget_shift(got, step, 4 * per)
-        assert r_host.tolist() == O.maxmin_shift(want, 4 * per, step)
-
-
-def test_host_calibration_rejects_bad_arguments():
-    rec = np.ones((3, 16))
-    with pytest.raises(SA.SaError):
-        SA.sa_budget_shift(rec, 4096, 3 * 4096 + 1)  # not a whole number of steps per head
-    with pytest.raises(SA.SaError):
-        SA.sa_budget_shift(rec, 5000, 3 * 5000)  # step does not divide 2^16
-    with pytest.raises(SA.SaError):
-        SA.sa_budget_recovery(np.ones((1, 2, 3, 3), np.float32), _budget(2, min_blocks=1), 4096)
 
 
 # ---------------------------------------------------------------- output deviation (R37)
