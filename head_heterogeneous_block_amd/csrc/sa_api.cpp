@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <queue>
 #include <string>
 #include <utility>
@@ -1060,6 +1061,63 @@ sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* 
                                 size_t workspace_bytes, void* stream) {
   return decode_impl(desc, budgets, q, k, v, nullptr, o, lse, block_idx, block_cnt, kmax, out_f32, workspace,
                      workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free decode
+// The scratch of sa_sparse_attn_decode_noalloc: one fixed array in device
+// memory per GPU, held from the loading of this library's code object on that
+// GPU until the process ends.  In host code the name is only a host-side
+// stand-in: the device address comes from hipGetSymbolAddress, once per device
+// (with that device current), and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[SA_DECODE_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first
+// call on that device).
+sa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_NO_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(SA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+sa_status sa_sparse_attn_decode_noalloc(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* q,
+                                        const void* k, const void* v, void* o, float* lse,
+                                        const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
+                                        int32_t out_f32, void* stream) {
+  sa_status s = check_desc(desc, false);
+  if (s) return s;
+  if ((s = check_budgets(desc, budgets, false))) return s;
+  const size_t need = decode_attn_ws(desc, budgets).total;
+  if (need > size_t(SA_DECODE_SCRATCH_BYTES))
+    return fail(SA_ERR_WORKSPACE, "decode needs %zu bytes of scratch, the fixed array holds %zu", need,
+                size_t(SA_DECODE_SCRATCH_BYTES));
+  if ((s = check_device())) return s;
+  void* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws))) return s;
+  // nothing in the scratch has to start at zero: the plan kernel writes every
+  // atom list and count the attention reads, and every chunk partial is
+  // written before the combine reads it
+  return decode_impl(desc, budgets, q, k, v, nullptr, o, lse, block_idx, block_cnt, kmax, out_f32, ws,
+                     size_t(SA_DECODE_SCRATCH_BYTES), stream);
 }
 
 sa_status sa_sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* q,

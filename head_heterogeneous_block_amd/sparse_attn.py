@@ -35,7 +35,7 @@ EXPORTED = [
     "sa_prefill_block_counts", "sa_decode_block_counts",
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_sparse_attn_prefill_queues",
-    "sa_decode_workspace_size", "sa_sparse_attn_decode",
+    "sa_decode_workspace_size", "sa_sparse_attn_decode", "sa_sparse_attn_decode_noalloc",
     "sa_pool_keys_decode_paged", "sa_sparse_attn_decode_paged",
     "sa_block_attention_mass", "sa_budget_recovery", "sa_budget_shift", "sa_output_deviation",
 ]
@@ -101,6 +101,8 @@ _SIG = {
     "sa_decode_workspace_size": (ctypes.c_size_t, [_descp, _budp, ctypes.c_int32]),
     "sa_sparse_attn_decode": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                ctypes.c_int32, _P, ctypes.c_size_t, _P]),
+    "sa_sparse_attn_decode_noalloc": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, _P, _P, _P, _P,
+                                                       ctypes.c_int32, ctypes.c_int32, _P]),
     "sa_pool_keys_decode_paged": (ctypes.c_int32, [_descp, _budp, _P, ctypes.POINTER(sa_kv_pages), _P, _P]),
     "sa_sparse_attn_decode_paged": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, ctypes.POINTER(sa_kv_pages), _P,
                                                      _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P,
@@ -384,6 +386,15 @@ def sa_sparse_attn_decode(desc: sa_attn_desc, budgets, q, k, v, o, lse, block_id
     _check(_lib.sa_sparse_attn_decode(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                       _ptr(block_idx), _ptr(block_cnt), kmax, 1 if out_f32 else 0, _ptr(workspace),
                                       workspace.numel(), _stream(q)))
+
+
+def sa_sparse_attn_decode_noalloc(desc: sa_attn_desc, budgets, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
+                                  out_f32: bool = False) -> None:
+    """sa_sparse_attn_decode with the library's fixed per-GPU scratch array
+    instead of a workspace (no allocation; calls on one GPU must not overlap)."""
+    _check(_lib.sa_sparse_attn_decode_noalloc(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                              _ptr(lse), _ptr(block_idx), _ptr(block_cnt), kmax,
+                                              1 if out_f32 else 0, _stream(q)))
 
 
 def sa_pool_keys_decode_paged(desc: sa_attn_desc, budgets, k_pages: torch.Tensor, pages: sa_kv_pages,

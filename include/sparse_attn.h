@@ -320,6 +320,29 @@ sa_status sa_sparse_attn_decode(const sa_attn_desc* desc, const sa_head_budget* 
                                 int32_t kmax, int32_t out_f32, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* Size of the fixed scratch array of sa_sparse_attn_decode_noalloc (one per
+ * GPU, held until the process ends): 16 MiB.  The 128K-token, 16-sequence,
+ * 32/8-head decode step needs 6.3 MiB (sa_decode_workspace_size). */
+#define SA_DECODE_SCRATCH_BYTES (16u << 20)
+
+/* sa_sparse_attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It calls no allocating routine; its
+ * scratch is a fixed array of SA_DECODE_SCRATCH_BYTES in device memory, one per
+ * GPU (looked up on the first call on a device, with that device current).
+ * Arguments, layouts and results are those of sa_sparse_attn_decode (same
+ * kernels, bitwise the same output).  Returns SA_ERR_WORKSPACE, before any
+ * launch, when sa_decode_workspace_size(desc, budgets, kmax) exceeds
+ * SA_DECODE_SCRATCH_BYTES.  Every call on one GPU uses that GPU's one array:
+ * calls that overlap on one GPU (several streams or threads at once) race and
+ * must be serialised by the caller.  Nothing in the array needs to start at
+ * zero; it keeps the last call's contents. */
+sa_status sa_sparse_attn_decode_noalloc(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                                        const void* q, const void* k, const void* v, void* o,
+                                        float* lse, const int32_t* block_idx,
+                                        const int32_t* block_cnt, int32_t kmax, int32_t out_f32,
+                                        void* stream);
+
 /* ---------------------------------------------------------------- calibration */
 
 /* Offline calibration of per-head budgets: each head gets the budget that keeps
