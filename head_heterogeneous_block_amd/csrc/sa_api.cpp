@@ -90,7 +90,8 @@ sa_status check_desc(const sa_attn_desc* d, bool prefill) {
   if (d->kv_len < 1) return fail(SA_ERR_INVALID_ARG, "kv_len %d", d->kv_len);
   if (!(d->softmax_scale >= 0.f) || std::isinf(d->softmax_scale))
     return fail(SA_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
-  if (d->kernel_variant != 0) return fail(SA_ERR_INVALID_ARG, "kernel_variant %d (must be 0)", d->kernel_variant);
+  if (d->kernel_variant != 0 && d->kernel_variant != 1)
+    return fail(SA_ERR_INVALID_ARG, "kernel_variant %d (0 or 1)", d->kernel_variant);
   if (prefill) {
     if (d->q_len != d->kv_len) return fail(SA_ERR_INVALID_ARG, "prefill needs q_len == kv_len");
     if (d->block_size != 64 && d->block_size != 128)
@@ -791,7 +792,8 @@ static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const voi
   p.n_queues = n_queues;
   for (int32_t i = 0; i <= n_queues; ++i) p.qoff[i] = queue_offsets ? queue_offsets[i] : (i ? int(n_tiles) : 0);
   const int grid = items_by_bin ? n_bins : int(n_tiles);
-  hipError_t e = sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, grid, (hipStream_t)stream);
+  hipError_t e = sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, desc->kernel_variant, grid,
+                                    (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill kernel launch");
   return ok();
 }

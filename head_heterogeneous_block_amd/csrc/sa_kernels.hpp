@@ -106,9 +106,12 @@ struct PrefillParams {
   int n_queues = 1;
   int qoff[kMaxQueues + 1] = {};
 };
-// workgroup of B/32 waves, 32 queries each; grid = persistent bins, queue
-// workers or tiles
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int grid, hipStream_t stream);
+// grid = persistent bins, queue workers or tiles.  variant 0: the
+// 32-rows-per-wave kernel (B/32 waves); variant 1 (bf16, B = 128): the
+// 64-rows-per-wave kernel (workgroups of 2 waves).
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int variant, int grid,
+                          hipStream_t stream);
+hipError_t launch_prefill_wide(const PrefillParams& p, int D, int grid, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode attention
 // Union of the selected 16-token atoms of the query heads of one KV group.

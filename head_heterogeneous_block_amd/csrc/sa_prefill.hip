@@ -593,7 +593,8 @@ hipError_t launch_t(const PrefillParams& p, int grid, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int grid, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int variant, int grid,
+                          hipStream_t stream) {
   if (p.queue) {
     // a kernel, not a memset, so that the call can be captured in a graph
     if (p.n_queues < 1 || p.n_queues > PrefillParams::kMaxQueues) return hipErrorInvalidValue;
@@ -601,6 +602,7 @@ hipError_t launch_prefill(const PrefillParams& p, int dtype, int D, int B, int g
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (dtype == 0 && B == 128 && variant == 1) return launch_prefill_wide(p, D, grid, stream);
   if (dtype == 0) {
     if (D == 128 && B == 128) return launch_t<bf16_t, 128, 128>(p, grid, stream);
     if (D == 128 && B == 64) return launch_t<bf16_t, 128, 64>(p, grid, stream);

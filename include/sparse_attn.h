@@ -84,7 +84,9 @@ typedef struct {
   int32_t block_size;
   int32_t dtype;
   float softmax_scale;
-  int32_t kernel_variant; /* reserved for alternative kernel shapes; must be 0 */
+  int32_t kernel_variant; /* prefill attention: 0 = 32 query rows per wave (default), 1 = 64
+                             query rows per wave (bf16 with block_size 128; others run 0);
+                             same results up to rounding order */
   int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
 } sa_attn_desc;
 
