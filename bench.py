@@ -50,6 +50,10 @@ def parse():
                          "table and max-min shifting on the host) on the 32K prefill workload")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the decode step over the same cache held in 128-token pages")
+    ap.add_argument("--tail", action="store_true",
+                    help="also measure the schedules' idle tail on the 64K Qwen2.5-72B-shaped layer (the 128K "
+                         "layer is always measured)")
+    ap.add_argument("--no-tail", action="store_true", help="skip the idle-tail measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) so that a "
                          "counter run can scale its HBM byte counters")
@@ -106,6 +110,73 @@ def traffic_from_profiles():
     if rec.get("kernel_source_sha256") != h:
         return None
     return rec.get("bytes_per_launch")
+
+
+def tail_report(spec_name, dev, stream, n_bins, queues):
+    """How well each schedule fills the chip to the end of the prefill
+    attention: one launch per schedule that records every workgroup's start and
+    end on the GPU's constant clock.  busy_w = end_w - start_w; span = last end
+    - first start; tail idle = 1 - sum(busy) / (slots * span) with slots the
+    workgroups the chip runs at once (2 per CU); makespan/mean = max(busy) /
+    mean(busy), beside the value the schedule predicts from the block counts
+    (the loads)."""
+    import numpy as np
+    import torch
+    from head_heterogeneous_block_amd import sparse_attn as SA
+    from head_heterogeneous_block_amd import workloads as W
+    spec = W.BY_NAME[spec_name]
+    inp = W.make_prefill(spec, W.seed_of(spec), device=dev)
+    base = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins, queue=True, queues=queues)
+    base.select(inp.q, inp.k)
+    o = torch.empty_like(inp.q)
+    loads = base.counts.reshape(-1).astype(np.int64)
+    lpt_pred = SA.sa_lpt_schedule(loads.tolist(), n_bins)[3]
+    plans = {
+        "queue_xcd_partitions": (base, float(lpt_pred.max() / lpt_pred.mean())),
+        "queue_one": (SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins, queue=True, queues=1),
+                      float(lpt_pred.max() / lpt_pred.mean())),
+        "lpt_bins": (SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins), None),
+        "natural_grid": (SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=0), None),
+    }
+    out = {"workload": spec.name, "workgroups": n_bins, "slots": n_bins,
+           "predicted_note": "queues: makespan/mean of the LPT schedule of the loads onto the workgroups (the "
+                             "greedy rule the queue runs online); bins: that of the bins themselves"}
+    for name, (pl, pred) in plans.items():
+        if pl is not base:
+            pl.block_idx.copy_(base.block_idx)
+            pl.block_cnt.copy_(base.block_cnt)
+        if name == "lpt_bins":
+            pred = float(pl.bin_load.max() / pl.bin_load.mean())
+        pl.attend(inp.q, inp.k, inp.v, o)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        t = pl.attend_timed(inp.q, inp.k, inp.v, o)
+        b.record(stream)
+        b.synchronize()
+        ms = a.elapsed_time(b)
+        t = t.cpu().numpy().astype(np.float64)
+        t0, t1 = t[:, 0].min(), t[:, 1].max()
+        busy = t[:, 1] - t[:, 0]
+        span = t1 - t0
+        rec = {"ms": ms, "span_ticks": span, "ticks_per_ms": span / ms if ms > 0 else None,
+               "busy_idle_tail": 1.0 - busy.sum() / (n_bins * span)}
+        if name != "natural_grid":
+            rec.update({"busy_ms_p10_p50_p90": [float(np.percentile(busy, q)) / (span / ms) for q in (10, 50, 90)],
+                        "busy_spread": float((busy.max() - busy.min()) / busy.mean()),
+                        "makespan_over_mean_measured": float(busy.max() / busy.mean()),
+                        "makespan_over_mean_predicted": pred,
+                        "last_start_to_end_ms": float((t1 - t[:, 0].max()) / (span / ms))})
+        else:
+            # one workgroup per tile: the chip-wide occupancy over the last tenth of the span
+            late = t0 + 0.9 * span
+            occ = np.clip(np.minimum(t[:, 1], t1) - np.maximum(t[:, 0], late), 0, None).sum() / (n_bins * 0.1 * span)
+            rec.update({"tiles": int(t.shape[0]), "occupancy_last_tenth": float(occ)})
+        out[name] = rec
+        del pl
+    del plans, base, inp
+    torch.cuda.empty_cache()
+    return out
 
 
 def calibration_timing(dev, stream):
@@ -483,6 +554,13 @@ def main():
     }
     if args.calibrate:
         out["calibration"] = calibration_timing(dev, stream)
+    if args.only in ("prefill", "all") and not args.no_tail:
+        del plan
+        torch.cuda.empty_cache()
+        tails = [tail_report(pspec.name, dev, stream, n_bins, args.queues)]
+        if args.tail:
+            tails.append(tail_report("qwen2.5-72b-prefill-64k", dev, stream, n_bins, args.queues))
+        out["tail"] = tails
     print(json.dumps(out))
 
 

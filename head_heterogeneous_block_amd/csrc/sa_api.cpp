@@ -728,7 +728,7 @@ static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const voi
                               float* lse, const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
                               const int32_t* bin_offsets, const int32_t* items_by_bin, int32_t n_bins,
                               const int32_t* queue_offsets, int32_t n_queues, int32_t out_f32, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              size_t workspace_bytes, void* stream, uint64_t* wg_times = nullptr) {
   sa_status s = check_desc(desc, true);
   if (s) return s;
   if (!q || !k || !v || !o || !block_idx || !block_cnt) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
@@ -791,6 +791,9 @@ static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const voi
   p.queue = queue ? static_cast<int*>(workspace) : nullptr;
   p.n_queues = n_queues;
   for (int32_t i = 0; i <= n_queues; ++i) p.qoff[i] = queue_offsets ? queue_offsets[i] : (i ? int(n_tiles) : 0);
+  if (wg_times && (reinterpret_cast<uintptr_t>(wg_times) & 7))
+    return fail(SA_ERR_INVALID_ARG, "wg_times must be 8-byte aligned");
+  p.wg_times = wg_times;
   const int grid = items_by_bin ? n_bins : int(n_tiles);
   hipError_t e = sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, desc->kernel_variant, grid,
                                     (hipStream_t)stream);
@@ -816,6 +819,24 @@ sa_status sa_sparse_attn_prefill_queues(const sa_attn_desc* desc, const void* q,
   if (!queue_offsets || !order) return fail(SA_ERR_INVALID_ARG, "queue_offsets or order is NULL");
   return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, nullptr, order, n_workgroups, queue_offsets,
                       n_queues, out_f32, workspace, workspace_bytes, stream);
+}
+
+sa_status sa_sparse_attn_prefill_timed(const sa_attn_desc* desc, const void* q, const void* k, const void* v,
+                                       void* o, float* lse, const int32_t* block_idx, const int32_t* block_cnt,
+                                       int32_t kmax, const int32_t* bin_offsets, const int32_t* items_by_bin,
+                                       int32_t n_bins, const int32_t* queue_offsets, int32_t n_queues,
+                                       int32_t out_f32, uint64_t* wg_times, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (!wg_times) return fail(SA_ERR_INVALID_ARG, "wg_times is NULL");
+  if (queue_offsets) {
+    if (n_queues < 1 || n_queues > kMaxQueues)
+      return fail(SA_ERR_INVALID_ARG, "n_queues %d outside [1, %d]", n_queues, kMaxQueues);
+    if (!items_by_bin || bin_offsets) return fail(SA_ERR_INVALID_ARG, "queues need items_by_bin and no bin_offsets");
+  } else {
+    n_queues = 1;
+  }
+  return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, bin_offsets, items_by_bin, n_bins,
+                      queue_offsets, n_queues, out_f32, workspace, workspace_bytes, stream, wg_times);
 }
 
 size_t sa_decode_workspace_size(const sa_attn_desc* desc, const sa_head_budget* budgets, int32_t kmax) {

@@ -105,6 +105,9 @@ struct PrefillParams {
   static constexpr int kMaxQueues = 16;
   int n_queues = 1;
   int qoff[kMaxQueues + 1] = {};
+  // nullable: workgroup w writes the constant clock (s_memrealtime) at its
+  // start to wg_times[2 w] and at its end to wg_times[2 w + 1]
+  uint64_t* wg_times = nullptr;
 };
 // grid = persistent bins, queue workers or tiles.  variant 0: the
 // 32-rows-per-wave kernel (B/32 waves); variant 1 (bf16, B = 128): the

@@ -57,6 +57,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   char* const kring = smem;                 // K slots 0, 1
   char* const vring = smem + 2 * C::kTile;  // V slots 0, 1
 
+  wg_stamp(0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -521,7 +522,10 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   cur.item = -1;
   seek(it_beg, 0);
   Step s0 = cur;
-  if (!s0.valid) return;
+  if (!s0.valid) {
+    wg_stamp(1);
+    return;
+  }
   advance();
   Step s1 = cur;
   advance();
@@ -578,6 +582,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   };
   while (iteration(0, sa, sb) && iteration(1, sb, sa)) {
   }
+  wg_stamp(1);
 }
 
 __global__ void queue_reset_kernel(int* counters, int n) {

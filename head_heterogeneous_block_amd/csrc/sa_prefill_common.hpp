@@ -82,6 +82,17 @@ __device__ __forceinline__ F kernel_arg(int offset) {
 }
 #define COLD(field) kernel_arg<decltype(PrefillParams::field)>(offsetof(PrefillParams, field))
 
+// Start (which = 0) or end (1) stamp of this workgroup on the constant clock,
+// when the launch records them: one lane writes it with a vector store.
+__device__ __forceinline__ void wg_stamp(int which) {
+  uint64_t* const t = COLD(wg_times);
+  if (t == nullptr) return;
+  const uint64_t now = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    __builtin_nontemporal_store(now, t + 2 * blockIdx.x + which);
+  }
+}
+
 
 }  // namespace prefill
 }  // namespace sa

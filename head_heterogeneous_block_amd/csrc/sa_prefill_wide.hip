@@ -76,6 +76,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   char* const kring = smem;                    // K slots 0..3
   char* const vring = smem + kWSlots * kTile;  // V slots 0..3
 
+  wg_stamp(0);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -396,7 +397,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // iterations earlier) must have landed while the loads of the last two
   // iterations may stay in flight.
   Step s0 = cs.cur;
-  if (!s0.valid) return;
+  if (!s0.valid) {
+    wg_stamp(1);
+    return;
+  }
   cs.advance();
   Step s1 = cs.cur;
   cs.advance();
@@ -520,6 +524,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
          iteration(2, sB0, sB1, pA0, pA1) && iteration(3, sB1, sB0, pA1, pA0)) {
   }
   wait_vmcnt<0>();  // no load may still write LDS when the workgroup ends
+  wg_stamp(1);
 }
 
 template <int D>

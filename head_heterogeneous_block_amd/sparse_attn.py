@@ -35,6 +35,7 @@ EXPORTED = [
     "sa_prefill_block_counts", "sa_decode_block_counts",
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_sparse_attn_prefill_queues",
+    "sa_sparse_attn_prefill_timed",
     "sa_decode_workspace_size", "sa_sparse_attn_decode", "sa_sparse_attn_decode_noalloc",
     "sa_pool_keys_decode_paged", "sa_sparse_attn_decode_paged",
     "sa_block_attention_mass", "sa_budget_recovery", "sa_budget_shift", "sa_output_deviation",
@@ -98,6 +99,9 @@ _SIG = {
     "sa_sparse_attn_prefill_queues": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _i32p,
                                                        ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P,
                                                        ctypes.c_size_t, _P]),
+    "sa_sparse_attn_prefill_timed": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+                                                      ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                                      ctypes.c_size_t, _P]),
     "sa_decode_workspace_size": (ctypes.c_size_t, [_descp, _budp, ctypes.c_int32]),
     "sa_sparse_attn_decode": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32,
                                                ctypes.c_int32, _P, ctypes.c_size_t, _P]),
@@ -381,6 +385,20 @@ def sa_sparse_attn_prefill_queues(desc: sa_attn_desc, q, k, v, o, lse, block_idx
                                               _ptr(ws), 0 if ws is None else ws.numel(), _stream(q)))
 
 
+def sa_sparse_attn_prefill_timed(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
+                                 bin_offsets, items_by_bin, n_bins: int, queue_offsets: Optional[np.ndarray],
+                                 out_f32: bool, wg_times: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> None:
+    """A prefill launch recording each workgroup's start and end on the constant
+    clock into wg_times (int64 [2 * grid])."""
+    off = None if queue_offsets is None else np.ascontiguousarray(queue_offsets, dtype=np.int32)
+    ws = workspace
+    _check(_lib.sa_sparse_attn_prefill_timed(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(block_idx), _ptr(block_cnt), kmax,
+        _ptr(bin_offsets), _ptr(items_by_bin), n_bins, None if off is None else off.ctypes.data_as(_i32p),
+        0 if off is None else off.size - 1, 1 if out_f32 else 0, _ptr(wg_times), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream(q)))
+
+
 def sa_sparse_attn_decode(desc: sa_attn_desc, budgets, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
                           workspace: torch.Tensor, out_f32: bool = False) -> None:
     _check(_lib.sa_sparse_attn_decode(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -586,6 +604,20 @@ class PrefillPlan:
             return
         sa_sparse_attn_prefill(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
                                self.bin_offsets, self.items_by_bin, self.n_bins, self.out_f32, self.attn_ws)
+
+    def grid(self) -> int:
+        """Workgroups of a launch: the persistent workgroups, or one per tile."""
+        return self.n_bins if self.items_by_bin is not None else int(self.counts.size)
+
+    def attend_timed(self, q, k, v, o, lse=None) -> torch.Tensor:
+        """attend(), also recording each workgroup's start and end on the GPU's
+        constant clock; returns int64 [grid, 2]."""
+        t = torch.zeros((self.grid(), 2), dtype=torch.int64, device=q.device)
+        sa_sparse_attn_prefill_timed(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
+                                     self.bin_offsets, self.items_by_bin, self.n_bins if self.items_by_bin is not None
+                                     else 0, self.queue_offsets if self.queue else None, self.out_f32, t,
+                                     self.attn_ws)
+        return t
 
 
 class DecodePlan:

@@ -307,6 +307,26 @@ sa_status sa_sparse_attn_prefill_queues(const sa_attn_desc* desc, const void* q,
                                         const int32_t* order, int32_t n_workgroups, int32_t out_f32,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* A prefill launch that records when each workgroup ran, to measure how well a
+ * schedule fills the chip to the end (the idle tail that head load balancing
+ * removes: "S-HPLB: Efficient LLM Attention Serving via Sparsity-Aware Head
+ * Parallelism Load Balance", Italian summary §1 and §4).  Arguments as
+ * sa_sparse_attn_prefill (queue_offsets NULL: bins, single queue or natural
+ * order) or as sa_sparse_attn_prefill_queues (queue_offsets and n_queues set,
+ * items_by_bin the order, n_bins the workgroup count).
+ *   wg_times [dev] uint64 [2 * grid], 8-byte aligned, grid = n_bins (bins,
+ *   queues) or the tile count (natural order): workgroup w writes the GPU's
+ *   constant clock (s_memrealtime) when it starts to wg_times[2 w] and when it
+ *   finishes to wg_times[2 w + 1].  The clock's rate is the device's wall-clock
+ *   rate (hipDeviceAttributeWallClockRate). */
+sa_status sa_sparse_attn_prefill_timed(const sa_attn_desc* desc, const void* q, const void* k,
+                                       const void* v, void* o, float* lse, const int32_t* block_idx,
+                                       const int32_t* block_cnt, int32_t kmax,
+                                       const int32_t* bin_offsets, const int32_t* items_by_bin,
+                                       int32_t n_bins, const int32_t* queue_offsets, int32_t n_queues,
+                                       int32_t out_f32, uint64_t* wg_times, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 size_t sa_decode_workspace_size(const sa_attn_desc* desc, const sa_head_budget* budgets,
                                 int32_t kmax);
 
