@@ -54,6 +54,8 @@ def parse():
                     help="also measure the schedules' idle tail on the 64K Qwen2.5-72B-shaped layer (the 128K "
                          "layer is always measured)")
     ap.add_argument("--no-tail", action="store_true", help="skip the idle-tail measurement")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the MFMA and HBM-read rates this GPU sustains")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain elementwise copy of 1 GiB (read 1 GiB, write 1 GiB) so that a "
                          "counter run can scale its HBM byte counters")
@@ -96,6 +98,67 @@ def prefill_kernel_hash() -> str:
         with open(os.path.join(ROOT, "head_heterogeneous_block_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def measured_peaks(dev, stream, reps=7):
+    """The roofline denominators this GPU sustains, from the library's two
+    probes, each checked before its rate is used: the bf16 MFMA rate (8
+    independent 32x32x16 chains per wave, every accumulator ending at an exact
+    value) and the HBM streaming-read rate over a 4 GiB buffer (far beyond L2
+    and the 256 MB MALL; the XOR of the probe's outputs must match that of the
+    buffer).  Best of a few launch shapes, median of `reps` launches each."""
+    import torch
+    from head_heterogeneous_block_amd import sparse_attn as SA
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {}
+    iters = 8192
+    best = None
+    for per_cu in (1, 2):
+        n_wg = n_cu * per_cu
+        sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+        fl = SA.sa_measure_mfma_peak(n_wg, iters, sink)  # warm
+        ms = timed(lambda: SA.sa_measure_mfma_peak(n_wg, iters, sink), stream, reps)[0]
+        if not bool((sink == 128.0 * iters).all()):
+            raise RuntimeError("MFMA probe: wrong accumulator values")
+        rate = fl / (ms * 1e-3) / 1e12
+        if best is None or rate > best[0]:
+            best = (rate, n_wg, ms)
+    out["mfma_bf16_tflops"] = best[0]
+    out["mfma_probe"] = f"{best[1]} workgroups x 4 waves x 8 chains x {iters} v_mfma_f32_32x32x16_bf16, {best[2]:.3f} ms"
+    nbytes = 4 << 30
+    buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev)
+    x = buf
+    while x.numel() > 1:  # XOR fold of the whole buffer on the GPU
+        h = x.numel() // 2
+        x = torch.bitwise_xor(x[:h], x[h:2 * h]) if x.numel() % 2 == 0 else torch.cat(
+            [torch.bitwise_xor(x[:h], x[h:2 * h]), x[2 * h:]])
+    want = int(x.item())
+    del x
+    best = None
+    for per_cu in (4, 8, 16, 32):
+        n_wg = n_cu * per_cu
+        sink = torch.empty(n_wg * 256, dtype=torch.int32, device=dev)
+        SA.sa_measure_hbm_read(buf, n_wg, sink)
+        ms = timed(lambda: SA.sa_measure_hbm_read(buf, n_wg, sink), stream, reps)[0]
+        y = sink
+        while y.numel() > 1:
+            h = y.numel() // 2
+            y = torch.bitwise_xor(y[:h], y[h:2 * h])  # n_wg * 256 is a power of two times n_cu
+            if y.numel() % 2:
+                break
+        got = 0
+        for v in y.cpu().tolist():
+            got ^= v
+        if got != want:
+            raise RuntimeError("HBM read probe: XOR of the outputs does not match the buffer")
+        rate = nbytes / (ms * 1e-3) / 1e9
+        if best is None or rate > best[0]:
+            best = (rate, n_wg, ms)
+    del buf
+    torch.cuda.empty_cache()
+    out["hbm_read_gbps"] = best[0]
+    out["hbm_probe"] = f"4 GiB non-temporal 16-byte reads, {best[1]} workgroups x 256 threads, {best[2]:.3f} ms"
+    return out
 
 
 def traffic_from_profiles():
@@ -413,15 +476,23 @@ def main():
         dbytes = M.decode_bytes(dbidx, dbcnt, din.budget["granularity"], dspec.n_q_heads, dspec.n_kv_heads,
                                 dspec.kv_len, dspec.head_dim, 2, scoring)
 
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks(dev, stream)
+        print(f"[bench] measured peaks: {peaks}", file=sys.stderr, flush=True)
+
     prefill_ms = res.get("sel_ms", 0.0) + res.get("att_ms", 0.0)
     tflops = flops / (res["att_mean_ms"] * 1e-3) / 1e12 if "att_ms" in res else None
     traffic = traffic_from_profiles()
+    pk_mfma = peaks["mfma_bf16_tflops"] if peaks else None
     roofline = {
         "bound": "mfma",
         "achieved": tflops,
         "peak": M.PEAK_BF16_FLOPS / 1e12,
         "unit": "TFLOP/s",
         "frac": tflops / (M.PEAK_BF16_FLOPS / 1e12) if tflops else None,
+        "peak_measured": pk_mfma,
+        "frac_measured": tflops / pk_mfma if tflops and pk_mfma else None,
         "traffic": traffic,
         "kernel": "prefill_kernel (sa_sparse_attn_prefill)",
         "flops_per_launch": flops,
@@ -541,6 +612,7 @@ def main():
                    "step_ms_scrubbed": res.get("dstep_scrub_ms"),
                    "bytes": dbytes, "step_gbps": dgbps,
                    "hbm_frac": dgbps / (M.PEAK_HBM_BYTES / 1e9) if dgbps else None,
+                   "hbm_frac_measured": dgbps / peaks["hbm_read_gbps"] if dgbps and peaks else None,
                    "kv_gbps_attention_kernel": kv_gbps},
         "decode_paged": None if "paged_step_ms" not in res else {
             "page_size": 128, "step_ms": res["paged_step_ms"],
@@ -548,6 +620,7 @@ def main():
             "hbm_frac": dbytes["total"] / (res["paged_step_ms"] * 1e-3) / M.PEAK_HBM_BYTES,
             "same_output_as_contiguous": res["paged_same"]},
         "roofline": roofline,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "cpu_baseline_decode": cpu_dec,
         "ablation": ablation,

@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["sa_api.cpp", "sa_select.hip", "sa_prefill.hip", "sa_prefill_wide.hip", "sa_decode.hip", "sa_calib.hip"]
+SOURCES = ["sa_api.cpp", "sa_select.hip", "sa_prefill.hip", "sa_prefill_wide.hip", "sa_decode.hip", "sa_calib.hip", "sa_peaks.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1152,4 +1152,30 @@ sa_status sa_sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_head_bu
                      workspace, workspace_bytes, stream);
 }
 
+
+sa_status sa_measure_mfma_peak(int32_t n_workgroups, int32_t iters, float* sink, void* stream) {
+  if (!sink) return fail(SA_ERR_INVALID_ARG, "sink is NULL");
+  if (n_workgroups < 1 || n_workgroups > (1 << 20)) return fail(SA_ERR_INVALID_ARG, "n_workgroups %d out of [1, 2^20]", n_workgroups);
+  if (iters < 1 || iters > 65536) return fail(SA_ERR_INVALID_ARG, "iters %d out of [1, 65536]", iters);
+  if (reinterpret_cast<uintptr_t>(sink) & 3) return fail(SA_ERR_INVALID_ARG, "sink must be 4-byte aligned");
+  sa_status s = check_device();
+  if (s) return s;
+  const hipError_t e = sa::launch_mfma_peak(n_workgroups, iters, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mfma peak");
+  return ok();
+}
+
+sa_status sa_measure_hbm_read(const void* buf, int64_t bytes, int32_t n_workgroups, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(SA_ERR_INVALID_ARG, "NULL pointer");
+  if (bytes < 16 || bytes % 16) return fail(SA_ERR_INVALID_ARG, "bytes %lld must be a positive multiple of 16", (long long)bytes);
+  if (n_workgroups < 1 || n_workgroups > (1 << 20)) return fail(SA_ERR_INVALID_ARG, "n_workgroups %d out of [1, 2^20]", n_workgroups);
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3))
+    return fail(SA_ERR_INVALID_ARG, "buf must be 16-byte aligned, sink 4-byte aligned");
+  sa_status s = check_device();
+  if (s) return s;
+  const hipError_t e = sa::launch_hbm_read(buf, bytes, sink, n_workgroups, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hbm read");
+  return ok();
+}
+
 }  // extern "C"

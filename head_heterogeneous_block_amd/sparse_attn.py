@@ -39,6 +39,7 @@ EXPORTED = [
     "sa_decode_workspace_size", "sa_sparse_attn_decode", "sa_sparse_attn_decode_noalloc",
     "sa_pool_keys_decode_paged", "sa_sparse_attn_decode_paged",
     "sa_block_attention_mass", "sa_budget_recovery", "sa_budget_shift", "sa_output_deviation",
+    "sa_measure_mfma_peak", "sa_measure_hbm_read",
 ]
 
 
@@ -118,6 +119,8 @@ _SIG = {
     "sa_output_deviation": (ctypes.c_int32, [_descp, _P, _P, _P, _P]),
     "sa_budget_shift": (ctypes.c_int32, [ctypes.POINTER(ctypes.c_double), ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int64, ctypes.POINTER(ctypes.c_uint32)]),
+    "sa_measure_mfma_peak": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    "sa_measure_hbm_read": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
 }
 for _name, (_res, _args) in _SIG.items():
     _f = getattr(_lib, _name)
@@ -451,6 +454,25 @@ def sa_output_deviation(desc: sa_attn_desc, o_approx: torch.Tensor, o_ref: torch
     if dev.dtype != torch.float64 or dev.numel() < desc.n_q_heads:
         raise ValueError("dev must be a float64 tensor of n_q_heads entries")
     _check(_lib.sa_output_deviation(ctypes.byref(desc), _ptr(o_approx), _ptr(o_ref), _ptr(dev), _stream(o_ref)))
+
+
+def sa_measure_mfma_peak(n_workgroups: int, iters: int, sink: torch.Tensor) -> int:
+    """Launch the bf16 MFMA rate probe on sink's device and stream; returns the
+    flops it does (every sink entry becomes 128 * iters)."""
+    if sink.dtype != torch.float32 or sink.numel() < n_workgroups * 256:
+        raise ValueError("sink must be fp32 with n_workgroups * 256 entries")
+    _check(_lib.sa_measure_mfma_peak(n_workgroups, iters, _ptr(sink), _stream(sink)))
+    return n_workgroups * 4 * 8 * iters * 32768
+
+
+def sa_measure_hbm_read(buf: torch.Tensor, n_workgroups: int, sink: torch.Tensor) -> int:
+    """Launch the HBM streaming-read probe over buf (all of its bytes); returns
+    the bytes read.  The XOR of sink's entries equals that of buf's 32-bit words."""
+    if not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < n_workgroups * 256:
+        raise ValueError("buf must be contiguous, sink int32 with n_workgroups * 256 entries")
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.sa_measure_hbm_read(_ptr(buf), nbytes, n_workgroups, _ptr(sink), _stream(sink)))
+    return nbytes
 
 
 def deviation_table(q, k, v, budget: dict, block: int, step_q16: int, n_bins: int = 512) -> np.ndarray:

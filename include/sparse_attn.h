@@ -465,6 +465,32 @@ sa_status sa_sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_head_bu
                                       int32_t out_f32, void* workspace, size_t workspace_bytes,
                                       void* stream);
 
+
+/* ------------------------------------------------------------ measurement */
+
+/* The bf16 matrix-core rate the GPU sustains: the denominator that the
+ * attention kernels' achieved rate is set beside, next to the published dense
+ * bf16 peak (MI355X: 2.5 PFLOP/s at 2.4 GHz).  n_workgroups workgroups of four
+ * waves; every wave runs 8 independent accumulation chains of iters
+ * v_mfma_f32_32x32x16_bf16 each on operands of ones, so the work is exactly
+ *   n_workgroups * 4 * 8 * iters * 32768 flops
+ * and every accumulator element ends at 16 * iters.
+ *   sink [dev] fp32 [n_workgroups * 256]: each entry 128 * iters (exact), the
+ *        proof the work ran; owned by the caller.
+ * n_workgroups in [1, 1 << 20], iters in [1, 65536]; asynchronous on stream. */
+sa_status sa_measure_mfma_peak(int32_t n_workgroups, int32_t iters, float* sink, void* stream);
+
+/* The HBM streaming-read rate the GPU sustains: the denominator for the
+ * decode path, which reads its selected KV blocks once (published MI355X
+ * peak: 8 TB/s).  Grid-stride 16-byte non-temporal loads of the whole buffer,
+ * n_workgroups workgroups of 256 threads.
+ *   buf  [dev] bytes bytes, 16-byte aligned, bytes a multiple of 16; read only
+ *   sink [dev] uint32 [n_workgroups * 256]: the XOR of all of them equals the
+ *        XOR of every 32-bit word of buf (the proof every byte was read)
+ * n_workgroups in [1, 1 << 20]; asynchronous on stream. */
+sa_status sa_measure_hbm_read(const void* buf, int64_t bytes, int32_t n_workgroups, uint32_t* sink,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

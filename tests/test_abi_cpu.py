@@ -434,3 +434,24 @@ def test_output_deviation_validation():
     if not torch.cuda.is_available():
         assert lib.sa_output_deviation(ctypes.byref(d), fake, fake, fake, None) in (SA.SA_ERR_NO_DEVICE,
                                                                                      SA.SA_ERR_HIP)
+
+
+def test_measure_probes_validation():
+    """The rate probes reject bad sizes and pointers before any launch; valid
+    calls reach the device check."""
+    import torch
+    lib = SA._lib
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.sa_measure_mfma_peak(0, 16, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 0, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 65537, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 16, None, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 16, ctypes.c_void_p((1 << 20) + 2), None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_hbm_read(fake, 100, 256, fake, None) == SA.SA_ERR_INVALID_ARG   # not a multiple of 16
+    assert lib.sa_measure_hbm_read(fake, 0, 256, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_hbm_read(ctypes.c_void_p((1 << 20) + 8), 1 << 20, 256, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_hbm_read(fake, 1 << 20, 0, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_hbm_read(None, 1 << 20, 256, fake, None) == SA.SA_ERR_INVALID_ARG
+    if not torch.cuda.is_available():
+        assert lib.sa_measure_mfma_peak(256, 16, fake, None) in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
+        assert lib.sa_measure_hbm_read(fake, 1 << 20, 256, fake, None) in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
