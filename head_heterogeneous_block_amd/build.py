@@ -8,6 +8,7 @@ shared library next to this file.
 from __future__ import annotations
 
 import concurrent.futures
+import importlib.util
 import os
 import shutil
 import subprocess
@@ -35,9 +36,9 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, obj: str) -> None:
+def _compile(src: str, obj: str, extra=()) -> None:
     lang = ["-x", "hip"]  # sa_api.cpp launches kernels through hip runtime: compile every file as HIP
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -46,21 +47,35 @@ def _compile(src: str, obj: str) -> None:
         sys.stderr.write("\n".join(noise) + "\n")
 
 
-def build(verbose: bool = False) -> str:
-    out_dir = os.path.join(ROOT, "_build")
+def build(verbose: bool = False, sanitize: bool | None = None) -> str:
+    """Compile every source and link the library; returns its path.  With
+    ``sanitize`` (default: SA_SANITIZE=1 in the environment) the host code is
+    built with AddressSanitizer and UndefinedBehaviorSanitizer into
+    libsparse_attn_san.so instead (device code is unchanged); the binding loads
+    that one when SA_SANITIZE=1 (see build_sanitize.py, which also runs the CPU
+    tests under it)."""
+    if sanitize is None:
+        sanitize = os.environ.get("SA_SANITIZE") == "1"
+    extra, link_extra, lib, sub = [], [], LIB, "_build"
+    if sanitize:
+        spec = importlib.util.spec_from_file_location("sa_build_sanitize", os.path.join(HERE, "build_sanitize.py"))
+        san = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(san)
+        extra, link_extra, lib, sub = san.HOST_FLAGS, san.LINK_FLAGS, san.SAN_LIB, os.path.join("_build", "san")
+    out_dir = os.path.join(ROOT, sub)
     os.makedirs(out_dir, exist_ok=True)
     objs = [os.path.join(out_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        list(ex.map(_compile, SOURCES, objs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        list(ex.map(lambda a: _compile(a[0], a[1], extra), zip(SOURCES, objs)))
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

@@ -9,9 +9,11 @@
 
 #include <algorithm>
 #include <atomic>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <queue>
@@ -248,11 +250,92 @@ float scale_of(const sa_attn_desc* d) {
   return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt(float(d->head_dim));
 }
 
+// ---------------------------------------------------------------- debug checks
+// With checks on (SA_DEBUG_CHECKS set to anything but "0" in the environment
+// when the library loads, or sa_set_debug_checks(1)), every attention call
+// first copies the index tables its kernels read back to the host (which
+// synchronises the stream) and rejects the call with SA_ERR_INVALID_ARG if one
+// is out of range.  The kernels themselves skip entries they cannot use, so
+// without the checks a corrupt table gives wrong attention but no fault.
+std::atomic<int> g_debug{[] {
+  const char* e = std::getenv("SA_DEBUG_CHECKS");
+  return (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
+}()};
+
+template <typename T>
+sa_status fetch(std::vector<T>& host, const T* dev, size_t n, hipStream_t st) {
+  host.resize(n);
+  if (n == 0) return ok();
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = hipMemcpy(host.data(), dev, n * sizeof(T), hipMemcpyDeviceToHost);
+  return e == hipSuccess ? ok() : hip_fail(e, "debug check copy");
+}
+
+// rows of ascending block lists: row r holds cnt[r] <= kmax entries, each in
+// [0, limit(r)), strictly increasing (a repeated block would be attended twice)
+template <typename Limit>
+sa_status check_lists(const int32_t* block_idx, const int32_t* block_cnt, int64_t rows, int32_t kmax, Limit limit,
+                      hipStream_t st, const char* what) {
+  std::vector<int32_t> cnt, idx;
+  sa_status s = fetch(cnt, block_cnt, size_t(rows), st);
+  if (s || (s = fetch(idx, block_idx, size_t(rows) * size_t(kmax), st))) return s;
+  for (int64_t r = 0; r < rows; ++r) {
+    const int32_t c = cnt[r];
+    if (c < 0 || c > kmax) return fail(SA_ERR_INVALID_ARG, "%s: block_cnt[%lld] = %d outside [0, %d]", what, (long long)r, c, kmax);
+    const int32_t lim = limit(r);
+    for (int32_t j = 0; j < c; ++j) {
+      const int32_t n = idx[size_t(r) * kmax + j];
+      if (n < 0 || n >= lim)
+        return fail(SA_ERR_INVALID_ARG, "%s: block_idx[%lld][%d] = %d outside [0, %d)", what, (long long)r, j, n, lim);
+      if (j > 0 && n <= idx[size_t(r) * kmax + j - 1])
+        return fail(SA_ERR_INVALID_ARG, "%s: block_idx[%lld] not strictly increasing at %d", what, (long long)r, j);
+    }
+  }
+  return ok();
+}
+
+// items: a permutation of [0, n); offsets (device, n_bins + 1): 0 .. n, non-decreasing
+sa_status check_items(const int32_t* items, const int32_t* offsets, int32_t n_bins, int64_t n, hipStream_t st) {
+  std::vector<int32_t> it, off;
+  sa_status s = fetch(it, items, size_t(n), st);
+  if (s) return s;
+  std::vector<char> seen(size_t(n), 0);
+  for (int64_t i = 0; i < n; ++i) {
+    if (it[i] < 0 || it[i] >= n) return fail(SA_ERR_INVALID_ARG, "items_by_bin[%lld] = %d outside [0, %lld)", (long long)i, it[i], (long long)n);
+    if (seen[it[i]]++) return fail(SA_ERR_INVALID_ARG, "tile %d listed twice in items_by_bin", it[i]);
+  }
+  if (!offsets) return ok();
+  if ((s = fetch(off, offsets, size_t(n_bins) + 1, st))) return s;
+  if (off[0] != 0 || off[n_bins] != n) return fail(SA_ERR_INVALID_ARG, "bin_offsets must run from 0 to %lld", (long long)n);
+  for (int32_t b = 0; b < n_bins; ++b)
+    if (off[b + 1] < off[b]) return fail(SA_ERR_INVALID_ARG, "bin_offsets decrease at bin %d", b);
+  return ok();
+}
+
+// page-table entries of the logical pages that hold cache rows, in [0, pages_per_head)
+sa_status check_table(const sa_attn_desc* d, const sa_kv_pages* pg, hipStream_t st) {
+  std::vector<int32_t> t;
+  const int64_t rows = int64_t(d->batch) * d->n_kv_heads;
+  sa_status s = fetch(t, pg->table, size_t(rows) * size_t(pg->max_pages), st);
+  if (s) return s;
+  const int64_t used = cdiv(d->kv_len, pg->page_size);
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t p = 0; p < used; ++p) {
+      const int32_t e = t[size_t(r) * pg->max_pages + p];
+      if (e < 0 || e >= pg->pages_per_head)
+        return fail(SA_ERR_INVALID_ARG, "page table [%lld][%lld] = %d outside [0, %d)", (long long)(r / d->n_kv_heads),
+                    (long long)p, e, pg->pages_per_head);
+    }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
 
 int32_t sa_version(void) { return 10000; }
+
+int32_t sa_set_debug_checks(int32_t on) { return g_debug.exchange(on ? 1 : 0); }
 
 const char* sa_last_error(void) { return g_err.c_str(); }
 
@@ -462,6 +545,96 @@ sa_status sa_prefill_block_counts(const sa_attn_desc* desc, const sa_head_budget
         km = std::max(km, k);
       }
   if (kmax) *kmax = km;
+  return ok();
+}
+
+sa_status sa_prefill_schedule(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                              const sa_prefill_schedule_opts* opts, int32_t* items, int32_t* offsets,
+                              int32_t* n_offsets, int64_t* bin_load) {
+  if (!opts || !n_offsets) return fail(SA_ERR_INVALID_ARG, "opts or n_offsets is NULL");
+  sa_status st = check_desc(desc, true);
+  if (st) return st;
+  if ((st = check_budgets(desc, budgets, true))) return st;
+  *n_offsets = 0;
+  const sa_prefill_schedule_opts& o = *opts;
+  if (o.kind == SA_SCHED_GRID) return ok();
+  if (o.kind != SA_SCHED_BINS && o.kind != SA_SCHED_BINS_XCD && o.kind != SA_SCHED_QUEUE)
+    return fail(SA_ERR_INVALID_ARG, "schedule kind %d", o.kind);
+  const int32_t nb = int32_t(cdiv(desc->q_len, desc->block_size));
+  const int32_t Hq = desc->n_q_heads, Hkv = desc->n_kv_heads, G = Hq / Hkv;
+  const int64_t n64 = int64_t(desc->batch) * Hq * nb;
+  if (n64 > INT32_MAX) return fail(SA_ERR_INVALID_ARG, "%lld tiles exceed int32", (long long)n64);
+  const int32_t n = int32_t(n64);
+  if (!items || !offsets) return fail(SA_ERR_INVALID_ARG, "items or offsets is NULL");
+  std::vector<int32_t> cnt(n);
+  if ((st = sa_prefill_block_counts(desc, budgets, cnt.data(), nullptr))) return st;
+  std::vector<int64_t> loads(cnt.begin(), cnt.end());
+  // item = (b * Hq + h) * nb + m
+  const auto bh_of = [&](int32_t it) { return it / nb; };
+  if (o.kind == SA_SCHED_QUEUE) {
+    std::vector<int32_t> group(n);
+    switch (o.queue_group) {
+      case SA_QUEUE_KV_TIERS:
+      case SA_QUEUE_KV:
+        for (int32_t it = 0; it < n; ++it) group[it] = bh_of(it) / G;  // (b, KV head) = (b * Hq + h) / G
+        break;
+      case SA_QUEUE_HEAD: {
+        const int32_t n_bh = desc->batch * Hq;
+        std::vector<int64_t> tot(n_bh, 0);
+        for (int32_t it = 0; it < n; ++it) tot[bh_of(it)] += loads[it];
+        std::vector<int32_t> by(n_bh), rank(n_bh);
+        for (int32_t i = 0; i < n_bh; ++i) by[i] = i;
+        std::stable_sort(by.begin(), by.end(), [&](int32_t a, int32_t b) { return tot[a] > tot[b]; });
+        for (int32_t r = 0; r < n_bh; ++r) rank[by[r]] = r;
+        for (int32_t it = 0; it < n; ++it) group[it] = rank[bh_of(it)];
+        break;
+      }
+      case SA_QUEUE_FLAT:
+        break;
+      default:
+        return fail(SA_ERR_INVALID_ARG, "queue_group %d", o.queue_group);
+    }
+    const int32_t* gp = o.queue_group == SA_QUEUE_FLAT ? nullptr : group.data();
+    if (o.queue_group == SA_QUEUE_KV_TIERS && o.n_queues > 1) {
+      if ((st = sa_lpt_queue_partition(loads.data(), gp, n, desc->batch * Hkv, o.n_queues, 4, o.queue_chunk, items,
+                                       offsets)))
+        return st;
+      *n_offsets = o.n_queues + 1;
+      return ok();
+    }
+    if (o.n_queues != 1 && o.n_queues != 0 && o.queue_group != SA_QUEUE_KV_TIERS)
+      return fail(SA_ERR_INVALID_ARG, "n_queues > 1 needs queue_group SA_QUEUE_KV_TIERS");
+    st = o.queue_group == SA_QUEUE_KV_TIERS ? sa_lpt_queue_order_tiered(loads.data(), gp, n, 4, items)
+                                            : sa_lpt_queue_order(loads.data(), gp, n, items);
+    if (st) return st;
+    offsets[0] = 0;
+    offsets[1] = n;
+    *n_offsets = 2;
+    return ok();
+  }
+  // static bins
+  if (o.n_bins < 1) return fail(SA_ERR_INVALID_ARG, "n_bins must be >= 1");
+  if (o.bin_order != 0 && o.bin_order != 1) return fail(SA_ERR_INVALID_ARG, "bin_order %d", o.bin_order);
+  std::vector<int32_t> bin_of(n);
+  if (o.kind == SA_SCHED_BINS_XCD) {
+    if (o.xcd_groups < 1 || o.xcd_chunk < 1) return fail(SA_ERR_INVALID_ARG, "xcd_groups and xcd_chunk must be >= 1");
+    // chunk = (b * Hkv + h / G) * n_m + m / xcd_chunk
+    const int32_t n_m = int32_t(cdiv(nb, o.xcd_chunk));
+    std::vector<int32_t> chunk(n);
+    for (int32_t it = 0; it < n; ++it) {
+      const int32_t bh = bh_of(it), m = it % nb;
+      const int32_t b = bh / Hq, h = bh % Hq;
+      chunk[it] = (b * Hkv + h / G) * n_m + m / o.xcd_chunk;
+    }
+    const int32_t n_chunks = desc->batch * Hkv * n_m;
+    st = sa_lpt_schedule_grouped(loads.data(), chunk.data(), n, n_chunks, o.xcd_groups, o.n_bins, bin_of.data(),
+                                 offsets, items, bin_load);
+  } else {
+    st = sa_lpt_schedule(loads.data(), n, o.n_bins, bin_of.data(), offsets, items, bin_load);
+  }
+  if (st) return st;
+  if (o.bin_order == 0 && (st = sa_lpt_order_bins(offsets, o.n_bins, items))) return st;
+  *n_offsets = o.n_bins + 1;
   return ok();
 }
 
@@ -794,6 +967,13 @@ static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const voi
   if (wg_times && (reinterpret_cast<uintptr_t>(wg_times) & 7))
     return fail(SA_ERR_INVALID_ARG, "wg_times must be 8-byte aligned");
   p.wg_times = wg_times;
+  if (g_debug.load()) {
+    const int NB = int(nb);
+    if ((s = check_lists(block_idx, block_cnt, n_tiles, kmax, [NB](int64_t t) { return int32_t(t % NB) + 1; },
+                         (hipStream_t)stream, "prefill")))
+      return s;
+    if (items_by_bin && (s = check_items(items_by_bin, bin_offsets, n_bins, n_tiles, (hipStream_t)stream))) return s;
+  }
   const int grid = items_by_bin ? n_bins : int(n_tiles);
   hipError_t e = sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, desc->kernel_variant, grid,
                                     (hipStream_t)stream);
@@ -878,6 +1058,13 @@ static sa_status decode_impl(const sa_attn_desc* desc, const sa_head_budget* bud
   }
   if ((s = check_device())) return s;
   hipStream_t st = (hipStream_t)stream;
+  if (g_debug.load()) {
+    const int Hq = desc->n_q_heads, L = desc->kv_len;
+    if ((s = check_lists(block_idx, block_cnt, int64_t(desc->batch) * Hq, kmax,
+                         [&](int64_t r) { return int32_t(cdiv(L, budgets[r % Hq].granularity)); }, st, "decode")))
+      return s;
+    if (pages && (s = check_table(desc, pages, st))) return s;
+  }
   char* ws = static_cast<char*>(workspace);
   uint32_t* atoms = reinterpret_cast<uint32_t*>(ws + w.atoms);
   int32_t* n_union = reinterpret_cast<int32_t*>(ws + w.n_union);

@@ -376,19 +376,6 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     la += s0 + s1;
     if constexpr (kLse) xa += x0 + x1;
   };
-  // O += P(i) V(i) alone (the last step of a tile)
-  auto pv_only = [&](int vslot, const u32x4 (&pac)[2], const u32x4 (&pb)[2]) {
-    const char* vs = vring + vslot * kTile;
-    pause();  // P_B was just written by the VALU
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
-        const u32x4 a = vfrag(vs, kc, dt);
-        mfma_o(oa[dt], a, pac[kc]);
-        mfma_o(ob[dt], a, pb[kc]);
-      }
-  };
 
   // ---------------------------------------------------------------- walk
   // s0 = step i (its P V this iteration), s1 = i+1 (its Q K^T), s2, s3, and

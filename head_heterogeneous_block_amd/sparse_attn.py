@@ -17,7 +17,10 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsparse_attn.so")
+# SA_SANITIZE=1 loads the AddressSanitizer / UBSan build of the host code
+# (build_sanitize.py; needs the sanitizer runtime preloaded)
+LIB_PATH = os.path.join(_HERE, "libsparse_attn_san.so" if os.environ.get("SA_SANITIZE") == "1"
+                        else "libsparse_attn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
@@ -30,9 +33,9 @@ SA_BF16, SA_F32 = 0, 1
 MAX_HEADS = 128
 
 EXPORTED = [
-    "sa_version", "sa_last_error", "sa_lpt_schedule", "sa_lpt_schedule_grouped", "sa_lpt_order_bins",
+    "sa_version", "sa_last_error", "sa_set_debug_checks", "sa_lpt_schedule", "sa_lpt_schedule_grouped", "sa_lpt_order_bins",
     "sa_lpt_queue_order", "sa_lpt_queue_order_tiered", "sa_lpt_queue_partition",
-    "sa_prefill_block_counts", "sa_decode_block_counts",
+    "sa_prefill_block_counts", "sa_decode_block_counts", "sa_prefill_schedule",
     "sa_decode_pooled_size", "sa_pool_keys_decode", "sa_select_workspace_size", "sa_select_blocks",
     "sa_prefill_workspace_size", "sa_sparse_attn_prefill", "sa_sparse_attn_prefill_queues",
     "sa_sparse_attn_prefill_timed",
@@ -65,6 +68,16 @@ class sa_head_budget(ctypes.Structure):
                 ("n_local", ctypes.c_int32), ("granularity", ctypes.c_int32)]
 
 
+class sa_prefill_schedule_opts(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("n_bins", ctypes.c_int32), ("bin_order", ctypes.c_int32),
+                ("xcd_groups", ctypes.c_int32), ("xcd_chunk", ctypes.c_int32), ("queue_group", ctypes.c_int32),
+                ("n_queues", ctypes.c_int32), ("queue_chunk", ctypes.c_int32)]
+
+
+SA_SCHED_GRID, SA_SCHED_BINS, SA_SCHED_BINS_XCD, SA_SCHED_QUEUE = 0, 1, 2, 3
+QUEUE_GROUPS = {"kv_tiers": 0, "kv": 1, "head": 2, "flat": 3}
+
+
 class sa_kv_pages(ctypes.Structure):
     _fields_ = [("table", ctypes.c_void_p), ("page_size", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("pages_per_head", ctypes.c_int32)]
@@ -79,6 +92,7 @@ _budp = ctypes.POINTER(sa_head_budget)
 _SIG = {
     "sa_version": (ctypes.c_int32, []),
     "sa_last_error": (ctypes.c_char_p, []),
+    "sa_set_debug_checks": (ctypes.c_int32, [ctypes.c_int32]),
     "sa_lpt_schedule": (ctypes.c_int32, [_i64p, ctypes.c_int32, ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
     "sa_lpt_order_bins": (ctypes.c_int32, [_i32p, ctypes.c_int32, _i32p]),
     "sa_lpt_queue_order": (ctypes.c_int32, [_i64p, _i32p, ctypes.c_int32, _i32p]),
@@ -89,6 +103,8 @@ _SIG = {
                                                  ctypes.c_int32, _i32p, _i32p, _i32p, _i64p]),
     "sa_prefill_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
     "sa_decode_block_counts": (ctypes.c_int32, [_descp, _budp, _i32p, _i32p]),
+    "sa_prefill_schedule": (ctypes.c_int32, [_descp, _budp, ctypes.POINTER(sa_prefill_schedule_opts), _i32p, _i32p,
+                                             _i32p, _i64p]),
     "sa_decode_pooled_size": (ctypes.c_size_t, [_descp, _budp]),
     "sa_pool_keys_decode": (ctypes.c_int32, [_descp, _budp, _P, _P, _P]),
     "sa_select_workspace_size": (ctypes.c_size_t, [_descp, _budp, ctypes.c_int32]),
@@ -233,6 +249,12 @@ def sa_version() -> int:
     return int(_lib.sa_version())
 
 
+def sa_set_debug_checks(on: bool) -> bool:
+    """Switch the library's host-side index-table checks before every attention
+    launch on or off (process-wide); returns the previous setting."""
+    return bool(_lib.sa_set_debug_checks(1 if on else 0))
+
+
 def sa_lpt_schedule(loads: Sequence[int], n_bins: int):
     """Greedy longest-load-first placement (host).  Returns numpy
     ``(bin_of_item, bin_offsets, items_by_bin, bin_load)``."""
@@ -323,6 +345,31 @@ def sa_prefill_block_counts(desc: sa_attn_desc, budgets) -> tuple[np.ndarray, in
     _check(_lib.sa_prefill_block_counts(ctypes.byref(desc), budgets, counts.ctypes.data_as(_i32p),
                                         ctypes.byref(kmax)))
     return counts, int(kmax.value)
+
+
+def sa_prefill_schedule(desc: sa_attn_desc, budgets, kind: int, n_bins: int = 0, bin_order: int = 0,
+                        xcd_groups: int = 0, xcd_chunk: int = 0, queue_group: int = 0, n_queues: int = 1,
+                        queue_chunk: int = 0):
+    """The host schedule of the prefill tiles: (items, offsets, bin_load) as
+    numpy arrays (bin_load None for the queue; all None for the natural grid)."""
+    opts = sa_prefill_schedule_opts(kind, n_bins, bin_order, xcd_groups, xcd_chunk, queue_group, n_queues,
+                                    queue_chunk)
+    if kind == SA_SCHED_GRID:
+        n_off = ctypes.c_int32(0)
+        _check(_lib.sa_prefill_schedule(ctypes.byref(desc), budgets, ctypes.byref(opts), None, None,
+                                        ctypes.byref(n_off), None))
+        return None, None, None
+    nb = -(-desc.q_len // desc.block_size)
+    n = desc.batch * desc.n_q_heads * nb
+    items = np.zeros(max(n, 1), dtype=np.int32)
+    offsets = np.zeros(max(n_bins, n_queues, 1) + 1, dtype=np.int32)
+    is_bins = kind in (SA_SCHED_BINS, SA_SCHED_BINS_XCD)
+    load = np.zeros(max(n_bins, 1), dtype=np.int64) if is_bins else None
+    n_off = ctypes.c_int32(0)
+    _check(_lib.sa_prefill_schedule(ctypes.byref(desc), budgets, ctypes.byref(opts), items.ctypes.data_as(_i32p),
+                                    offsets.ctypes.data_as(_i32p), ctypes.byref(n_off),
+                                    load.ctypes.data_as(_i64p) if is_bins else None))
+    return items[:n], offsets[:n_off.value], load
 
 
 def sa_decode_block_counts(desc: sa_attn_desc, budgets) -> tuple[np.ndarray, int]:
@@ -552,67 +599,30 @@ class PrefillPlan:
         self.attn_ws = _workspace(sa_prefill_workspace_size(self.desc, self.kmax, n_bins), dev)
         self.queue = queue
         self.queue_offsets = None
+        self.bin_load = None
+        self.bin_offsets = self.items_by_bin = None
         if queue:
             if n_bins < 1:
                 raise ValueError("the work queue needs n_bins >= 1 workgroups")
-            # item = (b * Hq + h) * NB + m
-            G = q.shape[1] // k.shape[1]
-            bh = np.arange(self.counts.size, dtype=np.int64) // self.nb
-            if queue_group == "kv":
-                # grouped by (b, KV head) = (b * Hq + h) // G
-                group = (bh // G).astype(np.int32)
-            elif queue_group == "kv_tiers":
-                # load tiers of a quarter octave, heaviest tier first, grouped by
-                # (b, KV head) inside a tier: the longest tiles still open the
-                # queue (the greedy tail) and tiles in flight share a KV head
-                group = (bh // G).astype(np.int32)
-            elif queue_group == "flat":
-                group = None
-            elif queue_group == "head":
-                # grouped by (b, query head), the heads with the largest total
-                # load first, so the lightest head's short tiles end the queue
-                tot = self.counts.reshape(-1, self.nb).sum(axis=1)
-                rank = np.empty(tot.size, dtype=np.int64)
-                rank[np.argsort(-tot, kind="stable")] = np.arange(tot.size)
-                group = rank[bh].astype(np.int32)
-            else:
+            if queue_group not in QUEUE_GROUPS:
                 raise ValueError(f"queue_group {queue_group!r}")
-            if queues > 1 and queue_group == "kv_tiers":
-                n_groups = q.shape[0] * k.shape[1]
-                order, self.queue_offsets = sa_lpt_queue_partition(self.counts.reshape(-1), group, n_groups, queues,
-                                                                   4, queue_chunk)
-            elif queue_group == "kv_tiers":
-                order = sa_lpt_queue_order_tiered(self.counts.reshape(-1), group, 4)
-            else:
-                order = sa_lpt_queue_order(self.counts.reshape(-1), group)
-            self.bin_load = None
-            self.bin_offsets = None
-            self.items_by_bin = torch.from_numpy(order).to(dev)
+            nq = queues if queue_group == "kv_tiers" else 1
+            items, off, _ = sa_prefill_schedule(self.desc, self.budgets, SA_SCHED_QUEUE,
+                                                queue_group=QUEUE_GROUPS[queue_group], n_queues=nq,
+                                                queue_chunk=queue_chunk)
+            if nq > 1:
+                self.queue_offsets = off
+            self.items_by_bin = torch.from_numpy(items).to(dev)
         elif n_bins > 0:
-            loads = self.counts.reshape(-1)
-            if xcd_groups > 0:
-                # item = (b * Hq + h) * NB + m; chunk = ((b * Hkv + h / G) * n_m + m / xcd_chunk)
-                Hq, Hkv = q.shape[1], k.shape[1]
-                it = np.arange(loads.size)
-                m = it % self.nb
-                bh = it // self.nb
-                b, h = bh // Hq, bh % Hq
-                n_m = -(-self.nb // xcd_chunk)
-                chunk = ((b * Hkv + h // (Hq // Hkv)) * n_m + m // xcd_chunk).astype(np.int32)
-                _, off, items, load = sa_lpt_schedule_grouped(loads, chunk, int(chunk.max()) + 1 if chunk.size else 1,
-                                                              xcd_groups, n_bins)
-            else:
-                _, off, items, load = sa_lpt_schedule(loads, n_bins)
-            if bin_order == "index":
-                items = sa_lpt_order_bins(off, items)
-            elif bin_order != "lpt":
+            if bin_order not in ("index", "lpt"):
                 raise ValueError(bin_order)
+            items, off, load = sa_prefill_schedule(self.desc, self.budgets,
+                                                   SA_SCHED_BINS_XCD if xcd_groups > 0 else SA_SCHED_BINS,
+                                                   n_bins=n_bins, bin_order=0 if bin_order == "index" else 1,
+                                                   xcd_groups=xcd_groups, xcd_chunk=xcd_chunk)
             self.bin_load = load
             self.bin_offsets = torch.from_numpy(off).to(dev)
             self.items_by_bin = torch.from_numpy(items).to(dev)
-        else:
-            self.bin_load = None
-            self.bin_offsets = self.items_by_bin = None
 
     def select(self, q, k) -> None:
         sa_select_blocks(self.desc, self.budgets, q, k, None, self.block_idx, self.block_cnt, self.kmax,

@@ -111,6 +111,19 @@ int32_t sa_version(void);
  * next call on this thread. */
 const char* sa_last_error(void);
 
+/* Host-side checks of the index tables before every attention launch:
+ * block_idx / block_cnt (counts in [0, kmax]; entries strictly increasing,
+ * prefill in [0, m], decode in [0, ceil(kv_len / granularity))), the prefill
+ * schedule (items_by_bin a permutation of the tiles, bin offsets from 0 to the
+ * tile count, non-decreasing) and, for paged decode, the page-table entries of
+ * the pages in use (in [0, pages_per_head)).  A failed check returns
+ * SA_ERR_INVALID_ARG with the first bad entry in sa_last_error, and nothing is
+ * launched.  The checks copy the tables to the host after synchronising the
+ * stream, so they are for debugging, not for the timed path.  Off by default;
+ * on when SA_DEBUG_CHECKS is set (and not "0") in the environment when the
+ * library loads.  Returns the previous setting; process-wide. */
+int32_t sa_set_debug_checks(int32_t on);
+
 /* ---------------------------------------------------------------- host-only */
 
 /* Greedy longest-load-first placement (host, synchronous, O(n log n + n log
@@ -259,6 +272,53 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
                            const void* q, const void* k, const float* k_pooled,
                            int32_t* block_idx, int32_t* block_cnt, int32_t kmax,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole host schedule of a prefill layer's attention tiles in one call
+ * (host, synchronous): block counts from the budgets (the tile loads), the
+ * group keys, and the placement, using the calls above.  Tile item =
+ * (b * n_q_heads + h) * n_blocks + m, n_tiles = batch * n_q_heads * n_blocks.
+ *   kind SA_SCHED_GRID: one workgroup per tile in natural order; nothing is
+ *        written (*n_offsets = 0).
+ *   kind SA_SCHED_BINS: sa_lpt_schedule of the loads onto n_bins bins.
+ *   kind SA_SCHED_BINS_XCD: sa_lpt_schedule_grouped: chunks of xcd_chunk
+ *        query blocks of one (sequence, KV head) onto xcd_groups cache
+ *        partitions, then the greedy rule inside each (n_bins a multiple of
+ *        xcd_groups).
+ *   Bins (both kinds) are walked in ascending item order (bin_order 0,
+ *   sa_lpt_order_bins) or in assignment order (1).
+ *   kind SA_SCHED_QUEUE: one order for the work queue, by queue_group:
+ *     SA_QUEUE_KV_TIERS  load tiers of a quarter octave, heaviest first,
+ *                        grouped by (sequence, KV head) inside a tier; with
+ *                        n_queues > 1 cut into that many partitions
+ *                        (sa_lpt_queue_partition, runs of at most queue_chunk
+ *                        tiles, 0 = no limit);
+ *     SA_QUEUE_KV        grouped by (sequence, KV head), longest first inside;
+ *     SA_QUEUE_HEAD      grouped by (sequence, query head), the head with the
+ *                        largest total load first (lower index on ties),
+ *                        longest first inside;
+ *     SA_QUEUE_FLAT      longest first.
+ *   items    [host] int32 [n_tiles] out (kinds other than GRID)
+ *   offsets  [host] int32 out: bins: [n_bins + 1] bin offsets; queue:
+ *            [n_queues + 1] partition offsets (n_queues 1 unless KV_TIERS)
+ *   n_offsets [host] out: entries written to offsets
+ *   bin_load [host] int64 [n_bins] out, bins only (may be NULL)
+ * Sizes outside their ranges are SA_ERR_INVALID_ARG. */
+enum { SA_SCHED_GRID = 0, SA_SCHED_BINS = 1, SA_SCHED_BINS_XCD = 2, SA_SCHED_QUEUE = 3 };
+enum { SA_QUEUE_KV_TIERS = 0, SA_QUEUE_KV = 1, SA_QUEUE_HEAD = 2, SA_QUEUE_FLAT = 3 };
+typedef struct {
+  int32_t kind;
+  int32_t n_bins;       /* bins: number of bins (>= 1) */
+  int32_t bin_order;    /* bins: 0 item order, 1 assignment order */
+  int32_t xcd_groups;   /* SA_SCHED_BINS_XCD: cache partitions */
+  int32_t xcd_chunk;    /* SA_SCHED_BINS_XCD: query blocks per chunk */
+  int32_t queue_group;  /* SA_SCHED_QUEUE: SA_QUEUE_* */
+  int32_t n_queues;     /* SA_SCHED_QUEUE with SA_QUEUE_KV_TIERS: 1 .. 16 */
+  int32_t queue_chunk;  /* SA_SCHED_QUEUE with SA_QUEUE_KV_TIERS: run length limit */
+} sa_prefill_schedule_opts;
+
+sa_status sa_prefill_schedule(const sa_attn_desc* desc, const sa_head_budget* budgets,
+                              const sa_prefill_schedule_opts* opts, int32_t* items, int32_t* offsets,
+                              int32_t* n_offsets, int64_t* bin_load);
 
 /* ---------------------------------------------------------------- attention */
 

@@ -11,3 +11,4 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: larger CPU oracle cases")
+    config.addinivalue_line("markers", "sanitize: builds the ASan/UBSan host library and reruns the CPU tier on it")

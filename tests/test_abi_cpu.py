@@ -455,3 +455,90 @@ def test_measure_probes_validation():
     if not torch.cuda.is_available():
         assert lib.sa_measure_mfma_peak(256, 16, fake, None) in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
         assert lib.sa_measure_hbm_read(fake, 1 << 20, 256, fake, None) in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
+
+
+def _sched_case(seed):
+    """A batch-2, 8-query-head, 2-KV-head prefill descriptor with per-head
+    budgets, its tile loads (the oracle's budget rule) and group keys."""
+    import torch
+    rng = np.random.default_rng(seed)
+    S, Hq, Hkv, blk = 64 * 37, 8, 2, 64
+    q = torch.empty((2, Hq, S, 64), dtype=torch.bfloat16, device="meta")
+    k = torch.empty((2, Hkv, S, 64), dtype=torch.bfloat16, device="meta")
+    d = SA.make_prefill_desc(q, k, k, q, blk)
+    bud = {"min_blocks": [2] * Hq, "ratio_q16": [int(x) for x in rng.integers(1000, 40000, Hq)],
+           "n_sink": [1] * Hq, "n_local": [1] * Hq, "granularity": [blk] * Hq}
+    nb = -(-S // blk)
+    loads = np.array([O.budget_blocks(m + 1, 2, bud["ratio_q16"][h]) for b in range(2) for h in range(Hq)
+                      for m in range(nb)], dtype=np.int64)
+    bh = np.arange(loads.size) // nb
+    return d, SA.make_budgets(bud), loads, bh, nb, Hq, Hkv
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_prefill_schedule_bins(seed):
+    """sa_prefill_schedule's bins are the greedy placement of the budget rule's
+    tile loads (the oracle's LPT), walked in item or assignment order, and the
+    two-level form equals sa_lpt_schedule_grouped on (sequence, KV head, chunk)
+    keys written out here from their definition."""
+    d, b, loads, bh, nb, Hq, Hkv = _sched_case(seed)
+    for n_bins in (1, 7, 64):
+        items, off, load = SA.sa_prefill_schedule(d, b, SA.SA_SCHED_BINS, n_bins=n_bins, bin_order=1)
+        _, w_off, w_items, w_load = O.lpt_schedule(loads.tolist(), n_bins)
+        assert load.tolist() == w_load.tolist()
+        assert off.tolist() == w_off.tolist() and items.tolist() == w_items.tolist()
+        items0, off0, _ = SA.sa_prefill_schedule(d, b, SA.SA_SCHED_BINS, n_bins=n_bins, bin_order=0)
+        assert off0.tolist() == off.tolist()
+        for bn in range(n_bins):
+            assert items0[off[bn]:off[bn + 1]].tolist() == sorted(items[off[bn]:off[bn + 1]].tolist())
+    G = Hq // Hkv
+    chunk_len = 8
+    n_m = -(-nb // chunk_len)
+    it = np.arange(loads.size)
+    bb, hh, mm = bh // Hq, bh % Hq, it % nb
+    chunk = ((bb * Hkv + hh // G) * n_m + mm // chunk_len).astype(np.int32)
+    _, off_w, items_w, load_w = SA.sa_lpt_schedule_grouped(loads, chunk, int(chunk.max()) + 1, 4, 16)
+    items, off, load = SA.sa_prefill_schedule(d, b, SA.SA_SCHED_BINS_XCD, n_bins=16, bin_order=1, xcd_groups=4,
+                                              xcd_chunk=chunk_len)
+    assert items.tolist() == items_w.tolist() and off.tolist() == off_w.tolist() and load.tolist() == load_w.tolist()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_prefill_schedule_queue(seed):
+    """The queue orders: KV-tier order and partitions equal the calls they
+    name on (sequence, KV head) keys; the "head" order puts heads in
+    non-increasing total load, each head's tiles together, longest first."""
+    d, b, loads, bh, nb, Hq, Hkv = _sched_case(seed)
+    G = Hq // Hkv
+    kv = (bh // G).astype(np.int32)
+    items, off, load = SA.sa_prefill_schedule(d, b, SA.SA_SCHED_QUEUE, queue_group=0, n_queues=1)
+    assert load is None and off.tolist() == [0, loads.size]
+    assert items.tolist() == SA.sa_lpt_queue_order_tiered(loads, kv, 4).tolist()
+    items, off, _ = SA.sa_prefill_schedule(d, b, SA.SA_SCHED_QUEUE, queue_group=0, n_queues=8, queue_chunk=5)
+    w_items, w_off = SA.sa_lpt_queue_partition(loads, kv, 2 * Hkv, 8, 4, 5)
+    assert items.tolist() == w_items.tolist() and off.tolist() == w_off.tolist()
+    items, _, _ = SA.sa_prefill_schedule(d, b, SA.SA_SCHED_QUEUE, queue_group=1)
+    assert items.tolist() == SA.sa_lpt_queue_order(loads, kv).tolist()
+    items, _, _ = SA.sa_prefill_schedule(d, b, SA.SA_SCHED_QUEUE, queue_group=3)
+    assert items.tolist() == SA.sa_lpt_queue_order(loads, None).tolist()
+    items, _, _ = SA.sa_prefill_schedule(d, b, SA.SA_SCHED_QUEUE, queue_group=2)
+    heads = bh[items]
+    tot = np.bincount(bh, weights=loads)
+    runs = [heads[0]] + [heads[i] for i in range(1, heads.size) if heads[i] != heads[i - 1]]
+    assert len(runs) == tot.size  # each head's tiles are contiguous
+    assert all(tot[runs[i]] >= tot[runs[i + 1]] for i in range(len(runs) - 1))
+    for h in runs:
+        seg = loads[items[heads == h]]
+        assert np.all(seg[:-1] >= seg[1:])
+
+
+def test_prefill_schedule_validation():
+    d, b, *_ = _sched_case(0)
+    for kw in (dict(kind=9), dict(kind=SA.SA_SCHED_BINS, n_bins=0), dict(kind=SA.SA_SCHED_BINS_XCD, n_bins=6,
+                                                                         xcd_groups=4, xcd_chunk=8),
+               dict(kind=SA.SA_SCHED_BINS, n_bins=4, bin_order=2), dict(kind=SA.SA_SCHED_QUEUE, queue_group=7),
+               dict(kind=SA.SA_SCHED_QUEUE, queue_group=1, n_queues=4),
+               dict(kind=SA.SA_SCHED_QUEUE, queue_group=0, n_queues=17)):
+        with pytest.raises(SA.SaError):
+            SA.sa_prefill_schedule(d, b, **kw)
+    assert SA.sa_prefill_schedule(d, b, SA.SA_SCHED_GRID) == (None, None, None)
