@@ -183,16 +183,15 @@ size_t pooled_elems(const sa_attn_desc* d, int g) {
 }
 
 // ---- workspace layouts
+// prefill: the pooled keys only (query pooling, scores and top-k share one kernel)
 struct PrefillSelectWs {
-  size_t qpool, kpool, scores, total;
+  size_t kpool, total;
 };
 PrefillSelectWs prefill_select_ws(const sa_attn_desc* d) {
   const size_t nb = cdiv(d->q_len, d->block_size);
   PrefillSelectWs w;
-  w.qpool = 0;
-  w.kpool = w.qpool + align256(size_t(d->batch) * d->n_q_heads * nb * d->head_dim * 4);
-  w.scores = w.kpool + align256(size_t(d->batch) * d->n_kv_heads * nb * d->head_dim * 4);
-  w.total = w.scores + align256(size_t(d->batch) * d->n_q_heads * nb * nb * 4);
+  w.kpool = 0;
+  w.total = align256(size_t(d->batch) * d->n_kv_heads * nb * d->head_dim * 4);
   return w;
 }
 
@@ -764,6 +763,9 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
     sa_decode_block_counts(desc, budgets, nullptr, &need);
   }
   if (kmax < need) return fail(SA_ERR_INVALID_ARG, "kmax %d < largest block count %d", kmax, need);
+  if (prefill && cdiv(desc->q_len, desc->block_size) > sa::kSelMaxBlocks)
+    return fail(SA_ERR_UNSUPPORTED, "%lld query blocks > %d", (long long)cdiv(desc->q_len, desc->block_size),
+                sa::kSelMaxBlocks);
   const size_t ws_need = prefill ? prefill_select_ws(desc).total : decode_select_ws(desc, budgets, !k_pooled).total;
   if (!workspace || workspace_bytes < ws_need)
     return fail(SA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws_need, workspace_bytes);
@@ -785,21 +787,12 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
   if (prefill) {
     const PrefillSelectWs w = prefill_select_ws(desc);
     const int nb = int(cdiv(desc->q_len, desc->block_size));
-    float* qp = reinterpret_cast<float*>(ws + w.qpool);
     float* kp = reinterpret_cast<float*>(ws + w.kpool);
-    float* sc = reinterpret_cast<float*>(ws + w.scores);
     sa::PoolParams pp{};
     pp.g = desc->block_size;
     pp.nb = nb;
-    pp.T = desc->q_len;
+    pp.T = desc->kv_len;
     pp.blocks_per_wg = 1;
-    pp.x = q;
-    pp.s0 = desc->q_stride[0];
-    pp.s1 = desc->q_stride[1];
-    pp.s2 = desc->q_stride[2];
-    pp.out = qp;
-    pp.heads = desc->n_q_heads;
-    if ((e = sa::launch_pool(pp, desc->dtype, D, desc->batch, st)) != hipSuccess) return hip_fail(e, "pool Q");
     pp.x = k;
     pp.s0 = desc->k_stride[0];
     pp.s1 = desc->k_stride[1];
@@ -807,21 +800,26 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
     pp.out = kp;
     pp.heads = desc->n_kv_heads;
     if ((e = sa::launch_pool(pp, desc->dtype, D, desc->batch, st)) != hipSuccess) return hip_fail(e, "pool K");
-    sa::PrefillScoreParams sp{};
-    sp.qp = qp;
+    sa::PrefillSelectParams sp{};
+    sp.q = q;
+    sp.qs0 = desc->q_stride[0];
+    sp.qs1 = desc->q_stride[1];
+    sp.qs2 = desc->q_stride[2];
     sp.kp = kp;
-    sp.s = sc;
+    sp.idx = block_idx;
+    sp.cnt = block_cnt;
+    sp.kmax = kmax;
     sp.Hq = desc->n_q_heads;
     sp.G = G;
+    sp.S = desc->q_len;
     sp.NB = nb;
+    sp.R = sa::sel_rows(nb);
+    sp.rowlen = sa::sel_rowlen(nb);
+    sp.n_mg = int(cdiv(nb, sp.R));
     sp.scale = scale;
-    if ((e = sa::launch_prefill_scores(sp, D, desc->batch, st)) != hipSuccess) return hip_fail(e, "block scores");
-    tp.s = sc;
-    tp.s_row = nb;
-    tp.rows = desc->batch * desc->n_q_heads * nb;
-    tp.mode = 0;
-    tp.NB = nb;
-    if ((e = sa::launch_topk(tp, nb, st)) != hipSuccess) return hip_fail(e, "top-k");
+    sp.heads = tp.heads;
+    if ((e = sa::launch_select_prefill(sp, desc->dtype, D, desc->block_size, desc->batch, st)) != hipSuccess)
+      return hip_fail(e, "prefill selection");
     return ok();
   }
   // decode
@@ -884,7 +882,6 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
   tp.s = sc;
   tp.s_row = w.nc_max;
   tp.rows = desc->batch * desc->n_q_heads;
-  tp.mode = 1;
   tp.kv_len = desc->kv_len;
   if ((e = sa::launch_topk(tp, w.nc_max, st)) != hipSuccess) return hip_fail(e, "decode top-k");
   return ok();

@@ -37,14 +37,35 @@ struct PoolParams {
 hipError_t launch_pool(const PoolParams& p, int dtype, int D, int batch, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill selection
-struct PrefillScoreParams {
-  const float* qp;  // [batch*Hq][NB][D]
-  const float* kp;  // [batch*Hkv][NB][D]
-  float* s;         // [batch*Hq][NB][NB]
-  int Hq, G, NB;
+// Pool + score + top-k in one kernel: a workgroup takes up to kSelRows
+// consecutive query blocks of one (sequence, query head); their scores against
+// the causal pooled keys live in LDS, rows padded to sel_rowlen floats.
+constexpr int kSelRows = 16;
+constexpr int kSelFloats = kSelRows * (1024 + 32 + 4);
+constexpr int kSelMaxBlocks = 8192;
+__host__ __device__ inline int sel_rowlen(int nb) {
+  const int nbp = (nb + 63) & ~63;
+  return nbp + nbp / 32 + 4;  // one pad float per 32 (top-k reads), + 4 (MFMA row stores)
+}
+__host__ __device__ inline int sel_rows(int nb) {
+  const int r = kSelFloats / sel_rowlen(nb);
+  return r < kSelRows ? r : kSelRows;
+}
+struct PrefillSelectParams {
+  const void* q;      // [batch][Hq][S][D] (strided, D contiguous), dtype bf16 or fp32
+  int64_t qs0, qs1, qs2;
+  const float* kp;    // pooled keys [batch*Hkv][NB][D]
+  int32_t* idx;       // out: [batch*Hq*NB][kmax]
+  int32_t* cnt;       // out: [batch*Hq*NB]
+  int kmax;
+  int Hq, G, S, NB;
+  int R, rowlen, n_mg;  // rows per workgroup, LDS row length, workgroups per (sequence, head)
   float scale;
+  HeadTable heads;
 };
-hipError_t launch_prefill_scores(const PrefillScoreParams& p, int D, int batch, hipStream_t stream);
+// grid: batch * Hq * n_mg workgroups of 256 threads; block 64 or 128, D 64 or 128
+hipError_t launch_select_prefill(const PrefillSelectParams& p, int dtype, int D, int block, int batch,
+                                 hipStream_t stream);
 
 struct TopkParams {
   const float* s;       // scores; row r at s + r * s_row
@@ -53,9 +74,8 @@ struct TopkParams {
   int32_t* cnt;         // out: [rows]
   int kmax;
   int rows;
-  int mode;             // 0: prefill rows (bh, m): candidates m+1; 1: decode rows (b, h)
-  int Hq, NB;           // prefill: rows = batch*Hq*NB
-  int kv_len;           // decode
+  int Hq;               // rows (b, h) = b * Hq + h
+  int kv_len;
   HeadTable heads;
 };
 hipError_t launch_topk(const TopkParams& p, int max_cand, hipStream_t stream);

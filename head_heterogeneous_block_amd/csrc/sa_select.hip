@@ -59,18 +59,29 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     float acc[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) acc[e] = 0.f;
-    for (int r = rg; r < cnt; r += kRG) {
-      // read once: non-temporal, so the rows are not kept in the caches
-      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(lo + r) * rs + ch * 16));
-      if constexpr (sizeof(T) == 2) {
+    // eight rows' loads in flight per thread, then summed in row order (rows
+    // past the block end read as zeros, which leave the sums unchanged)
+    for (int r0 = rg; r0 < cnt; r0 += 8 * kRG) {
+      u32x4 w[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf16_lo(w[e]);
-          acc[2 * e + 1] += bf16_hi(w[e]);
+      for (int u = 0; u < 8; ++u) {
+        const int r = r0 + u * kRG;
+        // read once: non-temporal, so the rows are not kept in the caches
+        w[u] = r < cnt ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (int64_t)(lo + r) * rs + ch * 16))
+                       : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += bf16_lo(w[u][e]);
+            acc[2 * e + 1] += bf16_hi(w[u][e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[u][e]);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[e]);
       }
     }
 #pragma unroll
@@ -86,83 +97,343 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   }
 }
 
-// ---------------------------------------------------------------- prefill block scores
-// s[bh][m][n] = scale * <Qbar[bh][m], Kbar[bkv][n]> for the causal 128x128
-// tiles, in fp32 on the MFMA pipe (v_mfma_f32_32x32x2f32; each wave one 64x64
-// quadrant as 2x2 MFMA tiles).  fp32 keeps the scores exact enough for the
-// 1e-4 relative gaps the selection is checked against.  Qbar and Kbar rows are
-// staged through LDS in 32-wide d chunks, shared by the four waves.
-constexpr int kScoreTile = 128;
+// ---------------------------------------------------------------- prefill selection
+// One kernel per selection: pooling of the query blocks, their scores against
+// the pooled keys, and the per-row top-k, with nothing between the steps
+// leaving the chip (the scores of a workgroup's rows live in LDS).
+//
+// Workgroup = up to R consecutive query blocks m0 .. m0+R-1 of one (sequence,
+// query head) (R = 16 for up to 1024 blocks, fewer for longer sequences so the
+// rows fit in LDS); the workgroups of the last query blocks, which score the
+// most keys, start first.
+//   1. pool: the R blocks' rows of Q, summed in fp32 (16-byte non-temporal
+//      loads, two blocks' loads in flight per thread), divided by the row
+//      count: the block means Qbar, in LDS;
+//   2. score: S[r][n] = scale * <Qbar[r], Kbar[n]> for n < m0 + R on the fp32
+//      MFMA pipe (v_mfma_f32_16x16x4f32: A = the 16 rows of Qbar, held in
+//      registers; B = 16 pooled keys read from L2; lane group g of the wave
+//      takes channels [g D/4, (g+1) D/4), so each MFMA consumes 4 channels and
+//      D/4 of them cover the dot product).  fp32 keeps the scores exact enough
+//      for the 1e-4 relative gaps the selection is checked against;
+//   3. top-k: wave w takes rows w, w+4, ...: the exact radix select of the
+//      key bytes (below), reading the row's keys from LDS.
+// Exact top-k of one row of scores by one wave (the Select step's per-row
+// budget): forced candidates ([0, ns) and [nl_lo, n_cand)) are kept, and kk of
+// the others are picked, the largest keys (order-preserving maps of the
+// scores), ties to the lowest index.  Lane l owns candidates [l cpt, (l+1) cpt).
+// The kk-th largest key is found by a radix select over the bytes of
+// rel = key - min + 1 (0 = not rankable), from the top set bit of the range
+// down, with a 256-bin LDS histogram per pass (hw: two of them, alternating);
+// one scan of the per-lane counts then places the kept candidates in ascending
+// index order.  With kReg, cpt = kC and every rel stays in a register;
+// otherwise cpt = ceil(n_cand / 64) and each pass reads the row again from LDS.
+template <int kC, bool kReg>
+__device__ __forceinline__ void topk_row_wave(const float* srow, int n_cand, int k, int kk, int ns, int nl_lo,
+                                              int32_t* out, int lane, uint32_t* hw) {
+  const int cpt = kReg ? kC : (n_cand + 63) >> 6;
+  const int n0 = lane * cpt;
+  uint32_t regs[kReg ? kC : 1];
+  auto key_of = [&](int c) -> uint32_t {
+    const int n = n0 + c;
+    const int nn = min(n, n_cand - 1);  // reads stay in the row
+    const float v = srow[nn + (nn >> 5)];
+    return (n < n_cand && n >= ns && n < nl_lo) ? ordered_key(v) : 0u;
+  };
+  uint32_t kmin = 0xffffffffu, kmx = 0u;
+  if constexpr (kReg) {
+#pragma unroll
+    for (int c = 0; c < kC; ++c) regs[c] = key_of(c);  // every read issued before any is used
+  }
+#pragma unroll(kReg ? kC : 4)
+  for (int c = 0; c < cpt; ++c) {
+    const uint32_t key = kReg ? regs[c] : key_of(c);
+    if (key != 0u) {
+      kmin = min(kmin, key);
+      kmx = max(kmx, key);
+    }
+  }
+  kmin = wave_umin(kmin);
+  kmx = wave_umax(kmx);
+  if constexpr (kReg) {
+#pragma unroll
+    for (int c = 0; c < kC; ++c) regs[c] = regs[c] != 0u ? regs[c] - kmin + 1u : 0u;
+  }
+  auto rel_of = [&](int c) -> uint32_t {
+    if constexpr (kReg) return regs[c];
+    const uint32_t key = key_of(c);
+    return key != 0u ? key - kmin + 1u : 0u;
+  };
+  const uint32_t range = kmx - kmin + 1u;  // >= 1: more than kk >= 1 rankable keys exist
+  const int bits = 32 - __clz(range);
+  uint32_t prefix = 0, pmask = 0, need = uint32_t(kk);
+  uint32_t thr = 0, ties_wanted = 0;
+  int width = bits < 8 ? bits : 8;
+  int shift = bits - width;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) hw[4 * lane + u] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+  for (int pass = 0;; ++pass) {
+    uint32_t* const hh = hw + (pass & 1) * 256;
+    const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll(kReg ? kC : 4)
+    for (int c = 0; c < cpt; ++c) {
+      const uint32_t rel = rel_of(c);
+      if (rel != 0u && (rel & pmask) == prefix) atomicAdd(&hh[(rel >> shift) & dmask], 1u);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // the digit whose bin holds the need-th largest key: lane l scans bins
+    // 255 - 4l .. 252 - 4l (digits in descending order)
+    uint32_t hc[4], loc = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      hc[u] = hh[255 - (4 * lane + u)];
+      loc += hc[u];
+    }
+    uint32_t above = wave_scan_incl(loc) - loc;
+    int hit = -1;
+    uint32_t h_rem = 0, h_bin = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (hit < 0 && above < need && above + hc[u] >= need) {
+        hit = u;
+        h_rem = need - above;
+        h_bin = hc[u];
+      }
+      above += hc[u];
+    }
+    const int src = int(__builtin_ctzll(__ballot(hit >= 0)));
+    const int hu = __builtin_amdgcn_readlane(hit, src);
+    const uint32_t digit = 255u - uint32_t(4 * src + hu);
+    const uint32_t rem = uint32_t(__builtin_amdgcn_readlane(int(h_rem), src));
+    const uint32_t bin = uint32_t(__builtin_amdgcn_readlane(int(h_bin), src));
+    uint32_t* const hn = hw + ((pass + 1) & 1) * 256;  // cleared for the next pass
+#pragma unroll
+    for (int u = 0; u < 4; ++u) hn[4 * lane + u] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    prefix |= digit << shift;
+    pmask |= dmask << shift;
+    need = rem;
+    if (rem == bin && prefix != 0u) {
+      thr = prefix - 1u;  // every key of this bin is kept: threshold just below it
+      ties_wanted = 0;
+      break;
+    }
+    if (shift == 0) {
+      thr = prefix;
+      ties_wanted = rem;
+      break;
+    }
+    width = shift < 8 ? shift : 8;
+    shift -= width;
+  }
+  // kept: forced, rel > thr, and the ties_wanted lowest-index rel == thr; one
+  // scan of the packed counts (ties << 16 | kept) gives each lane its first
+  // output position and the ties at lower indices
+  uint32_t n_tie = 0, n_gt = 0;
+#pragma unroll(kReg ? kC : 4)
+  for (int c = 0; c < cpt; ++c) {
+    const int n = n0 + c;
+    const uint32_t rel = rel_of(c);
+    if (n < n_cand) {
+      if (rel == 0u || rel > thr) ++n_gt;  // forced (rel 0), or above the threshold
+      else if (rel == thr) ++n_tie;
+    }
+  }
+  const uint32_t packed = (n_tie << 16) | n_gt;
+  const uint32_t before = wave_scan_incl(packed) - packed;
+  // (written without a guarded subtraction; see the decode top-k below)
+  const uint32_t taken_before = min(before >> 16, ties_wanted);
+  uint32_t ties_left = min(n_tie, ties_wanted - taken_before);
+  uint32_t pos = (before & 0xffffu) + taken_before;
+#pragma unroll(kReg ? kC : 4)
+  for (int c = 0; c < cpt; ++c) {
+    const int n = n0 + c;
+    const uint32_t rel = rel_of(c);
+    bool take = false;
+    if (n < n_cand) {
+      take = rel == 0u || rel > thr;
+      if (!take && rel == thr && ties_left > 0u) {
+        take = true;
+        --ties_left;
+      }
+    }
+    if (take && pos < uint32_t(k)) out[pos++] = n;
+  }
+}
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_scores_kernel(PrefillScoreParams p) {
-  constexpr int kT = kScoreTile;
-  constexpr int kDC = 32;  // d columns staged per pass
-  __shared__ float qs[kT][kDC + 1];
-  __shared__ float ks[kT][kDC + 1];
-  const int n0 = blockIdx.x * kT, m0 = blockIdx.y * kT;
-  if (n0 > m0 + kT - 1) return;  // entirely above the diagonal
-  const int bh = blockIdx.z;
+template <typename T, int D, int B>
+__global__ __launch_bounds__(256, 2) void select_prefill_kernel(PrefillSelectParams p) {
+  __shared__ float sarea[kSelFloats];
+  __shared__ uint32_t hist[4][2][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int BH = int(gridDim.x) / p.n_mg;
+  const int mg = p.n_mg - 1 - int(blockIdx.x) / BH;  // heaviest rows first
+  const int bh = int(blockIdx.x) % BH;
   const int bi = bh / p.Hq, h = bh % p.Hq;
   const int bkv = bi * (p.Hq / p.G) + h / p.G;
-  const float* qp = p.qp + (int64_t)bh * p.NB * D;
-  const float* kp = p.kp + (int64_t)bkv * p.NB * D;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int mi = wave >> 1, ni = wave & 1;  // this wave's 64 x 64 quadrant
-  const int col = lane & 31, kh = lane >> 5;
-  f32x16 acc[2][2];
+  const int m0 = mg * p.R;
+  const int R = min(p.R, p.NB - m0);
+
+  // the first two key tiles of this wave's scoring load while the queries pool
+  constexpr int kJ = D / 4;  // MFMAs per 16 x 16 tile
+  const int ci = lane & 15, kg = lane >> 4;
+  const int ncols = m0 + R;  // score columns 0 .. m0+R-1
+  const int ntiles = (ncols + 15) >> 4;
+  const float* kb = p.kp + int64_t(bkv) * p.NB * D + kg * kJ;
+  auto load_b = [&](int t, float (&b)[kJ]) {
+    const int n = t * 16 + ci;
+    if (t < ntiles && n < p.NB) {
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-  for (int d0 = 0; d0 < D; d0 += kDC) {
-    f32x4 va[kT * kDC / 4 / 256], vb[kT * kDC / 4 / 256];
-#pragma unroll
-    for (int u = 0; u < kT * kDC / 4 / 256; ++u) {
-      const int i = u * 256 + tid;
-      const int r = i / (kDC / 4), c = (i % (kDC / 4)) * 4;
-      va[u] = (m0 + r < p.NB) ? *reinterpret_cast<const f32x4*>(qp + (int64_t)(m0 + r) * D + d0 + c) : f32x4{};
-      vb[u] = (n0 + r < p.NB) ? *reinterpret_cast<const f32x4*>(kp + (int64_t)(n0 + r) * D + d0 + c) : f32x4{};
-    }
-#pragma unroll
-    for (int u = 0; u < kT * kDC / 4 / 256; ++u) {
-      const int i = u * 256 + tid;
-      const int r = i / (kDC / 4), c = (i % (kDC / 4)) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qs[r][c + e] = va[u][e];
-        ks[r][c + e] = vb[u][e];
+      for (int j = 0; j < kJ; j += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(kb + int64_t(n) * D + j);
+        b[j] = v[0];
+        b[j + 1] = v[1];
+        b[j + 2] = v[2];
+        b[j + 3] = v[3];
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) b[j] = 0.f;
     }
-    __syncthreads();
+  };
+  float b0[kJ], b1[kJ];
+  load_b(wave, b0);
+  load_b(wave + 4, b1);
+
+  // ---- 1. pool
+  constexpr int kE = 16 / int(sizeof(T));  // elements per 16-byte chunk
+  constexpr int kCh = D / kE;              // chunks per row
+  constexpr int kRG = 256 / kCh;           // row groups
+  constexpr int kRPT = B / kRG;            // rows per thread per block
+  static_assert(kRPT >= 1 && B % kRG == 0, "row split");
+  static_assert(2 * kRG * (D + 1) + kSelRows * D <= kSelFloats, "pool area");
+  float* part = sarea;                      // [2][kRG][D + 1]
+  float* qbar = sarea + 2 * kRG * (D + 1);  // [kSelRows][D]
+  {
+    const int ch = tid % kCh, rg = tid / kCh;
+    const char* qb = static_cast<const char*>(p.q) + (bi * p.qs0 + h * p.qs1) * int64_t(sizeof(T));
+    const int64_t rs = p.qs2 * int64_t(sizeof(T));
+    for (int r0 = 0; r0 < R; r0 += 2) {
+      int cnt[2];
+      u32x4 w[2][kRPT];
 #pragma unroll
-    for (int kk = 0; kk < kDC; kk += 2) {
-      float av[2], bv[2];
+      for (int u = 0; u < 2; ++u) {
+        const int lo = (m0 + r0 + u) * B;
+        cnt[u] = r0 + u < R ? min(B, p.S - lo) : 0;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        av[t] = qs[mi * 64 + t * 32 + col][kk + kh];
-        bv[t] = ks[ni * 64 + t * 32 + col][kk + kh];
+        for (int i = 0; i < kRPT; ++i) {
+          const int row = rg + i * kRG;
+          w[u][i] = row < cnt[u] ? __builtin_nontemporal_load(
+                                       reinterpret_cast<const u32x4*>(qb + int64_t(lo + row) * rs + ch * 16))
+                                 : u32x4{0u, 0u, 0u, 0u};
+        }
       }
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int u = 0; u < 2; ++u) {
+        float acc[kE];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+        for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kRPT; ++i) {
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[2 * e] += bf16_lo(w[u][i][e]);
+              acc[2 * e + 1] += bf16_hi(w[u][i][e]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[u][i][e]);
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < kE; ++e) part[(u * kRG + rg) * (D + 1) + ch * kE + e] = acc[e];
+      }
+      __syncthreads();
+      for (int x = tid; x < 2 * D; x += 256) {
+        const int u = x / D, d = x % D;
+        float sum = 0.f;
+#pragma unroll 8
+        for (int g = 0; g < kRG; ++g) sum += part[(u * kRG + g) * (D + 1) + d];
+        if (r0 + u < kSelRows) qbar[(r0 + u) * D + d] = cnt[u] > 0 ? sum / float(cnt[u]) : 0.f;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
-  // acc[a][b][i] holds row 8 (i / 4) + 4 kh + i % 4 of row tile a, column col of column tile b
-  float* sbase = p.s + (int64_t)bh * p.NB * p.NB;
+
+  // ---- 2. score
+  float a[kJ];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int n = n0 + ni * 64 + b * 32 + col;
+  for (int j = 0; j < kJ; ++j) a[j] = ci < R ? qbar[ci * D + kg * kJ + j] : 0.f;
+  __syncthreads();  // the score rows overwrite qbar
+  {
+    auto store = [&](int t, const f32x4& acc) {
+      const int n = t * 16 + ci;
+      if (t < ntiles && n < ncols) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + mi * 64 + a * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
-        if (m < p.NB && n <= m) sbase[(int64_t)m * p.NB + n] = acc[a][b][i] * p.scale;
+        for (int v = 0; v < 4; ++v) {
+          const int r = 4 * kg + v;
+          if (r < R) sarea[r * p.rowlen + n + (n >> 5)] = acc[v] * p.scale;
+        }
       }
+    };
+    auto mma_store = [&](int t, const float (&x0)[kJ], const float (&x1)[kJ]) {
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kJ; ++j) {
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], x0[j], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], x1[j], acc1, 0, 0, 0);
+      }
+      store(t, acc0);
+      store(t + 4, acc1);
+    };
+    // two tiles per step (t and t + 4: independent accumulators); the keys of
+    // the next step load into the other register set while this one's MFMAs run
+    float c0[kJ], c1[kJ];
+    for (int t = wave; t < ntiles; t += 16) {
+      load_b(t + 8, c0);
+      load_b(t + 12, c1);
+      mma_store(t, b0, b1);
+      if (t + 8 >= ntiles) break;
+      load_b(t + 16, b0);
+      load_b(t + 20, b1);
+      mma_store(t + 8, c0, c1);
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. top-k, one row per wave at a time
+  uint32_t* hw = &hist[wave][0][0];
+  for (int r = wave; r < R; r += 4) {
+    const int m = m0 + r;
+    const int n_cand = m + 1;
+    const int64_t row = int64_t(bh) * p.NB + m;
+    const int k = budget_blocks(n_cand, p.heads.min_blocks[h], p.heads.ratio_q16[h]);
+    const int ns = min<int>(p.heads.n_sink[h], n_cand);
+    const int nl_lo = max(ns, n_cand - p.heads.n_local[h]);  // forced: [0, ns) U [nl_lo, n_cand)
+    const int kk = k - ns - (n_cand - nl_lo);                 // to pick among the others
+    int32_t* out = p.idx + row * p.kmax;
+    if (lane == 0) p.cnt[row] = k;
+    for (int i = k + lane; i < p.kmax; i += 64) out[i] = -1;
+    if (kk <= 0 || k == n_cand) {
+      // (k >= the forced count: the budget validation keeps min_blocks >=
+      // n_sink + n_local; the bounds below only guard the row)
+      for (int n = lane; n < n_cand; n += 64) {
+        const int at = k == n_cand ? n : n < ns ? n : n >= nl_lo ? ns + (n - nl_lo) : -1;
+        if (at >= 0 && at < k) out[at] = n;
+      }
+      continue;
+    }
+    const float* srow = sarea + r * p.rowlen;
+    const int cr = (n_cand + 63) >> 6;  // candidates per lane this row needs
+    if (cr <= 4) topk_row_wave<4, true>(srow, n_cand, k, kk, ns, nl_lo, out, lane, hw);
+    else if (cr <= 8) topk_row_wave<8, true>(srow, n_cand, k, kk, ns, nl_lo, out, lane, hw);
+    else if (cr <= 16) topk_row_wave<16, true>(srow, n_cand, k, kk, ns, nl_lo, out, lane, hw);
+    else topk_row_wave<1, false>(srow, n_cand, k, kk, ns, nl_lo, out, lane, hw);
   }
 }
 
@@ -208,16 +479,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(TopkParams p) {
   const int row = blockIdx.x;
   if (row >= p.rows) return;
   const int tid = threadIdx.x;
-  int h, n_cand;
-  if (p.mode == 0) {
-    const int m = row % p.NB;
-    h = (row / p.NB) % p.Hq;
-    n_cand = m + 1;
-  } else {
-    h = row % p.Hq;
-    const int g = p.heads.gran[h];
-    n_cand = (p.kv_len + g - 1) / g;
-  }
+  const int h = row % p.Hq;
+  const int n_cand = (p.kv_len + p.heads.gran[h] - 1) / p.heads.gran[h];
   const int k = budget_blocks(n_cand, p.heads.min_blocks[h], p.heads.ratio_q16[h]);
   const int ns = min<int>(p.heads.n_sink[h], n_cand);
   // forced: [0, ns) U [nl_lo, n_cand), the two ranges made disjoint
@@ -509,34 +772,35 @@ hipError_t launch_pool(const PoolParams& p, int dtype, int D, int batch, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_scores(const PrefillScoreParams& p, int D, int batch, hipStream_t stream) {
-  const int t = (p.NB + kScoreTile - 1) / kScoreTile;
-  dim3 grid(t, t, batch * p.Hq);
-  if (D == 128) hipLaunchKernelGGL((prefill_scores_kernel<128>), grid, dim3(256), 0, stream, p);
-  else if (D == 64) hipLaunchKernelGGL((prefill_scores_kernel<64>), grid, dim3(256), 0, stream, p);
+template <typename T, int D>
+hipError_t select_prefill_launch(const PrefillSelectParams& p, int block, int batch, hipStream_t stream) {
+  const dim3 grid(batch * p.Hq * p.n_mg);
+  if (block == 128) hipLaunchKernelGGL((select_prefill_kernel<T, D, 128>), grid, dim3(256), 0, stream, p);
+  else if (block == 64) hipLaunchKernelGGL((select_prefill_kernel<T, D, 64>), grid, dim3(256), 0, stream, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
+hipError_t launch_select_prefill(const PrefillSelectParams& p, int dtype, int D, int block, int batch,
+                                 hipStream_t stream) {
+  if (p.NB < 1 || p.NB > kSelMaxBlocks || p.R != sel_rows(p.NB) || p.rowlen != sel_rowlen(p.NB) ||
+      p.n_mg != (p.NB + p.R - 1) / p.R)
+    return hipErrorInvalidValue;
+  if (dtype == 0 && D == 128) return select_prefill_launch<bf16_t, 128>(p, block, batch, stream);
+  if (dtype == 0 && D == 64) return select_prefill_launch<bf16_t, 64>(p, block, batch, stream);
+  if (dtype == 1 && D == 128) return select_prefill_launch<float, 128>(p, block, batch, stream);
+  if (dtype == 1 && D == 64) return select_prefill_launch<float, 64>(p, block, batch, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_topk(const TopkParams& p, int max_cand, hipStream_t stream) {
-  if (p.mode == 0) {
-    if (max_cand <= 64) return topk_launch<64, 1>(p, stream);
-    if (max_cand <= 128) return topk_launch<64, 2>(p, stream);
-    if (max_cand <= 256) return topk_launch<64, 4>(p, stream);
-    if (max_cand <= 512) return topk_launch<64, 8>(p, stream);
-    if (max_cand <= 1024) return topk_launch<64, 16>(p, stream);
-    if (max_cand <= 2048) return topk_launch<64, 32>(p, stream);
-    if (max_cand <= 4096) return topk_launch<256, 16>(p, stream);
-    if (max_cand <= 8192) return topk_launch<256, 32>(p, stream);
-  } else {
-    // decode rows are few (batch x heads): wide workgroups, few keys per thread
-    if (max_cand <= 256) return topk_launch<256, 1>(p, stream);
-    if (max_cand <= 1024) return topk_launch<256, 4>(p, stream);
-    if (max_cand <= 2048) return topk_launch<256, 8>(p, stream);
-    if (max_cand <= 4096) return topk_launch<512, 8>(p, stream);
-    if (max_cand <= 8192) return topk_launch<1024, 8>(p, stream);
-    if (max_cand <= 16384) return topk_launch<1024, 16>(p, stream);
-  }
+  // decode rows are few (batch x heads): wide workgroups, few keys per thread
+  if (max_cand <= 256) return topk_launch<256, 1>(p, stream);
+  if (max_cand <= 1024) return topk_launch<256, 4>(p, stream);
+  if (max_cand <= 2048) return topk_launch<256, 8>(p, stream);
+  if (max_cand <= 4096) return topk_launch<512, 8>(p, stream);
+  if (max_cand <= 8192) return topk_launch<1024, 8>(p, stream);
+  if (max_cand <= 16384) return topk_launch<1024, 16>(p, stream);
   return hipErrorInvalidValue;
 }
 

@@ -542,3 +542,24 @@ def test_prefill_schedule_validation():
         with pytest.raises(SA.SaError):
             SA.sa_prefill_schedule(d, b, **kw)
     assert SA.sa_prefill_schedule(d, b, SA.SA_SCHED_GRID) == (None, None, None)
+
+
+def test_prefill_selection_block_limit():
+    """The prefill selection holds a workgroup's score rows in LDS: more than
+    8192 query blocks is SA_ERR_UNSUPPORTED, found before any device call."""
+    import torch
+    q = torch.empty((1, 1, 8193 * 64, 64), dtype=torch.bfloat16, device="meta")
+    d = SA.make_prefill_desc(q, q, q, q, 64)
+    b = SA.make_budgets({"min_blocks": [2], "ratio_q16": [4096], "n_sink": [1], "n_local": [1], "granularity": [64]})
+    with pytest.raises(SA.SaError) as e:
+        SA.sa_prefill_block_counts(d, b)
+    assert e.value.status == SA.SA_ERR_UNSUPPORTED
+    fake = ctypes.c_void_p(1 << 20)
+    st = SA._lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 8193, fake, 1 << 40, None)
+    assert st == SA.SA_ERR_UNSUPPORTED
+    q8 = q[:, :, : 8192 * 64]
+    d8 = SA.make_prefill_desc(q8, q8, q8, q8, 64)
+    _, kmax8 = SA.sa_prefill_block_counts(d8, b)
+    st = SA._lib.sa_select_blocks(ctypes.byref(d8), b, fake, fake, None, fake, fake, kmax8, fake, 1 << 40, None)
+    if not torch.cuda.is_available():
+        assert st in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
