@@ -180,7 +180,7 @@ def traffic_from_profiles():
     return rec.get("bytes_per_launch")
 
 
-def tail_report(spec_name, dev, stream, n_bins, queues):
+def tail_report(spec_name, dev, stream, n_bins, queues, inp=None):
     """How well each schedule fills the chip to the end of the prefill
     attention: one launch per schedule that records every workgroup's start and
     end on the GPU's constant clock.  busy_w = end_w - start_w; span = last end
@@ -192,8 +192,9 @@ def tail_report(spec_name, dev, stream, n_bins, queues):
     import torch
     from head_heterogeneous_block_amd import sparse_attn as SA
     from head_heterogeneous_block_amd import workloads as W
-    spec = W.BY_NAME[spec_name]
-    inp = W.make_prefill(spec, W.seed_of(spec), device=dev)
+    spec = W.BY_NAME[spec_name] if isinstance(spec_name, str) else spec_name
+    if inp is None:
+        inp = W.make_prefill(spec, W.seed_of(spec), device=dev)
     base = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins, queue=True, queues=queues)
     base.select(inp.q, inp.k)
     o = torch.empty_like(inp.q)
@@ -244,6 +245,45 @@ def tail_report(spec_name, dev, stream, n_bins, queues):
         del pl
     del plans, base, inp
     torch.cuda.empty_cache()
+    return out
+
+
+def budget_fit_ablation(pspec, dev, stream, n_bins, queues, reps):
+    """The prefill layer under the two other readings of the fixed-total
+    budget shift (the inputs' Q, K, V unchanged): "clamp" bisects the common
+    factor with every ratio clamped to the stated range, "span" stretches the
+    drawn ratios onto the whole range (lowest head at its bottom, highest at its
+    top) at the same mean.  Per reading: the ratio range, the attended flops,
+    the default schedule's attention time, and the idle-tail report."""
+    import numpy as np
+    import torch
+    from head_heterogeneous_block_amd import metrics as M
+    from head_heterogeneous_block_amd import sparse_attn as SA
+    from head_heterogeneous_block_amd import workloads as W
+    out = {}
+    for fit in ("clamp", "span"):
+        spec = pspec.with_(budget_fit=fit)
+        inp = W.make_prefill(spec, W.seed_of(pspec), device=dev)
+        r = np.asarray(inp.budget["ratio_q16"], dtype=np.float64) / 65536.0
+        plan = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins, queue=True, queues=queues)
+        plan.select(inp.q, inp.k)
+        o = torch.empty_like(inp.q)
+        att = lambda: plan.attend(inp.q, inp.k, inp.v, o)  # noqa: E731
+        att()
+        ms = timed(att, stream, reps)[0]
+        flops = M.prefill_flops(plan.block_idx.cpu().numpy(), plan.block_cnt.cpu().numpy(), spec.seq_len,
+                                spec.block, spec.head_dim)
+        loads = plan.counts.reshape(-1).astype(np.int64)
+        del plan, o
+        torch.cuda.empty_cache()
+        out[fit] = {"ratio_min": float(r.min()), "ratio_max": float(r.max()), "ratio_mean": float(r.mean()),
+                    "attended_flops": flops, "attention_ms": ms, "attended_tflops": flops / (ms * 1e-3) / 1e12,
+                    "max_tile_blocks": int(loads.max()),
+                    "tail": tail_report(spec, dev, stream, n_bins, queues, inp=inp)}
+        del inp
+        torch.cuda.empty_cache()
+        print(f"[bench] budget fit {fit}: ratios {r.min():.4f}..{r.max():.4f}, attention {ms:.3f} ms",
+              file=sys.stderr, flush=True)
     return out
 
 
@@ -639,6 +679,8 @@ def main():
         if args.tail:
             tails.append(tail_report("qwen2.5-72b-prefill-64k", dev, stream, n_bins, args.queues))
         out["tail"] = tails
+    if args.only in ("prefill", "all") and not args.no_ablation:
+        out["ablation"]["budget_fit"] = budget_fit_ablation(pspec, dev, stream, n_bins, args.queues, reps)
     print(json.dumps(out))
 
 

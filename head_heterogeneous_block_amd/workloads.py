@@ -46,6 +46,7 @@ class PrefillSpec:
     lo: float = 0.0  # loguniform draw range, or bimodal (low, high) levels
     hi: float = 0.0
     mean: float = 0.0  # target mean ratio after the fixed-total rescale
+    budget_fit: str = "rescale"  # "rescale" | "clamp" | "span" (see prefill_budgets)
     frac_high: float = 0.0  # bimodal: share of heads at the high level
     n_hot: int = 8
     hot_k: float = 2.0  # K gets +hot_k * u_h on hot blocks
@@ -151,6 +152,15 @@ def prefill_budgets(spec: PrefillSpec, seed: int) -> dict:
     * ``bimodal``: ``round(frac_high * H)`` heads (a seeded choice) at ``hi``,
       the rest at ``lo``, then the same mean-preserving scale.
 
+    ``budget_fit="clamp"`` (the alternative reading of the fixed-total shift):
+    the common factor c is instead found by bisection so that the ratios
+    clamped to ``[lo, hi]`` have mean ``mean``; every ratio stays inside the
+    stated range (the plain rescale can move them below ``lo``).
+    ``budget_fit="span"`` (log-uniform draws only): the drawn log-ratios are
+    stretched onto the whole range, x = (log f - log f_min) / (log f_max -
+    log f_min), and r = lo * (hi / lo) ** (x ** g) with g found by bisection so
+    that the mean is ``mean``: the lowest head at ``lo``, the highest at ``hi``.
+
     Ratios are quantised once to units of 2**-16 (round half to even).
     """
     H = spec.n_q_heads
@@ -166,7 +176,31 @@ def prefill_budgets(spec: PrefillSpec, seed: int) -> dict:
             n_high = int(round(spec.frac_high * H))
             f = np.full(H, spec.lo)
             f[r.permutation(H)[:n_high]] = spec.hi
-        f = f * (spec.mean / f.mean())
+        if spec.budget_fit == "rescale":
+            f = f * (spec.mean / f.mean())
+        elif spec.budget_fit == "clamp":
+            if not spec.lo <= spec.mean <= spec.hi:
+                raise ValueError("clamp fit needs lo <= mean <= hi")
+            c_lo, c_hi = 0.0, spec.hi / f.min()  # mean of the clamped ratios grows with c, from lo to hi
+            for _ in range(200):
+                c = 0.5 * (c_lo + c_hi)
+                if np.clip(c * f, spec.lo, spec.hi).mean() < spec.mean:
+                    c_lo = c
+                else:
+                    c_hi = c
+            f = np.clip(0.5 * (c_lo + c_hi) * f, spec.lo, spec.hi)
+        elif spec.budget_fit == "span" and spec.budget_kind == "loguniform":
+            x = (np.log(f) - np.log(f.min())) / (np.log(f.max()) - np.log(f.min()))
+            g_lo, g_hi = 1e-3, 1e3  # the mean falls as g grows (x in [0, 1])
+            for _ in range(200):
+                g = math.sqrt(g_lo * g_hi)
+                if (spec.lo * (spec.hi / spec.lo) ** (x ** g)).mean() > spec.mean:
+                    g_lo = g
+                else:
+                    g_hi = g
+            f = spec.lo * (spec.hi / spec.lo) ** (x ** math.sqrt(g_lo * g_hi))
+        else:
+            raise ValueError(spec.budget_fit)
         ratio = np.rint(f * 65536.0).astype(np.int64)
     else:
         raise ValueError(spec.budget_kind)
