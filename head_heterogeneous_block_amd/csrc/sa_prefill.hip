@@ -414,6 +414,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       __builtin_amdgcn_s_setprio(1);
       u32x4 pf[4];
       float ps0 = 0.f, ps1 = 0.f, px0 = 0.f, px1 = 0.f;
+      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
       for (int dg = 0; dg < C::kDG; ++dg) {
 #pragma unroll
@@ -433,8 +434,12 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[kc >> 1][i + 1], c2, -m_use));
           const uint32_t pk = pack_bf16x2(p0, p1);
           pf[kc][w] = pk;
-          ps0 += bf16_lo(pk);
-          ps1 += bf16_hi(pk);
+          // the rounded pair summed in one v_dot2 against (1, 1): products
+          // exact, fp32 sum; two chains.  Taken on the packed word itself (a
+          // dot product on the fragment vector after it is built was folded
+          // wrongly by the compiler, reading some words twice)
+          if (w2 & 1) ps1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one2, ps1, false);
+          else ps0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one2, ps0, false);
           if constexpr (kLse) {
             px0 += p0;
             px1 += p1;
@@ -464,25 +469,29 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                                                              __builtin_bit_cast(bf16x8, pf[kc]), oacc[dt], 0, 0, 0);
         }
       }
-      // Issue order: K fragment reads run four MFMAs ahead; every Q K^T MFMA
-      // carries a share of the softmax VALU behind it, then every P V MFMA
-      // carries the transposed V reads of the MFMA two places later, so the
-      // MFMA pipe runs under the VALU work and LDS latency stays hidden.  Six
-      // VALU ops per Q K^T MFMA and three per P V MFMA measured about 1%
-      // faster than seven and two (eight and one, or five and four, slower).
+      // Issue order: K fragment reads run four MFMAs ahead; the Q K^T MFMAs
+      // go out nearly back to back (one VALU op behind each at D = 128), and
+      // every P V MFMA carries the transposed V reads of the MFMA two places
+      // later and most of the softmax VALU (eight ops at D = 128), so the
+      // MFMA pipe runs under the VALU work and LDS latency stays hidden.
+      // Measured on the 128K layer, one process: 1 / 8 VALU ops per Q K^T /
+      // P V MFMA 9.04 ms, 1 / 9, 1 / 10 and 0 / 8 within 0.3% of it, 1 / 7
+      // 9.33, 2 / 9 9.56, against 10.30 for the former 6 / 3 with the row
+      // sum taken by unpacking and adding the rounded pair.
+      constexpr int kQkValu = 128 / D, kPvValu = 8 * 128 / D;
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int u = 0; u < 2 * C::kDG; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, kQkValu, 0);  // VALU
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
       for (int u = 0; u < 4 * C::kDT; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read (transposed)
-        __builtin_amdgcn_sched_group_barrier(0x003, 3, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x003, kPvValu, 0);  // VALU
       }
       __builtin_amdgcn_s_setprio(0);
     } else {
