@@ -7,7 +7,7 @@ import pytest
 
 import oracle as O
 
-SA = pytest.importorskip("head_heterogeneous_block_amd.sparse_attn", reason="library not built")
+SA = pytest.importorskip("head_heterogeneous_block_amd.sparse_attn", reason="library not built", exc_type=ImportError)
 
 
 def _qk(seed, b=1, H=2, Hk=1, S=300, D=16, scale=1.0):

@@ -17,7 +17,7 @@ import oracle as O
 from head_heterogeneous_block_amd import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SA = pytest.importorskip("head_heterogeneous_block_amd.sparse_attn", reason="library not built")
+SA = pytest.importorskip("head_heterogeneous_block_amd.sparse_attn", reason="library not built", exc_type=ImportError)
 
 
 def _header_functions():
