@@ -261,7 +261,8 @@ def budget_fit_ablation(pspec, dev, stream, n_bins, queues, reps):
     from head_heterogeneous_block_amd import sparse_attn as SA
     from head_heterogeneous_block_amd import workloads as W
     out = {}
-    for fit in ("clamp", "span"):
+    # "span" stretches log-uniform draws; the bimodal and count budgets have no draw range to stretch
+    for fit in ("clamp", "span") if pspec.budget_kind == "loguniform" else ("clamp",):
         spec = pspec.with_(budget_fit=fit)
         inp = W.make_prefill(spec, W.seed_of(pspec), device=dev)
         r = np.asarray(inp.budget["ratio_q16"], dtype=np.float64) / 65536.0
