@@ -83,6 +83,26 @@ def timed(fn, stream, reps, scrub=None):
     return ts[len(ts) // 2], sum(ts) / len(ts), ts
 
 
+def graph_timed(fn, stream, reps):
+    """Median milliseconds of fn() captured once in a HIP graph and replayed on
+    `stream` (the same kernels, without the host's launch path between them)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = timed(g.replay, stream, reps)[0]
+    del g
+    return ms
+
+
 def pct(ts, q):
     """q-quantile of sorted samples (nearest rank)."""
     return ts[min(len(ts) - 1, max(0, int(round(q * (len(ts) - 1)))))]
@@ -481,6 +501,7 @@ def main():
         res["att_mean_ms"] = att_mean
         res["att_p10_p90_ms"] = [pct(att_ts, 0.1), pct(att_ts, 0.9)]
         res["att_scrub_ms"] = timed(att, stream, reps, scrub)[0]
+        res["layer_graph_ms"] = graph_timed(lambda: (sel(), att()), stream, reps)
     if args.only in ("decode", "all"):
         res["dsel_ms"] = timed(dsel, stream, reps)[0]
         res["datt_ms"] = timed(datt, stream, reps)[0]
@@ -488,6 +509,7 @@ def main():
         res["dstep_ms"] = dmed
         res["dstep_p10_p90_ms"] = [pct(dts, 0.1), pct(dts, 0.9)]
         res["dstep_scrub_ms"] = timed(lambda: (dsel(), datt()), stream, reps, scrub)[0]
+        res["dstep_graph_ms"] = graph_timed(lambda: (dsel(), datt()), stream, reps)
         if not args.no_paged:
             # the same decode step over the cache scattered into per-KV-head
             # pools of 128-token pages (the pools are built once, untimed)
@@ -651,11 +673,13 @@ def main():
         "prefill": {"select_ms": res.get("sel_ms"), "select_p10_p90_ms": res.get("sel_p10_p90_ms"),
                     "attention_ms": res.get("att_ms"), "attention_p10_p90_ms": res.get("att_p10_p90_ms"),
                     "attention_ms_scrubbed": res.get("att_scrub_ms"),
+                    "layer_ms_hip_graph": res.get("layer_graph_ms"),
                     "attended_tflops": tflops, "attended_flops": flops,
                     "mfma_frac": roofline["frac"], "schedule_host_ms": lpt_ms},
         "decode": {"select_ms": res.get("dsel_ms"), "attention_ms": res.get("datt_ms"),
                    "step_ms": res.get("dstep_ms"), "step_p10_p90_ms": res.get("dstep_p10_p90_ms"),
                    "step_ms_scrubbed": res.get("dstep_scrub_ms"),
+                   "step_ms_hip_graph": res.get("dstep_graph_ms"),
                    "bytes": dbytes, "step_gbps": dgbps,
                    "hbm_frac": dgbps / (M.PEAK_HBM_BYTES / 1e9) if dgbps else None,
                    "hbm_frac_measured": dgbps / peaks["hbm_read_gbps"] if dgbps and peaks else None,
