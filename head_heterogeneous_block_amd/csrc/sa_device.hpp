@@ -187,6 +187,29 @@ __device__ __forceinline__ void dma16_async(i32x4 r, char* lds, int voff) {
 #endif
 }
 
+// dma16_async with the LDS address given as a wave-uniform 32-bit LDS byte
+// address plus a compile-time offset, added into m0 by the same instruction
+// sequence (one scalar add per load; no generic-to-LDS pointer conversion).
+template <int kOff>
+__device__ __forceinline__ void dma16_async_at(i32x4 r, uint32_t lds_addr, int voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_add_u32 m0, %0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds" ::"s"(lds_addr), "i"(kOff), "v"(voff),
+               "s"(r)
+               : "memory");
+#else
+  (void)r, (void)lds_addr, (void)voff;
+#endif
+}
+// kN consecutive 1 KB wave loads: load u fills LDS [lds_addr + kOff + 1024 u,
+// + 1024) from per-lane offset voff[u]
+template <int kOff, int kN, int kU = 0>
+__device__ __forceinline__ void dma16_async_run(i32x4 r, uint32_t lds_addr, const int* voff) {
+  if constexpr (kU < kN) {
+    dma16_async_at<kOff + kU * 1024>(r, lds_addr, voff[kU]);
+    dma16_async_run<kOff, kN, kU + 1>(r, lds_addr, voff);
+  }
+}
+
 // dma16_async with the non-temporal cache policy (nt), for data read exactly
 // once: the lines are not kept for reuse.  A streaming read of HBM runs about
 // 13% faster this way on gfx950 (7.0 against 6.2 TB/s for a plain grid-stride

@@ -50,6 +50,13 @@ namespace {
 
 using namespace prefill;
 
+// A step of the cursor with the global byte addresses of its (batch, KV head)
+// K and V slices, computed once when the cursor enters a tile so that a
+// step's gathers only add the row offset.
+struct StepAt : Step {
+  uint64_t ka, va;
+};
+
 template <typename T, int D, int B, bool kLse>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
   using C = Cfg<T, D, B>;
@@ -173,7 +180,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   int nx_item = -1, nx_win = -1;            // prefetched first window of item nx_item
   int nx_tile = -1, nx_cnt = 0;             // queue mode: its tile and block count
   int q_next = 0;                           // queue mode: the item after the cursor's
-  Step cur;
+  StepAt cur;
   cur.valid = 0;
 
   auto item_tile = [&](int it, int& tile, int& cnt) {
@@ -231,7 +238,9 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           const int NB = COLD(NB), Hq = COLD(Hq);
           cur.m = tile % NB;
           cur.bh = tile / NB;
-          cur.kvs = ((cur.bh / Hq) << 16) | ((cur.bh % Hq) / COLD(G));
+          const int kb = cur.bh / Hq, kh = (cur.bh % Hq) / COLD(G);
+          cur.ka = reinterpret_cast<uint64_t>(COLD(k)) + (kb * COLD(ks0) + kh * COLD(ks1)) * (int64_t)sizeof(T);
+          cur.va = reinterpret_cast<uint64_t>(COLD(v)) + (kb * COLD(vs0) + kh * COLD(vs1)) * (int64_t)sizeof(T);
           prefetch_next(qmode ? q_next : it + 1);
         }
       }
@@ -281,17 +290,22 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // ring slots wait for them, so each step's gathers have a whole step to
   // land; the wait and barrier at the top of the next iteration order them
   // before their slots are read.
-  auto fetch = [&](const Step& s, int slot, bool k_side) {
-    const int kb = s.kvs >> 16, kh = s.kvs & 0xffff;
-    const char* base = k_side
-                           ? reinterpret_cast<const char*>(p.k) + (kb * p.ks0 + kh * p.ks1) * (int64_t)sizeof(T)
-                           : reinterpret_cast<const char*>(p.v) + (kb * p.vs0 + kh * p.vs1) * (int64_t)sizeof(T);
+  // this wave's share of each LDS slot starts kInstsPerWave KB into it
+  const uint32_t lds_wave =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)smem)) + wave * C::kInstsPerWave * 1024;
+  auto fetch = [&](const StepAt& s, int slot, bool k_side) {
     const int rs = k_side ? krs : vrs;
     const int row = s.n * B + s.hs * kKS;
-    const i32x4 r = buffer_rsrc_words(base + (int64_t)row * rs, max(S - row, 0) * rs);
-    char* dst = (k_side ? kring : vring) + slot * C::kTile + wave * C::kInstsPerWave * 1024;
-#pragma unroll
-    for (int u = 0; u < C::kInstsPerWave; ++u) dma16_async(r, dst + u * 1024, k_side ? k_voff[u] : v_voff[u]);
+    const i32x4 r = buffer_rsrc_words(reinterpret_cast<const char*>(k_side ? s.ka : s.va) + (int64_t)row * rs,
+                                      max(S - row, 0) * rs);
+    const uint32_t lw = __builtin_amdgcn_readfirstlane(lds_wave);
+    // smem: K slots 0, 1, then V slots 0, 1
+    const int* vo = k_side ? k_voff : v_voff;
+    const int which = (k_side ? 0 : 2) + slot;
+    if (which == 0) dma16_async_run<0, C::kInstsPerWave>(r, lw, vo);
+    else if (which == 1) dma16_async_run<C::kTile, C::kInstsPerWave>(r, lw, vo);
+    else if (which == 2) dma16_async_run<2 * C::kTile, C::kInstsPerWave>(r, lw, vo);
+    else dma16_async_run<3 * C::kTile, C::kInstsPerWave>(r, lw, vo);
   };
   // all of this wave's direct loads have landed in LDS (vmcnt(0) only)
   auto wait_loads = [&]() { wait_vmcnt<0>(); };
@@ -305,7 +319,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   float m_run = kNegInf, l_run = 0.f, l_lse = 0.f;
   int t_bh = 0, t_m = 0;  // tile being accumulated
 
-  auto start_tile = [&](const Step& s) {
+  auto start_tile = [&](const StepAt& s) {
     t_bh = s.bh;
     t_m = s.m;
     const int Hq = COLD(Hq);
@@ -383,7 +397,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
   // Masking of a step's scores in place (causal diagonal, sequence tail, or a
   // step this wave cannot see at all).
-  auto apply_mask = [&](const Step& s, f32x16(&sacc)[2]) {
+  auto apply_mask = [&](const StepAt& s, f32x16(&sacc)[2]) {
     const int key0 = s.hs * kKS;
     const bool diag = s.n == s.m;
     const int q_in_blk = wave * 32 + col;
@@ -530,13 +544,13 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   load_items(it_beg);
   cur.item = -1;
   seek(it_beg, 0);
-  Step s0 = cur;
+  StepAt s0 = cur;
   if (!s0.valid) {
     wg_stamp(1);
     return;
   }
   advance();
-  Step s1 = cur;
+  StepAt s1 = cur;
   advance();
   fetch(s0, 0, true);
   fetch(s0, 0, false);
