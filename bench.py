@@ -123,11 +123,14 @@ def prefill_kernel_hash() -> str:
 def measured_peaks(dev, stream, reps=7):
     """The roofline denominators this GPU sustains, from the library's two
     probes, each checked before its rate is used: the bf16 MFMA rate (8
-    independent 32x32x16 chains per wave, every accumulator ending at an exact
-    value) and the HBM streaming-read rate over a 4 GiB buffer (far beyond L2
+    independent 32x32x16 chains per wave; operands of ones, every accumulator
+    ending at an exact value, and pseudo-random operands, checked against the
+    fp64 value of the same products) and the HBM streaming-read rate over a 4 GiB buffer (far beyond L2
     and the 256 MB MALL; the XOR of the probe's outputs must match that of the
     buffer).  Best of a few launch shapes, median of `reps` launches each."""
+    import numpy as np
     import torch
+    from head_heterogeneous_block_amd import metrics as M
     from head_heterogeneous_block_amd import sparse_attn as SA
     n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     out = {}
@@ -150,6 +153,24 @@ def measured_peaks(dev, stream, reps=7):
     # 256 CUs x 4 SIMDs x 1024 flops per clock (one 32x32x16 MFMA per 32 clocks)
     out["mfma_implied_clock_ghz"] = best[0] * 1e12 / (n_cu * 4 * 1024) / 1e9
     out["mfma_probe"] = f"{best[1]} workgroups x 4 waves x 8 chains x {iters} v_mfma_f32_32x32x16_bf16, {best[2]:.3f} ms"
+    # the same loop on pseudo-random bf16 operands: real data draws more power,
+    # and the power limit holds a lower clock (the rate attention can reach)
+    best = None
+    for per_cu in (1, 2):
+        n_wg = n_cu * per_cu
+        sink = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+        fl = SA.sa_measure_mfma_peak(n_wg, iters, sink, operands=1)  # warm
+        ms = timed(lambda: SA.sa_measure_mfma_peak(n_wg, iters, sink, operands=1), stream, reps)[0]
+        want, scale = M.mfma_probe_random_sink(n_wg, iters)
+        if not np.all(np.abs(sink.cpu().double().numpy() - want) <= (iters + 8) * 2.0**-23 * scale + 1e-6):
+            raise RuntimeError("MFMA probe (random operands): wrong accumulator values")
+        rate = fl / (ms * 1e-3) / 1e12
+        if best is None or rate > best[0]:
+            best = (rate, n_wg, ms)
+    out["mfma_bf16_random_tflops"] = best[0]
+    out["mfma_random_implied_clock_ghz"] = best[0] * 1e12 / (n_cu * 4 * 1024) / 1e9
+    out["mfma_random_probe"] = (f"{best[1]} workgroups x 4 waves x 8 chains x {iters} v_mfma_f32_32x32x16_bf16 on "
+                                f"pseudo-random bf16 operands, {best[2]:.3f} ms")
     nbytes = 4 << 30
     buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev)
     x = buf
@@ -553,6 +574,7 @@ def main():
     tflops = flops / (res["att_mean_ms"] * 1e-3) / 1e12 if "att_ms" in res else None
     traffic = traffic_from_profiles()
     pk_mfma = peaks["mfma_bf16_tflops"] if peaks else None
+    pk_mfma_rnd = peaks["mfma_bf16_random_tflops"] if peaks else None
     roofline = {
         "bound": "mfma",
         "achieved": tflops,
@@ -561,6 +583,8 @@ def main():
         "frac": tflops / (M.PEAK_BF16_FLOPS / 1e12) if tflops else None,
         "peak_measured": pk_mfma,
         "frac_measured": tflops / pk_mfma if tflops and pk_mfma else None,
+        "peak_measured_random_operands": pk_mfma_rnd,
+        "frac_measured_random_operands": tflops / pk_mfma_rnd if tflops and pk_mfma_rnd else None,
         "traffic": traffic,
         "kernel": "prefill_kernel (sa_sparse_attn_prefill)",
         "flops_per_launch": flops,

@@ -1337,14 +1337,15 @@ sa_status sa_sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_head_bu
 }
 
 
-sa_status sa_measure_mfma_peak(int32_t n_workgroups, int32_t iters, float* sink, void* stream) {
+sa_status sa_measure_mfma_peak(int32_t n_workgroups, int32_t iters, int32_t operands, float* sink, void* stream) {
   if (!sink) return fail(SA_ERR_INVALID_ARG, "sink is NULL");
+  if (operands != 0 && operands != 1) return fail(SA_ERR_INVALID_ARG, "operands %d is not 0 (ones) or 1 (random)", operands);
   if (n_workgroups < 1 || n_workgroups > (1 << 20)) return fail(SA_ERR_INVALID_ARG, "n_workgroups %d out of [1, 2^20]", n_workgroups);
   if (iters < 1 || iters > 65536) return fail(SA_ERR_INVALID_ARG, "iters %d out of [1, 65536]", iters);
   if (reinterpret_cast<uintptr_t>(sink) & 3) return fail(SA_ERR_INVALID_ARG, "sink must be 4-byte aligned");
   sa_status s = check_device();
   if (s) return s;
-  const hipError_t e = sa::launch_mfma_peak(n_workgroups, iters, sink, (hipStream_t)stream);
+  const hipError_t e = sa::launch_mfma_peak(n_workgroups, iters, operands == 1, sink, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "mfma peak");
   return ok();
 }

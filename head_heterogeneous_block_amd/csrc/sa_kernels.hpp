@@ -208,7 +208,7 @@ hipError_t launch_output_deviation(const DeviationParams& p, hipStream_t stream)
 
 // roofline denominators: 8 independent chains of 32x32x16 bf16 MFMAs per wave
 // (four waves per workgroup), and a grid-stride non-temporal read of a buffer
-hipError_t launch_mfma_peak(int n_workgroups, int iters, float* sink, hipStream_t stream);
+hipError_t launch_mfma_peak(int n_workgroups, int iters, bool random_operands, float* sink, hipStream_t stream);
 hipError_t launch_hbm_read(const void* src, int64_t bytes, uint32_t* sink, int n_workgroups, hipStream_t stream);
 
 }  // namespace sa

@@ -74,3 +74,48 @@ def decode_bytes(block_idx: np.ndarray, block_cnt: np.ndarray, granularity, n_q_
     small = b * n_q_heads * (2 * head_dim * elem_bytes + block_idx.shape[2] * 4 + 4)
     return {"kv": kv, "pooled": pooled, "small": small, "total": kv + pooled + small,
             "union_tokens": union_tokens}
+
+
+def _lowbias32(x: np.ndarray) -> np.ndarray:
+    """The "lowbias32" integer hash (C. Wellons, "Prospecting for Hash
+    Functions") on uint32 arrays, wrapping like the GPU's 32-bit arithmetic."""
+    x = x.astype(np.uint64)
+    m = np.uint64(0xFFFFFFFF)
+    x ^= x >> np.uint64(16)
+    x = (x * np.uint64(0x7FEB352D)) & m
+    x ^= x >> np.uint64(15)
+    x = (x * np.uint64(0x846CA68B)) & m
+    x ^= x >> np.uint64(16)
+    return x
+
+
+def mfma_probe_random_sink(n_workgroups: int, iters: int):
+    """The sink of the MFMA rate probe with random operands (the header's
+    formula, in fp64): per global thread, iters times the sum over the 8 chains
+    of the accumulator entry each chain leaves in that lane's element c.
+    Returns (expected, scale): scale is the same sum over the absolute products,
+    against which the probe's fp32 accumulation error is measured."""
+    import torch
+
+    n = n_workgroups * 256
+    t = np.arange(n, dtype=np.uint64)
+    f = np.arange(8, dtype=np.uint64)
+    e = np.arange(8, dtype=np.uint64)
+    h = _lowbias32((64 * t[:, None, None] + 8 * f[None, :, None] + e[None, None, :]) & np.uint64(0xFFFFFFFF))
+    v = ((h & np.uint64(0xFFFF)).astype(np.int64) - 32768).astype(np.float32) / np.float32(32768.0)
+    v = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()  # round to nearest even
+    w = v.reshape(n // 64, 64, 8, 8)  # wave, lane, fragment, element
+    # fragment rows (A) / columns (B) are lane % 32; k = 8 * (lane / 32) + e
+    frag = np.concatenate([w[:, :32], w[:, 32:]], axis=-1)  # wave, row, fragment, k (16)
+    lane = np.arange(64)
+    expected = np.zeros((n // 64, 64))
+    scale = np.zeros((n // 64, 64))
+    for c in range(8):
+        a = frag[:, :, c % 4, :]          # wave, i, k
+        b = frag[:, :, 4 + c % 4, :]      # wave, j, k
+        d = np.einsum("wik,wjk->wij", a, b)
+        dabs = np.einsum("wik,wjk->wij", np.abs(a), np.abs(b))
+        row = 8 * (c // 4) + 4 * (lane // 32) + c % 4
+        expected += d[:, row, lane % 32]
+        scale += dabs[:, row, lane % 32]
+    return (iters * expected).reshape(-1), (iters * scale).reshape(-1)

@@ -135,7 +135,7 @@ _SIG = {
     "sa_output_deviation": (ctypes.c_int32, [_descp, _P, _P, _P, _P]),
     "sa_budget_shift": (ctypes.c_int32, [ctypes.POINTER(ctypes.c_double), ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int64, ctypes.POINTER(ctypes.c_uint32)]),
-    "sa_measure_mfma_peak": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    "sa_measure_mfma_peak": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "sa_measure_hbm_read": (ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P]),
 }
 for _name, (_res, _args) in _SIG.items():
@@ -503,12 +503,14 @@ def sa_output_deviation(desc: sa_attn_desc, o_approx: torch.Tensor, o_ref: torch
     _check(_lib.sa_output_deviation(ctypes.byref(desc), _ptr(o_approx), _ptr(o_ref), _ptr(dev), _stream(o_ref)))
 
 
-def sa_measure_mfma_peak(n_workgroups: int, iters: int, sink: torch.Tensor) -> int:
+def sa_measure_mfma_peak(n_workgroups: int, iters: int, sink: torch.Tensor, operands: int = 0) -> int:
     """Launch the bf16 MFMA rate probe on sink's device and stream; returns the
-    flops it does (every sink entry becomes 128 * iters)."""
+    flops it does.  operands 0: ones (every sink entry becomes 128 * iters);
+    1: pseudo-random bf16 operands (the sink entries follow the header's
+    formula)."""
     if sink.dtype != torch.float32 or sink.numel() < n_workgroups * 256:
         raise ValueError("sink must be fp32 with n_workgroups * 256 entries")
-    _check(_lib.sa_measure_mfma_peak(n_workgroups, iters, _ptr(sink), _stream(sink)))
+    _check(_lib.sa_measure_mfma_peak(n_workgroups, iters, operands, _ptr(sink), _stream(sink)))
     return n_workgroups * 4 * 8 * iters * 32768
 
 

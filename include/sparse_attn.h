@@ -532,13 +532,27 @@ sa_status sa_sparse_attn_decode_paged(const sa_attn_desc* desc, const sa_head_bu
  * attention kernels' achieved rate is set beside, next to the published dense
  * bf16 peak (MI355X: 2.5 PFLOP/s at 2.4 GHz).  n_workgroups workgroups of four
  * waves; every wave runs 8 independent accumulation chains of iters
- * v_mfma_f32_32x32x16_bf16 each on operands of ones, so the work is exactly
- *   n_workgroups * 4 * 8 * iters * 32768 flops
- * and every accumulator element ends at 16 * iters.
- *   sink [dev] fp32 [n_workgroups * 256]: each entry 128 * iters (exact), the
- *        proof the work ran; owned by the caller.
- * n_workgroups in [1, 1 << 20], iters in [1, 65536]; asynchronous on stream. */
-sa_status sa_measure_mfma_peak(int32_t n_workgroups, int32_t iters, float* sink, void* stream);
+ * v_mfma_f32_32x32x16_bf16 each, so the work is exactly
+ *   n_workgroups * 4 * 8 * iters * 32768 flops.
+ * operands = 0: every operand is 1.0 and every accumulator element ends at
+ *   16 * iters; sink entries are 128 * iters (exact).
+ * operands = 1: pseudo-random bf16 operands in [-1, 1), as matrix work on real
+ *   data has (the chip's power limit holds a lower clock for them).  Lane l of
+ *   global thread t = 256 * workgroup + thread holds four A and four B
+ *   fragments; element e (0..7) of fragment f (A: f = 0..3, B: f = 4..7) is
+ *   bf16 of ((h & 0xffff) - 32768) / 32768, rounded to nearest-even, with
+ *   h = lowbias32(64 t + 8 f + e) (x ^= x >> 16; x *= 0x7feb352d;
+ *   x ^= x >> 15; x *= 0x846ca68b; x ^= x >> 16, on uint32).  Chain c
+ *   multiplies A[c % 4] (rows: lane % 32, k: 8 * (lane / 32) + e) by B[c % 4]
+ *   (columns: lane % 32, same k); sink[t] = sum over c of element c of chain
+ *   c's accumulator, i.e. iters times the (row 8 (c / 4) + 4 (lane / 32) +
+ *   c % 4, column lane % 32) entry of that chain's 32 x 32 product, summed in
+ *   fp32.
+ *   sink [dev] fp32 [n_workgroups * 256]: the proof the work ran; owned by the
+ *        caller.
+ * n_workgroups in [1, 1 << 20], iters in [1, 65536], operands in {0, 1};
+ * asynchronous on stream. */
+sa_status sa_measure_mfma_peak(int32_t n_workgroups, int32_t iters, int32_t operands, float* sink, void* stream);
 
 /* The HBM streaming-read rate the GPU sustains: the denominator for the
  * decode path, which reads its selected KV blocks once (published MI355X

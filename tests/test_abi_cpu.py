@@ -442,18 +442,20 @@ def test_measure_probes_validation():
     import torch
     lib = SA._lib
     fake = ctypes.c_void_p(1 << 20)
-    assert lib.sa_measure_mfma_peak(0, 16, fake, None) == SA.SA_ERR_INVALID_ARG
-    assert lib.sa_measure_mfma_peak(256, 0, fake, None) == SA.SA_ERR_INVALID_ARG
-    assert lib.sa_measure_mfma_peak(256, 65537, fake, None) == SA.SA_ERR_INVALID_ARG
-    assert lib.sa_measure_mfma_peak(256, 16, None, None) == SA.SA_ERR_INVALID_ARG
-    assert lib.sa_measure_mfma_peak(256, 16, ctypes.c_void_p((1 << 20) + 2), None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(0, 16, 0, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 0, 0, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 65537, 1, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 16, 2, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 16, -1, fake, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 16, 0, None, None) == SA.SA_ERR_INVALID_ARG
+    assert lib.sa_measure_mfma_peak(256, 16, 0, ctypes.c_void_p((1 << 20) + 2), None) == SA.SA_ERR_INVALID_ARG
     assert lib.sa_measure_hbm_read(fake, 100, 256, fake, None) == SA.SA_ERR_INVALID_ARG   # not a multiple of 16
     assert lib.sa_measure_hbm_read(fake, 0, 256, fake, None) == SA.SA_ERR_INVALID_ARG
     assert lib.sa_measure_hbm_read(ctypes.c_void_p((1 << 20) + 8), 1 << 20, 256, fake, None) == SA.SA_ERR_INVALID_ARG
     assert lib.sa_measure_hbm_read(fake, 1 << 20, 0, fake, None) == SA.SA_ERR_INVALID_ARG
     assert lib.sa_measure_hbm_read(None, 1 << 20, 256, fake, None) == SA.SA_ERR_INVALID_ARG
     if not torch.cuda.is_available():
-        assert lib.sa_measure_mfma_peak(256, 16, fake, None) in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
+        assert lib.sa_measure_mfma_peak(256, 16, 1, fake, None) in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
         assert lib.sa_measure_hbm_read(fake, 1 << 20, 256, fake, None) in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
 
 
