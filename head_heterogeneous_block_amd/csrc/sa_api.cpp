@@ -746,7 +746,7 @@ size_t sa_select_workspace_size(const sa_attn_desc* desc, const sa_head_budget* 
 
 sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budgets, const void* q, const void* k,
                            const float* k_pooled, int32_t* block_idx, int32_t* block_cnt, int32_t kmax,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           float* key_norms, void* workspace, size_t workspace_bytes, void* stream) {
   if (!desc) return fail(SA_ERR_INVALID_ARG, "desc is NULL");
   const bool prefill = is_prefill(desc);
   sa_status s = check_desc(desc, prefill);
@@ -756,6 +756,8 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
   if (!aligned16(q) || !aligned16(k) || (k_pooled && !aligned16(k_pooled)))
     return fail(SA_ERR_INVALID_ARG, "q, k and k_pooled must be 16-byte aligned");
   int32_t need = 0;
+  if (reinterpret_cast<uintptr_t>(key_norms) & 3) return fail(SA_ERR_INVALID_ARG, "key_norms must be 4-byte aligned");
+  if (!prefill && key_norms) return fail(SA_ERR_INVALID_ARG, "key_norms is for prefill only");
   if (prefill) {
     if (k_pooled) return fail(SA_ERR_INVALID_ARG, "k_pooled must be NULL for prefill");
     sa_prefill_block_counts(desc, budgets, nullptr, &need);
@@ -799,6 +801,7 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
     pp.s2 = desc->k_stride[2];
     pp.out = kp;
     pp.heads = desc->n_kv_heads;
+    pp.norm_max = key_norms;
     if ((e = sa::launch_pool(pp, desc->dtype, D, desc->batch, st)) != hipSuccess) return hip_fail(e, "pool K");
     sa::PrefillSelectParams sp{};
     sp.q = q;
@@ -896,7 +899,7 @@ size_t sa_prefill_workspace_size(const sa_attn_desc* desc, int32_t kmax, int32_t
 
 static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
                               float* lse, const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
-                              const int32_t* bin_offsets, const int32_t* items_by_bin, int32_t n_bins,
+                              const float* key_norms, const int32_t* bin_offsets, const int32_t* items_by_bin, int32_t n_bins,
                               const int32_t* queue_offsets, int32_t n_queues, int32_t out_f32, void* workspace,
                               size_t workspace_bytes, void* stream, uint64_t* wg_times = nullptr) {
   sa_status s = check_desc(desc, true);
@@ -905,6 +908,7 @@ static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const voi
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(SA_ERR_INVALID_ARG, "q, k, v, o must be 16-byte aligned");
   if (kmax < 1) return fail(SA_ERR_INVALID_ARG, "kmax must be >= 1");
+  if (reinterpret_cast<uintptr_t>(key_norms) & 3) return fail(SA_ERR_INVALID_ARG, "key_norms must be 4-byte aligned");
   if (bin_offsets && !items_by_bin) return fail(SA_ERR_INVALID_ARG, "bin_offsets without items_by_bin");
   if (items_by_bin && n_bins < 1) return fail(SA_ERR_INVALID_ARG, "n_bins must be >= 1");
   const bool queue = items_by_bin && !bin_offsets;
@@ -964,6 +968,7 @@ static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const voi
   if (wg_times && (reinterpret_cast<uintptr_t>(wg_times) & 7))
     return fail(SA_ERR_INVALID_ARG, "wg_times must be 8-byte aligned");
   p.wg_times = wg_times;
+  p.key_norms = key_norms;
   if (g_debug.load()) {
     const int NB = int(nb);
     if ((s = check_lists(block_idx, block_cnt, n_tiles, kmax, [NB](int64_t t) { return int32_t(t % NB) + 1; },
@@ -980,27 +985,29 @@ static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const voi
 
 sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k, const void* v, void* o,
                                  float* lse, const int32_t* block_idx, const int32_t* block_cnt, int32_t kmax,
-                                 const int32_t* bin_offsets, const int32_t* items_by_bin, int32_t n_bins,
-                                 int32_t out_f32, void* workspace, size_t workspace_bytes, void* stream) {
-  return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, bin_offsets, items_by_bin, n_bins, nullptr,
-                      1, out_f32, workspace, workspace_bytes, stream);
+                                 const float* key_norms, const int32_t* bin_offsets, const int32_t* items_by_bin,
+                                 int32_t n_bins, int32_t out_f32, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, key_norms, bin_offsets, items_by_bin, n_bins,
+                      nullptr, 1, out_f32, workspace, workspace_bytes, stream);
 }
 
 sa_status sa_sparse_attn_prefill_queues(const sa_attn_desc* desc, const void* q, const void* k, const void* v,
                                         void* o, float* lse, const int32_t* block_idx, const int32_t* block_cnt,
-                                        int32_t kmax, const int32_t* queue_offsets, int32_t n_queues,
+                                        int32_t kmax, const float* key_norms, const int32_t* queue_offsets,
+                                        int32_t n_queues,
                                         const int32_t* order, int32_t n_workgroups, int32_t out_f32, void* workspace,
                                         size_t workspace_bytes, void* stream) {
   if (n_queues < 1 || n_queues > kMaxQueues)
     return fail(SA_ERR_INVALID_ARG, "n_queues %d outside [1, %d]", n_queues, kMaxQueues);
   if (!queue_offsets || !order) return fail(SA_ERR_INVALID_ARG, "queue_offsets or order is NULL");
-  return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, nullptr, order, n_workgroups, queue_offsets,
-                      n_queues, out_f32, workspace, workspace_bytes, stream);
+  return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, key_norms, nullptr, order, n_workgroups,
+                      queue_offsets, n_queues, out_f32, workspace, workspace_bytes, stream);
 }
 
 sa_status sa_sparse_attn_prefill_timed(const sa_attn_desc* desc, const void* q, const void* k, const void* v,
                                        void* o, float* lse, const int32_t* block_idx, const int32_t* block_cnt,
-                                       int32_t kmax, const int32_t* bin_offsets, const int32_t* items_by_bin,
+                                       int32_t kmax, const float* key_norms, const int32_t* bin_offsets, const int32_t* items_by_bin,
                                        int32_t n_bins, const int32_t* queue_offsets, int32_t n_queues,
                                        int32_t out_f32, uint64_t* wg_times, void* workspace, size_t workspace_bytes,
                                        void* stream) {
@@ -1012,7 +1019,7 @@ sa_status sa_sparse_attn_prefill_timed(const sa_attn_desc* desc, const void* q, 
   } else {
     n_queues = 1;
   }
-  return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, bin_offsets, items_by_bin, n_bins,
+  return prefill_impl(desc, q, k, v, o, lse, block_idx, block_cnt, kmax, key_norms, bin_offsets, items_by_bin, n_bins,
                       queue_offsets, n_queues, out_f32, workspace, workspace_bytes, stream, wg_times);
 }
 

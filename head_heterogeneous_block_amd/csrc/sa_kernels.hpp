@@ -33,6 +33,9 @@ struct PoolParams {
   float* out;            // [batch][heads][nb][D] fp32, contiguous
   int heads, T, g, nb, blocks_per_wg;
   PageTable pages;       // g divides page_size
+  // nullable: [batch][heads][nb] fp32, the largest Euclidean norm of a row of
+  // each block (contiguous rows only, not with pages)
+  float* norm_max = nullptr;
 };
 hipError_t launch_pool(const PoolParams& p, int dtype, int D, int batch, hipStream_t stream);
 
@@ -128,6 +131,10 @@ struct PrefillParams {
   // nullable: workgroup w writes the constant clock (s_memrealtime) at its
   // start to wg_times[2 w] and at its end to wg_times[2 w + 1]
   uint64_t* wg_times = nullptr;
+  // nullable: [batch][Hkv][NB] fp32, an upper bound of the Euclidean norm of
+  // every key row of each key block (PoolParams::norm_max); lets the kernel
+  // skip the running-max check of steps whose scores cannot overflow
+  const float* key_norms = nullptr;
 };
 // grid = persistent bins, queue workers or tiles.  variant 0: the
 // 32-rows-per-wave kernel (B/32 waves); variant 1 (bf16, B = 128): the

@@ -40,6 +40,8 @@
 // than 2^kLazy (decided per wave; O and l are then rescaled), so p <= 2^kLazy;
 // l and O share m, so the quotient is unchanged.
 
+#include <climits>
+
 #include "sa_device.hpp"
 #include "sa_kernels.hpp"
 #include "sa_prefill_common.hpp"
@@ -56,6 +58,11 @@ using namespace prefill;
 struct StepAt : Step {
   uint64_t ka, va;
 };
+
+// log2 headroom a score may have over the running max before P could grow
+// past 2^kSafe; with P <= 2^64 neither P, the row sum nor O can overflow fp32
+// for any |v| below 1e13 over up to 2^20 keys.
+constexpr float kSafe = 64.f;
 
 template <typename T, int D, int B, bool kLse>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(PrefillParams p) {
@@ -182,6 +189,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   int q_next = 0;                           // queue mode: the item after the cursor's
   StepAt cur;
   cur.valid = 0;
+  const float* const knorm = p.key_norms;  // nullable
 
   auto item_tile = [&](int it, int& tile, int& cnt) {
     if (qmode) {
@@ -317,6 +325,15 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // (bf16-rounded for bf16 inputs), so O / l_run is a convex combination of V
   // rows with those weights; l_lse: the same sum before rounding, for lse only.
   float m_run = kNegInf, l_run = 0.f, l_lse = 0.f;
+  // With a key-norm table: |score| <= |q| * (the block's key-norm bound), so
+  // a step whose bound times qn_c2 = scale * log2(e) * |q| stays within kSafe
+  // of the running max for every row needs no row max (P <= 2^kSafe).
+  // kn_lim: the largest key-norm bound (bf16 bits, rounded down) for which
+  // that holds in every row of the wave, -1 when none (the row max is then
+  // taken).
+  float qn_c2 = 0.f;
+  int kn_lim = -1;
+  int t_knb = 0;  // key-norm table row of the tile's (batch, KV head)
   int t_bh = 0, t_m = 0;  // tile being accumulated
 
   auto start_tile = [&](const StepAt& s) {
@@ -338,6 +355,27 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     l_lse = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt) oacc[dt] = f32x16{};
+    kn_lim = -1;
+    if (knorm) {
+      const int G = COLD(G);
+      t_knb = ((s.bh / Hq) * (Hq / G) + (s.bh % Hq) / G) * COLD(NB);
+      float q2 = 0.f;
+#pragma unroll
+      for (int dg = 0; dg < C::kDG; ++dg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (C::kBf16) {
+            // plain FMAs (a v_dot2 chain over vector elements is mis-folded
+            // by ROCm 7.2's compiler)
+            const float lo = bf16_lo(qf[dg][e]), hi = bf16_hi(qf[dg][e]);
+            q2 = fmaf(lo, lo, fmaf(hi, hi, q2));
+          } else {
+            const float x = __uint_as_float(qf[dg][e]);
+            q2 = fmaf(x, x, q2);
+          }
+        }
+      qn_c2 = __builtin_sqrtf(sum_xor32(q2)) * c2;
+    }
   };
 
   auto finish_tile = [&]() {
@@ -562,6 +600,12 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   qk(0, sa);
 
   auto iteration = [&](int slot, f32x16(&sc)[2], f32x16(&sn)[2]) -> bool {
+    // the step's key-norm bound (bf16 bits rounded up; 0x7fff: no table),
+    // issued before the barrier so that its latency hides behind it (a scalar
+    // load, through the constant address space: a vector load would be waited
+    // for with vmcnt(0), which also waits for the gathers)
+    const uint32_t kn_raw = knorm ? ((const __attribute__((address_space(4))) uint32_t*)(uintptr_t)knorm)[t_knb + s0.n]
+                                  : 0x7fff0000u;
     // K(i+1) and V(i) are in LDS; every wave is done with the slots refilled here
     wait_loads();
     __syncthreads();
@@ -570,9 +614,13 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const bool pipe = s1.valid && s1.item == s0.item;
     // rare: masking (causal diagonal, tail, or an invisible step)
     const int key0 = s0.hs * kKS;
-    if ((s0.n == s0.m && key0 + kKS - 1 > wave * 32) || s0.n * B + key0 + kKS > S) apply_mask(s0, sc);
-    // rare: raise the running max (always at the first step of a tile)
-    {
+    const bool masked = (s0.n == s0.m && key0 + kKS - 1 > wave * 32) || s0.n * B + key0 + kKS > S;
+    if (masked) apply_mask(s0, sc);
+    // rare: the row max and raising the running max (always at the first
+    // step of a tile; with a key-norm table only where the bound allows more
+    // than kSafe over the running max)
+    const int kn0 = int((kn_raw + 0xffffu) >> 16);
+    if (kn0 > kn_lim) {
       // row max: one v_max3 per pair of scores
       float mx = kNegInf;
 #pragma unroll
@@ -589,6 +637,15 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
         for (int dt = 0; dt < C::kDT; ++dt) oacc[dt] *= alpha;
         m_run = m_new;
+      }
+      if (knorm) {
+        // largest key-norm bound b with qn_c2 * b <= m_run + kSafe in every
+        // row (a row with q = 0 allows any; one with no max yet, none)
+        const float lim = qn_c2 > 0.f ? (m_run + kSafe) / qn_c2 : __builtin_huge_valf();
+        // non-negative floats order as their bits; shifted by one so that
+        // "none" (-1) is the unsigned minimum
+        const uint32_t u = lim >= 0.f ? (__float_as_uint(lim) >> 16) + 1u : 0u;  // bf16 bits, rounded down
+        kn_lim = __builtin_amdgcn_readfirstlane(int(wave_umin(u)) - 1);
       }
     }
     fused(slot, sc, sn);  // S(i+1) is speculative when step i+1 starts a new tile

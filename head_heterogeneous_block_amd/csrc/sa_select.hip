@@ -28,12 +28,14 @@ namespace {
 // One workgroup (256 threads) pools `blocks_per_wg` consecutive blocks of one
 // (batch, head).  Each thread owns one 16-byte column chunk and a strided set
 // of rows; row groups are combined through LDS.
-template <typename T, int D>
+template <typename T, int D, bool kNorm>
 __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
   constexpr int kE = 16 / int(sizeof(T));  // elements per chunk
   constexpr int kCh = D / kE;              // chunks per row
   constexpr int kRG = 256 / kCh;           // row groups
+  static_assert(kCh == 8 || kCh == 16 || kCh == 32, "a row's chunks are 8, 16 or 32 consecutive lanes");
   __shared__ float part[kRG][D + 1];
+  __shared__ float nrm[kRG];
   const int tid = threadIdx.x;
   const int ch = tid % kCh, rg = tid / kCh;
   const int h = blockIdx.y, bi = blockIdx.z;
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
     float acc[kE];
 #pragma unroll
     for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+    float n2max = 0.f;  // kNorm: largest squared norm among this row group's rows
     // eight rows' loads in flight per thread, then summed in row order (rows
     // past the block end read as zeros, which leave the sums unchanged)
     for (int r0 = rg; r0 < cnt; r0 += 8 * kRG) {
@@ -83,6 +86,33 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
           for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(w[u][e]);
         }
       }
+      if constexpr (kNorm) {
+        // squared norm of each of the eight rows: this lane's chunk, then the
+        // row's kCh consecutive lanes
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          // plain FMAs: ROCm 7.2's compiler folds chains of v_dot2 over
+          // elements of a vector wrongly (some pairs read twice)
+          float q2 = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (sizeof(T) == 2) {
+              const float lo = bf16_lo(w[u][e]), hi = bf16_hi(w[u][e]);
+              q2 = fmaf(lo, lo, fmaf(hi, hi, q2));
+            } else {
+              const float x = __uint_as_float(w[u][e]);
+              q2 = fmaf(x, x, q2);
+            }
+          }
+          if constexpr (kCh == 8) q2 = sum8(q2);
+          else q2 = row_sum16(q2);
+          if constexpr (kCh == 32) q2 += __shfl_xor(q2, 16);
+          n2max = fmaxf(n2max, q2);
+        }
+      }
+    }
+    if constexpr (kNorm) {
+      if (ch == 0) nrm[rg] = n2max;
     }
 #pragma unroll
     for (int e = 0; e < kE; ++e) part[rg][ch * kE + e] = acc[e];
@@ -92,6 +122,13 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p) {
 #pragma unroll 8
       for (int r = 0; r < kRG; ++r) s += part[r][d];
       p.out[(((int64_t)bi * p.heads + h) * p.nb + n) * D + d] = s / float(cnt);
+    }
+    if constexpr (kNorm) {
+      if (tid == 0) {
+        float m2 = 0.f;
+        for (int r = 0; r < kRG; ++r) m2 = fmaxf(m2, nrm[r]);
+        p.norm_max[((int64_t)bi * p.heads + h) * p.nb + n] = __builtin_sqrtf(m2);
+      }
     }
     __syncthreads();
   }
@@ -764,11 +801,23 @@ hipError_t launch_pool(const PoolParams& p, int dtype, int D, int batch, hipStre
                         p.pages.pages_per_head < 1))
     return hipErrorInvalidValue;
   dim3 grid((p.nb + p.blocks_per_wg - 1) / p.blocks_per_wg, p.heads, batch);
-  if (dtype == 0 && D == 128) hipLaunchKernelGGL((pool_kernel<bf16_t, 128>), grid, dim3(256), 0, stream, p);
-  else if (dtype == 0 && D == 64) hipLaunchKernelGGL((pool_kernel<bf16_t, 64>), grid, dim3(256), 0, stream, p);
-  else if (dtype == 1 && D == 128) hipLaunchKernelGGL((pool_kernel<float, 128>), grid, dim3(256), 0, stream, p);
-  else if (dtype == 1 && D == 64) hipLaunchKernelGGL((pool_kernel<float, 64>), grid, dim3(256), 0, stream, p);
-  else return hipErrorInvalidValue;
+  const bool nrm = p.norm_max != nullptr;
+  if (nrm && p.pages.table) return hipErrorInvalidValue;
+  if (dtype == 0 && D == 128) {
+    if (nrm) hipLaunchKernelGGL((pool_kernel<bf16_t, 128, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((pool_kernel<bf16_t, 128, false>), grid, dim3(256), 0, stream, p);
+  } else if (dtype == 0 && D == 64) {
+    if (nrm) hipLaunchKernelGGL((pool_kernel<bf16_t, 64, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((pool_kernel<bf16_t, 64, false>), grid, dim3(256), 0, stream, p);
+  } else if (dtype == 1 && D == 128) {
+    if (nrm) hipLaunchKernelGGL((pool_kernel<float, 128, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((pool_kernel<float, 128, false>), grid, dim3(256), 0, stream, p);
+  } else if (dtype == 1 && D == 64) {
+    if (nrm) hipLaunchKernelGGL((pool_kernel<float, 64, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((pool_kernel<float, 64, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

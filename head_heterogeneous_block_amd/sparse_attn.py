@@ -108,15 +108,15 @@ _SIG = {
     "sa_decode_pooled_size": (ctypes.c_size_t, [_descp, _budp]),
     "sa_pool_keys_decode": (ctypes.c_int32, [_descp, _budp, _P, _P, _P]),
     "sa_select_workspace_size": (ctypes.c_size_t, [_descp, _budp, ctypes.c_int32]),
-    "sa_select_blocks": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_size_t,
+    "sa_select_blocks": (ctypes.c_int32, [_descp, _budp, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t,
                                           _P]),
     "sa_prefill_workspace_size": (ctypes.c_size_t, [_descp, ctypes.c_int32, ctypes.c_int32]),
-    "sa_sparse_attn_prefill": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+    "sa_sparse_attn_prefill": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
                                                 ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t, _P]),
-    "sa_sparse_attn_prefill_queues": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _i32p,
+    "sa_sparse_attn_prefill_queues": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _i32p,
                                                        ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P,
                                                        ctypes.c_size_t, _P]),
-    "sa_sparse_attn_prefill_timed": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+    "sa_sparse_attn_prefill_timed": (ctypes.c_int32, [_descp, _P, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
                                                       ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int32, _P, _P,
                                                       ctypes.c_size_t, _P]),
     "sa_decode_workspace_size": (ctypes.c_size_t, [_descp, _budp, ctypes.c_int32]),
@@ -409,42 +409,46 @@ def sa_pool_keys_decode(desc: sa_attn_desc, budgets, k: torch.Tensor, k_pooled: 
 
 def sa_select_blocks(desc: sa_attn_desc, budgets, q: torch.Tensor, k: torch.Tensor,
                      k_pooled: Optional[torch.Tensor], block_idx: torch.Tensor, block_cnt: torch.Tensor,
-                     kmax: int, workspace: torch.Tensor) -> None:
+                     kmax: int, workspace: torch.Tensor, key_norms: Optional[torch.Tensor] = None) -> None:
     _check(_lib.sa_select_blocks(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(k_pooled), _ptr(block_idx),
-                                 _ptr(block_cnt), kmax, _ptr(workspace), workspace.numel(), _stream(q)))
+                                 _ptr(block_cnt), kmax, _ptr(key_norms), _ptr(workspace), workspace.numel(),
+                                 _stream(q)))
 
 
 def sa_sparse_attn_prefill(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
                            bin_offsets=None, items_by_bin=None, n_bins: int = 0, out_f32: bool = False,
-                           workspace: Optional[torch.Tensor] = None) -> None:
+                           workspace: Optional[torch.Tensor] = None, key_norms: Optional[torch.Tensor] = None) -> None:
     ws = workspace
     _check(_lib.sa_sparse_attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                       _ptr(block_idx), _ptr(block_cnt), kmax, _ptr(bin_offsets),
+                                       _ptr(block_idx), _ptr(block_cnt), kmax, _ptr(key_norms), _ptr(bin_offsets),
                                        _ptr(items_by_bin), n_bins, 1 if out_f32 else 0, _ptr(ws),
                                        0 if ws is None else ws.numel(), _stream(q)))
 
 
 def sa_sparse_attn_prefill_queues(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
                                   queue_offsets: np.ndarray, order, n_workgroups: int, out_f32: bool = False,
-                                  workspace: Optional[torch.Tensor] = None) -> None:
+                                  workspace: Optional[torch.Tensor] = None,
+                                  key_norms: Optional[torch.Tensor] = None) -> None:
     off = np.ascontiguousarray(queue_offsets, dtype=np.int32)
     ws = workspace
     _check(_lib.sa_sparse_attn_prefill_queues(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                              _ptr(block_idx), _ptr(block_cnt), kmax, off.ctypes.data_as(_i32p),
+                                              _ptr(block_idx), _ptr(block_cnt), kmax, _ptr(key_norms),
+                                              off.ctypes.data_as(_i32p),
                                               off.size - 1, _ptr(order), n_workgroups, 1 if out_f32 else 0,
                                               _ptr(ws), 0 if ws is None else ws.numel(), _stream(q)))
 
 
 def sa_sparse_attn_prefill_timed(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
                                  bin_offsets, items_by_bin, n_bins: int, queue_offsets: Optional[np.ndarray],
-                                 out_f32: bool, wg_times: torch.Tensor, workspace: Optional[torch.Tensor] = None) -> None:
+                                 out_f32: bool, wg_times: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                                 key_norms: Optional[torch.Tensor] = None) -> None:
     """A prefill launch recording each workgroup's start and end on the constant
     clock into wg_times (int64 [2 * grid])."""
     off = None if queue_offsets is None else np.ascontiguousarray(queue_offsets, dtype=np.int32)
     ws = workspace
     _check(_lib.sa_sparse_attn_prefill_timed(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(block_idx), _ptr(block_cnt), kmax,
-        _ptr(bin_offsets), _ptr(items_by_bin), n_bins, None if off is None else off.ctypes.data_as(_i32p),
+        _ptr(key_norms), _ptr(bin_offsets), _ptr(items_by_bin), n_bins, None if off is None else off.ctypes.data_as(_i32p),
         0 if off is None else off.size - 1, 1 if out_f32 else 0, _ptr(wg_times), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(q)))
 
@@ -582,11 +586,15 @@ class PrefillPlan:
     (default 8, one per XCD of MI355X) cuts the "kv_tiers" queue into that many
     partitions (sa_lpt_queue_partition): runs of one (load tier, sequence, KV
     head), of at most ``queue_chunk`` tiles (0: no limit), placed by LPT, each
-    partition in the tiered order; other ``queue_group`` orders use one queue."""
+    partition in the tiered order; other ``queue_group`` orders use one queue.
+    ``key_norms``: the selection also writes each key block's largest key-row
+    norm, and the attention uses it to skip the per-step row max where the
+    scores cannot overflow (False: every step takes the row max)."""
 
     def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
                  kernel_variant: int = 0, bin_order: str = "index", xcd_groups: int = 0, xcd_chunk: int = 64,
-                 queue: bool = False, queue_group: str = "kv_tiers", queues: int = 8, queue_chunk: int = 0):
+                 queue: bool = False, queue_group: str = "kv_tiers", queues: int = 8, queue_chunk: int = 0,
+                 key_norms: bool = True):
         self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_prefill_block_counts(self.desc, self.budgets)
@@ -599,6 +607,8 @@ class PrefillPlan:
         self.block_cnt = torch.empty((q.shape[0], q.shape[1], self.nb), dtype=torch.int32, device=dev)
         self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
         self.attn_ws = _workspace(sa_prefill_workspace_size(self.desc, self.kmax, n_bins), dev)
+        self.key_norms = (torch.empty((q.shape[0], k.shape[1], self.nb), dtype=torch.float32, device=dev)
+                          if key_norms else None)
         self.queue = queue
         self.queue_offsets = None
         self.bin_load = None
@@ -628,16 +638,17 @@ class PrefillPlan:
 
     def select(self, q, k) -> None:
         sa_select_blocks(self.desc, self.budgets, q, k, None, self.block_idx, self.block_cnt, self.kmax,
-                         self.select_ws)
+                         self.select_ws, self.key_norms)
 
     def attend(self, q, k, v, o, lse=None) -> None:
         if self.queue and self.queue_offsets is not None:
             sa_sparse_attn_prefill_queues(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
                                           self.queue_offsets, self.items_by_bin, self.n_bins, self.out_f32,
-                                          self.attn_ws)
+                                          self.attn_ws, self.key_norms)
             return
         sa_sparse_attn_prefill(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
-                               self.bin_offsets, self.items_by_bin, self.n_bins, self.out_f32, self.attn_ws)
+                               self.bin_offsets, self.items_by_bin, self.n_bins, self.out_f32, self.attn_ws,
+                               self.key_norms)
 
     def grid(self) -> int:
         """Workgroups of a launch: the persistent workgroups, or one per tile."""
@@ -650,7 +661,7 @@ class PrefillPlan:
         sa_sparse_attn_prefill_timed(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
                                      self.bin_offsets, self.items_by_bin, self.n_bins if self.items_by_bin is not None
                                      else 0, self.queue_offsets if self.queue else None, self.out_f32, t,
-                                     self.attn_ws)
+                                     self.attn_ws, self.key_norms)
         return t
 
 

@@ -267,11 +267,15 @@ size_t sa_select_workspace_size(const sa_attn_desc* desc, const sa_head_budget* 
  * decode [batch][n_q_heads][kmax]: the kept blocks in ascending order, -1
  * padded; block_cnt int32 [batch][n_q_heads][n_blocks] (prefill) or
  * [batch][n_q_heads] (decode).  kmax must be >= the largest count
- * (sa_*_block_counts). */
+ * (sa_*_block_counts).
+ * key_norms [dev] fp32 [batch][n_kv_heads][n_blocks], prefill only (NULL:
+ * not written; must be NULL for decode): the largest Euclidean norm of a key
+ * row of each key block, computed in fp32 from the same pass over k that
+ * pools it.  sa_sparse_attn_prefill* take it to skip work (see there). */
 sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budgets,
                            const void* q, const void* k, const float* k_pooled,
                            int32_t* block_idx, int32_t* block_cnt, int32_t kmax,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           float* key_norms, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The whole host schedule of a prefill layer's attention tiles in one call
  * (host, synchronous): block counts from the budgets (the tile loads), the
@@ -340,10 +344,21 @@ size_t sa_prefill_workspace_size(const sa_attn_desc* desc, int32_t kmax, int32_t
  *     calls that share a workspace must not overlap;
  *   - both NULL: one workgroup per tile in natural order (n_bins ignored).
  *   Every tile must appear exactly once.  workspace may be NULL except in the
- *   work-queue mode. */
+ *   work-queue mode.
+ *   key_norms [dev] fp32 [batch][n_kv_heads][n_blocks] (may be NULL): for each
+ *   key block an upper bound of the Euclidean norm of its key rows, as
+ *   sa_select_blocks writes it for the same k.  The kernel keeps the softmax
+ *   in the exp2 domain relative to a running max per row, which it must raise
+ *   before a score could push a probability past what fp32 can accumulate.
+ *   With the table, a step whose scores are bounded by scale * |q| * (the
+ *   block's bound) <= running max + 64 (in log2 units) needs no row max (the
+ *   first step of a tile always takes it); without it, every step takes the
+ *   row max.  The normalised result is the same softmax either way (the
+ *   running max cancels; only the bf16 rounding of the probabilities moves).
+ *   A table that is not an upper bound for k can overflow the accumulators. */
 sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k,
                                  const void* v, void* o, float* lse, const int32_t* block_idx,
-                                 const int32_t* block_cnt, int32_t kmax,
+                                 const int32_t* block_cnt, int32_t kmax, const float* key_norms,
                                  const int32_t* bin_offsets, const int32_t* items_by_bin,
                                  int32_t n_bins, int32_t out_f32, void* workspace,
                                  size_t workspace_bytes, void* stream);
@@ -362,7 +377,7 @@ sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const 
  * SA_ERR_INVALID_ARG; otherwise as sa_sparse_attn_prefill. */
 sa_status sa_sparse_attn_prefill_queues(const sa_attn_desc* desc, const void* q, const void* k,
                                         const void* v, void* o, float* lse, const int32_t* block_idx,
-                                        const int32_t* block_cnt, int32_t kmax,
+                                        const int32_t* block_cnt, int32_t kmax, const float* key_norms,
                                         const int32_t* queue_offsets, int32_t n_queues,
                                         const int32_t* order, int32_t n_workgroups, int32_t out_f32,
                                         void* workspace, size_t workspace_bytes, void* stream);
@@ -381,7 +396,7 @@ sa_status sa_sparse_attn_prefill_queues(const sa_attn_desc* desc, const void* q,
  *   rate (hipDeviceAttributeWallClockRate). */
 sa_status sa_sparse_attn_prefill_timed(const sa_attn_desc* desc, const void* q, const void* k,
                                        const void* v, void* o, float* lse, const int32_t* block_idx,
-                                       const int32_t* block_cnt, int32_t kmax,
+                                       const int32_t* block_cnt, int32_t kmax, const float* key_norms,
                                        const int32_t* bin_offsets, const int32_t* items_by_bin,
                                        int32_t n_bins, const int32_t* queue_offsets, int32_t n_queues,
                                        int32_t out_f32, uint64_t* wg_times, void* workspace,

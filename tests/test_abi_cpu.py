@@ -224,8 +224,8 @@ def test_slices_beyond_32_bit_offsets_rejected():
     b = SA.make_budgets({"min_blocks": [2] * 4, "ratio_q16": [0] * 4, "n_sink": [1] * 4, "n_local": [1] * 4,
                          "granularity": [128] * 4})
     fake = ctypes.c_void_p(1 << 20)
-    st = SA._lib.sa_sparse_attn_prefill(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 2, None, None, 0,
-                                        0, None, 0, None)
+    st = SA._lib.sa_sparse_attn_prefill(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 2, None, None, None,
+                                        0, 0, None, 0, None)
     assert st == SA.SA_ERR_UNSUPPORTED and "2 GiB" in SA._lib.sa_last_error().decode()
     qd = torch.empty((1, 4, 128), dtype=torch.bfloat16, device="meta")
     kd = torch.empty_strided((1, 1, L, 128), (L * 32768, L * 32768, 32768, 1), dtype=torch.bfloat16,
@@ -246,18 +246,24 @@ def test_device_calls_fail_cleanly_without_gpu():
     b = _bud()
     fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation and the device check come first
     lib = SA._lib
-    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 64, fake, 1 << 30, None)
+    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 64, None, fake, 1 << 30, None)
     assert st in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
-    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 1, fake, 1 << 30, None)
+    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 1, None, fake, 1 << 30, None)
     assert st == SA.SA_ERR_INVALID_ARG  # kmax below the largest count, caught before the device check
-    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 64, fake, 16, None)
+    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 64, None, fake, 16, None)
     assert st == SA.SA_ERR_WORKSPACE
-    st = lib.sa_sparse_attn_prefill(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 16, None, None, 0, 0,
-                                    None, 0, None)
+    st = lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 64, ctypes.c_void_p((1 << 20) + 2),
+                              fake, 1 << 30, None)
+    assert st == SA.SA_ERR_INVALID_ARG  # misaligned key_norms
+    st = lib.sa_sparse_attn_prefill(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 16, None, None, None, 0,
+                                    0, None, 0, None)
     assert st in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
     st = lib.sa_sparse_attn_prefill(ctypes.byref(d), ctypes.c_void_p(3), fake, fake, fake, None, fake, fake, 16,
-                                    None, None, 0, 0, None, 0, None)
+                                    None, None, None, 0, 0, None, 0, None)
     assert st == SA.SA_ERR_INVALID_ARG  # misaligned q
+    st = lib.sa_sparse_attn_prefill(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 16,
+                                    ctypes.c_void_p((1 << 20) + 2), None, None, 0, 0, None, 0, None)
+    assert st == SA.SA_ERR_INVALID_ARG  # misaligned key_norms
 
 
 def _paged_call(page_size=128, max_pages=8, pages_per_head=20, dtype="bf16", table=True, pages_null=False,
@@ -405,7 +411,7 @@ def test_prefill_queues_validation():
 
     def call(off, nq=None, nwg=8, ws=256):
         a = np.ascontiguousarray(off, dtype=np.int32)
-        return lib.sa_sparse_attn_prefill_queues(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 16,
+        return lib.sa_sparse_attn_prefill_queues(ctypes.byref(d), fake, fake, fake, fake, None, fake, fake, 16, None,
                                                  a.ctypes.data_as(SA._i32p), a.size - 1 if nq is None else nq,
                                                  fake, nwg, 0, fake, ws, None)
 
@@ -557,11 +563,11 @@ def test_prefill_selection_block_limit():
         SA.sa_prefill_block_counts(d, b)
     assert e.value.status == SA.SA_ERR_UNSUPPORTED
     fake = ctypes.c_void_p(1 << 20)
-    st = SA._lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 8193, fake, 1 << 40, None)
+    st = SA._lib.sa_select_blocks(ctypes.byref(d), b, fake, fake, None, fake, fake, 8193, None, fake, 1 << 40, None)
     assert st == SA.SA_ERR_UNSUPPORTED
     q8 = q[:, :, : 8192 * 64]
     d8 = SA.make_prefill_desc(q8, q8, q8, q8, 64)
     _, kmax8 = SA.sa_prefill_block_counts(d8, b)
-    st = SA._lib.sa_select_blocks(ctypes.byref(d8), b, fake, fake, None, fake, fake, kmax8, fake, 1 << 40, None)
+    st = SA._lib.sa_select_blocks(ctypes.byref(d8), b, fake, fake, None, fake, fake, kmax8, None, fake, 1 << 40, None)
     if not torch.cuda.is_available():
         assert st in (SA.SA_ERR_NO_DEVICE, SA.SA_ERR_HIP)
