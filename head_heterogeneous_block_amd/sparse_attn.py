@@ -650,14 +650,27 @@ class PrefillPlan:
                                self.bin_offsets, self.items_by_bin, self.n_bins, self.out_f32, self.attn_ws,
                                self.key_norms)
 
+    def share_tables(self, other: "PrefillPlan") -> None:
+        """Use the selection outputs of another plan of the same shape and
+        budgets (block lists, counts and key-norm table) instead of this plan's
+        own, e.g. to run the same selection under another schedule."""
+        if other.block_idx.shape != self.block_idx.shape:
+            raise ValueError("plans of different shapes")
+        self.block_idx = other.block_idx
+        self.block_cnt = other.block_cnt
+        self.key_norms = other.key_norms
+
     def grid(self) -> int:
         """Workgroups of a launch: the persistent workgroups, or one per tile."""
         return self.n_bins if self.items_by_bin is not None else int(self.counts.size)
 
-    def attend_timed(self, q, k, v, o, lse=None) -> torch.Tensor:
+    def attend_timed(self, q, k, v, o, lse=None, stamps: Optional[torch.Tensor] = None) -> torch.Tensor:
         """attend(), also recording each workgroup's start and end on the GPU's
-        constant clock; returns int64 [grid, 2]."""
-        t = torch.zeros((self.grid(), 2), dtype=torch.int64, device=q.device)
+        constant clock into ``stamps`` (int64 [grid, 2], allocated if None);
+        returns it."""
+        t = stamps if stamps is not None else torch.zeros((self.grid(), 2), dtype=torch.int64, device=q.device)
+        if t.dtype != torch.int64 or t.numel() < 2 * self.grid():
+            raise ValueError("stamps must be int64 with 2 * grid entries")
         sa_sparse_attn_prefill_timed(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
                                      self.bin_offsets, self.items_by_bin, self.n_bins if self.items_by_bin is not None
                                      else 0, self.queue_offsets if self.queue else None, self.out_f32, t,
