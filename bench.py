@@ -237,15 +237,18 @@ def tail_report(spec_name, dev, stream, n_bins, queues, inp=None):
     spec = W.BY_NAME[spec_name] if isinstance(spec_name, str) else spec_name
     if inp is None:
         inp = W.make_prefill(spec, W.seed_of(spec), device=dev)
-    base = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins, queue=True, queues=queues)
+    base = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins, queue=True, queues=queues,
+                          queue_group="kv_tiers")
     base.select(inp.q, inp.k)
     o = torch.empty_like(inp.q)
     loads = base.counts.reshape(-1).astype(np.int64)
     lpt_pred = SA.sa_lpt_schedule(loads.tolist(), n_bins)[3]
     plans = {
         "queue_xcd_partitions": (base, float(lpt_pred.max() / lpt_pred.mean())),
-        "queue_one": (SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins, queue=True, queues=1),
-                      float(lpt_pred.max() / lpt_pred.mean())),
+        "queue_one": (SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins, queue=True, queues=1,
+                                     queue_group="kv_tiers"), float(lpt_pred.max() / lpt_pred.mean())),
+        "queue_flat": (SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins, queue=True,
+                                      queue_group="flat"), float(lpt_pred.max() / lpt_pred.mean())),
         "lpt_bins": (SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=n_bins), None),
         "natural_grid": (SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=0), None),
     }
@@ -477,10 +480,15 @@ def main():
     print(f"[bench] prefill inputs {pspec.name} ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     n_bins = n_cu * args.bins_per_cu
     t0 = time.perf_counter()
-    # work queue: n_bins persistent workgroups take the tiles in load tiers,
-    # heaviest tier first, grouped by (sequence, KV head) inside a tier
+    # work queue: n_bins persistent workgroups take the tiles in the order the
+    # library picks for the size (SA_QUEUE_AUTO): beyond 256 query blocks per
+    # head, load tiers, heaviest tier first, grouped by (sequence, KV head)
+    # inside a tier and cut into one partition per XCD; up to 256, plain
+    # longest first on one queue
     plan = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
                           queues=args.queues)
+    default_order = ("load tiers, %d XCD partitions" % (len(plan.queue_offsets) - 1) if plan.queue_offsets is not None
+                     else "one queue (the library's choice for this size)")
     lpt_ms = (time.perf_counter() - t0) * 1e3
     o = torch.empty_like(pin.q)
     sel = lambda: plan.select(pin.q, pin.k)  # noqa: E731
@@ -616,18 +624,26 @@ def main():
         cont.items_by_bin = torch.arange(n_t, dtype=torch.int32, device=dev)
         cont.n_bins = n_bins
         ablation["contiguous_bins_ms"] = timed(lambda: cont.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
-        ablation["queue_xcd_partitions_ms" if args.queues > 1 else "queue_lpt_kv_tiers_ms"] = res["att_ms"]
+        ablation["default_order"] = default_order
+        ablation["default_ms"] = res["att_ms"]
+        if plan.queue_offsets is not None and args.queues == 8:
+            ablation["queue_xcd_partitions_ms"] = res["att_ms"]
+        else:
+            xq = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
+                                queue_group="kv_tiers", queues=8)
+            xq.share_tables(plan)
+            ablation["queue_xcd_partitions_ms"] = timed(lambda: xq.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+            del xq
         grouped = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
                                  queue_group="kv")
         grouped.share_tables(plan)
         ablation["queue_lpt_grouped_ms"] = timed(lambda: grouped.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
         del grouped
-        # the other of: one queue in load tiers / the same cut into one partition per XCD
+        # one queue in load tiers
         other = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
-                               queues=1 if args.queues > 1 else 8)
+                               queue_group="kv_tiers", queues=1)
         other.share_tables(plan)
-        ablation["queue_lpt_kv_tiers_ms" if args.queues > 1 else "queue_xcd_partitions_ms"] = timed(
-            lambda: other.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
+        ablation["queue_lpt_kv_tiers_ms"] = timed(lambda: other.attend(pin.q, pin.k, pin.v, o), stream, reps)[0]
         del other
         # the queue grouped by query head (heaviest head first) instead of by KV head
         byhead = SA.PrefillPlan(pin.q, pin.k, pin.v, pin.budget, pspec.block, n_bins=n_bins, queue=True,
@@ -692,8 +708,11 @@ def main():
                                f"Hkv={pspec.n_kv_heads}, D={pspec.head_dim}, block={pspec.block}) + decode "
                                f"{dspec.name} (batch={dspec.batch}, L={dspec.kv_len})",
                    "global_batch": 1, "seq_len": pspec.seq_len, "parallelism": "single GPU",
-                   "schedule": f"work queue: {n_bins} workgroups, tiles in load tiers (quarter octave) heaviest first, grouped by (sequence, KV head) within a tier"
-                   + (f"; cut into {args.queues} partitions (one per XCD) of (load tier, sequence, KV head) runs placed by LPT, workgroup w starting on partition w mod {args.queues} and moving on when it is empty" if args.queues > 1 else "")},
+                   "schedule": (f"work queue: {n_bins} workgroups, tiles in load tiers (quarter octave) heaviest first, grouped by (sequence, KV head) within a tier"
+                                + (f"; cut into {len(plan.queue_offsets) - 1} partitions (one per XCD) of (load tier, sequence, KV head) runs placed by LPT, workgroup w starting on partition w mod {len(plan.queue_offsets) - 1} and moving on when it is empty"
+                                   if plan.queue_offsets is not None else "")
+                                if plan.queue_offsets is not None or pspec.n_blocks > 256 else
+                                f"work queue: {n_bins} workgroups, one queue, tiles longest first (the library's order for up to 256 query blocks per head)")},
         "prefill": {"select_ms": res.get("sel_ms"), "select_p10_p90_ms": res.get("sel_p10_p90_ms"),
                     "attention_ms": res.get("att_ms"), "attention_p10_p90_ms": res.get("att_p10_p90_ms"),
                     "attention_ms_scrubbed": res.get("att_scrub_ms"),

@@ -215,7 +215,9 @@ DecodeSelectWs decode_select_ws(const sa_attn_desc* d, const sa_head_budget* b, 
 
 constexpr int kChunkAtoms = 40;  // atoms per decode attention wave: about one full round of waves at 128K
 constexpr int kAtomPad = 16;  // tokens an atom may reach past the cache end
-constexpr int kMaxQueues = sa::PrefillParams::kMaxQueues;  // work-queue partitions (one per XCD on MI355X)
+constexpr int kMaxQueues = sa::PrefillParams::kMaxQueues;
+// SA_QUEUE_AUTO: the largest query-block count per head that gets one queue, longest first
+constexpr int32_t kAutoFlatBlocks = 256;  // work-queue partitions (one per XCD on MI355X)
 
 struct DecodeAttnWs {
   size_t atoms, n_union, part_o, part_ml, total;
@@ -571,8 +573,23 @@ sa_status sa_prefill_schedule(const sa_attn_desc* desc, const sa_head_budget* bu
   // item = (b * Hq + h) * nb + m
   const auto bh_of = [&](int32_t it) { return it / nb; };
   if (o.kind == SA_SCHED_QUEUE) {
+    int32_t qgroup = o.queue_group, nq = o.n_queues;
+    if (qgroup == SA_QUEUE_AUTO) {
+      // Up to kAutoFlatBlocks query blocks per head, a tile is a large share of
+      // a workgroup's work and the start of the longest tiles decides the
+      // tail: plain longest first on one queue.  Beyond it, the tiered order
+      // in per-XCD partitions, whose workgroups share a KV head's blocks in
+      // their XCD's L2 (measured on MI355X: 32K tokens, 256 blocks, flat 3%
+      // ahead; 64K and 128K, the partitions 4% ahead of any one queue).
+      if (nb <= kAutoFlatBlocks) {
+        qgroup = SA_QUEUE_FLAT;
+        nq = 1;
+      } else {
+        qgroup = SA_QUEUE_KV_TIERS;
+      }
+    }
     std::vector<int32_t> group(n);
-    switch (o.queue_group) {
+    switch (qgroup) {
       case SA_QUEUE_KV_TIERS:
       case SA_QUEUE_KV:
         for (int32_t it = 0; it < n; ++it) group[it] = bh_of(it) / G;  // (b, KV head) = (b * Hq + h) / G
@@ -593,18 +610,18 @@ sa_status sa_prefill_schedule(const sa_attn_desc* desc, const sa_head_budget* bu
       default:
         return fail(SA_ERR_INVALID_ARG, "queue_group %d", o.queue_group);
     }
-    const int32_t* gp = o.queue_group == SA_QUEUE_FLAT ? nullptr : group.data();
-    if (o.queue_group == SA_QUEUE_KV_TIERS && o.n_queues > 1) {
-      if ((st = sa_lpt_queue_partition(loads.data(), gp, n, desc->batch * Hkv, o.n_queues, 4, o.queue_chunk, items,
+    const int32_t* gp = qgroup == SA_QUEUE_FLAT ? nullptr : group.data();
+    if (qgroup == SA_QUEUE_KV_TIERS && nq > 1) {
+      if ((st = sa_lpt_queue_partition(loads.data(), gp, n, desc->batch * Hkv, nq, 4, o.queue_chunk, items,
                                        offsets)))
         return st;
-      *n_offsets = o.n_queues + 1;
+      *n_offsets = nq + 1;
       return ok();
     }
-    if (o.n_queues != 1 && o.n_queues != 0 && o.queue_group != SA_QUEUE_KV_TIERS)
+    if (nq != 1 && nq != 0 && qgroup != SA_QUEUE_KV_TIERS)
       return fail(SA_ERR_INVALID_ARG, "n_queues > 1 needs queue_group SA_QUEUE_KV_TIERS");
-    st = o.queue_group == SA_QUEUE_KV_TIERS ? sa_lpt_queue_order_tiered(loads.data(), gp, n, 4, items)
-                                            : sa_lpt_queue_order(loads.data(), gp, n, items);
+    st = qgroup == SA_QUEUE_KV_TIERS ? sa_lpt_queue_order_tiered(loads.data(), gp, n, 4, items)
+                                     : sa_lpt_queue_order(loads.data(), gp, n, items);
     if (st) return st;
     offsets[0] = 0;
     offsets[1] = n;

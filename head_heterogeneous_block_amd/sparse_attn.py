@@ -75,7 +75,7 @@ class sa_prefill_schedule_opts(ctypes.Structure):
 
 
 SA_SCHED_GRID, SA_SCHED_BINS, SA_SCHED_BINS_XCD, SA_SCHED_QUEUE = 0, 1, 2, 3
-QUEUE_GROUPS = {"kv_tiers": 0, "kv": 1, "head": 2, "flat": 3}
+QUEUE_GROUPS = {"kv_tiers": 0, "kv": 1, "head": 2, "flat": 3, "auto": 4}
 
 
 class sa_kv_pages(ctypes.Structure):
@@ -579,10 +579,12 @@ class PrefillPlan:
     (sequence, KV head) onto ``xcd_groups`` cache partitions, then LPT inside.
     ``queue``: instead of fixed bins, the ``n_bins`` workgroups take the tiles
     longest first from a shared counter (the greedy rule applied online).
-    ``queue_group`` orders the queue: "kv_tiers" (default) in load tiers of a
-    quarter octave, heaviest first, grouped by (sequence, KV head) inside a
-    tier; "kv" grouped by (sequence, KV head) only; "head" grouped by query
-    head, heaviest head first; "flat" plain longest first.  ``queues`` > 1
+    ``queue_group`` orders the queue: "kv_tiers" in load tiers of a quarter
+    octave, heaviest first, grouped by (sequence, KV head) inside a tier; "kv"
+    grouped by (sequence, KV head) only; "head" grouped by query head,
+    heaviest head first; "flat" plain longest first; "auto" (default) the
+    library's choice by size (SA_QUEUE_AUTO: "flat" on one queue up to 256
+    query blocks per head, else "kv_tiers" in partitions).  ``queues`` > 1
     (default 8, one per XCD of MI355X) cuts the "kv_tiers" queue into that many
     partitions (sa_lpt_queue_partition): runs of one (load tier, sequence, KV
     head), of at most ``queue_chunk`` tiles (0: no limit), placed by LPT, each
@@ -593,7 +595,7 @@ class PrefillPlan:
 
     def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
                  kernel_variant: int = 0, bin_order: str = "index", xcd_groups: int = 0, xcd_chunk: int = 64,
-                 queue: bool = False, queue_group: str = "kv_tiers", queues: int = 8, queue_chunk: int = 0,
+                 queue: bool = False, queue_group: str = "auto", queues: int = 8, queue_chunk: int = 0,
                  key_norms: bool = True):
         self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
         self.budgets = make_budgets(budget)
@@ -618,11 +620,11 @@ class PrefillPlan:
                 raise ValueError("the work queue needs n_bins >= 1 workgroups")
             if queue_group not in QUEUE_GROUPS:
                 raise ValueError(f"queue_group {queue_group!r}")
-            nq = queues if queue_group == "kv_tiers" else 1
+            nq = queues if queue_group in ("kv_tiers", "auto") else 1
             items, off, _ = sa_prefill_schedule(self.desc, self.budgets, SA_SCHED_QUEUE,
                                                 queue_group=QUEUE_GROUPS[queue_group], n_queues=nq,
                                                 queue_chunk=queue_chunk)
-            if nq > 1:
+            if off.size > 2:  # partitions
                 self.queue_offsets = off
             self.items_by_bin = torch.from_numpy(items).to(dev)
         elif n_bins > 0:

@@ -300,7 +300,13 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
  *     SA_QUEUE_HEAD      grouped by (sequence, query head), the head with the
  *                        largest total load first (lower index on ties),
  *                        longest first inside;
- *     SA_QUEUE_FLAT      longest first.
+ *     SA_QUEUE_FLAT      longest first;
+ *     SA_QUEUE_AUTO      SA_QUEUE_FLAT on one queue for up to 256 query blocks
+ *                        per head (a tile is then a large share of a
+ *                        workgroup's work and the start of the longest tiles
+ *                        decides the tail), else SA_QUEUE_KV_TIERS in n_queues
+ *                        partitions (the workgroups of an XCD share a KV
+ *                        head's blocks in its L2); *n_offsets tells which.
  *   items    [host] int32 [n_tiles] out (kinds other than GRID)
  *   offsets  [host] int32 out: bins: [n_bins + 1] bin offsets; queue:
  *            [n_queues + 1] partition offsets (n_queues 1 unless KV_TIERS)
@@ -308,7 +314,7 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
  *   bin_load [host] int64 [n_bins] out, bins only (may be NULL)
  * Sizes outside their ranges are SA_ERR_INVALID_ARG. */
 enum { SA_SCHED_GRID = 0, SA_SCHED_BINS = 1, SA_SCHED_BINS_XCD = 2, SA_SCHED_QUEUE = 3 };
-enum { SA_QUEUE_KV_TIERS = 0, SA_QUEUE_KV = 1, SA_QUEUE_HEAD = 2, SA_QUEUE_FLAT = 3 };
+enum { SA_QUEUE_KV_TIERS = 0, SA_QUEUE_KV = 1, SA_QUEUE_HEAD = 2, SA_QUEUE_FLAT = 3, SA_QUEUE_AUTO = 4 };
 typedef struct {
   int32_t kind;
   int32_t n_bins;       /* bins: number of bins (>= 1) */
@@ -316,7 +322,7 @@ typedef struct {
   int32_t xcd_groups;   /* SA_SCHED_BINS_XCD: cache partitions */
   int32_t xcd_chunk;    /* SA_SCHED_BINS_XCD: query blocks per chunk */
   int32_t queue_group;  /* SA_SCHED_QUEUE: SA_QUEUE_* */
-  int32_t n_queues;     /* SA_SCHED_QUEUE with SA_QUEUE_KV_TIERS: 1 .. 16 */
+  int32_t n_queues;     /* SA_SCHED_QUEUE with SA_QUEUE_KV_TIERS or SA_QUEUE_AUTO: 1 .. 16 */
   int32_t queue_chunk;  /* SA_SCHED_QUEUE with SA_QUEUE_KV_TIERS: run length limit */
 } sa_prefill_schedule_opts;
 

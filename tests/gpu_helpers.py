@@ -91,12 +91,13 @@ def count_rows_prefill(gpu_idx, gpu_cnt, ora_idx, ora_cnt, scores, budget, heads
 
 
 def prefill_gpu(inp: W.PrefillInputs, n_bins: int = 0, out_f32: bool = True, with_lse: bool = True,
-                queue: bool = False, queues: int = 8, kernel_variant: int = 0, key_norms: bool = True):
+                queue: bool = False, queues: int = 8, kernel_variant: int = 0, key_norms: bool = True,
+                queue_group: str = "auto"):
     """Select + attend on the GPU; returns (block_idx, block_cnt, o, lse, plan) on the device."""
     from head_heterogeneous_block_amd import sparse_attn as SA
     q, k, v = inp.q, inp.k, inp.v
     plan = SA.PrefillPlan(q, k, v, inp.budget, inp.spec.block, n_bins=n_bins, out_f32=out_f32, queue=queue,
-                          queues=queues, kernel_variant=kernel_variant, key_norms=key_norms)
+                          queues=queues, kernel_variant=kernel_variant, key_norms=key_norms, queue_group=queue_group)
     o = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if with_lse else None
     plan.select(q, k)

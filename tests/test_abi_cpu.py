@@ -540,6 +540,36 @@ def test_prefill_schedule_queue(seed):
         assert np.all(seg[:-1] >= seg[1:])
 
 
+def test_prefill_schedule_auto():
+    """SA_QUEUE_AUTO: up to 256 query blocks per head, plain longest first on
+    one queue; beyond, the tiered order in n_queues partitions."""
+    import torch
+    d, b, loads, bh, nb, Hq, Hkv = _sched_case(0)  # 37 query blocks
+    items, off, _ = SA.sa_prefill_schedule(d, b, SA.SA_SCHED_QUEUE, queue_group=SA.QUEUE_GROUPS["auto"], n_queues=8)
+    assert off.tolist() == [0, loads.size]
+    assert items.tolist() == SA.sa_lpt_queue_order(loads, None).tolist()
+    rng = np.random.default_rng(5)
+    for S, want_parts in ((256 * 64, False), (257 * 64, True), (300 * 64 + 5, True)):
+        q = torch.empty((1, 4, S, 64), dtype=torch.bfloat16, device="meta")
+        k = torch.empty((1, 2, S, 64), dtype=torch.bfloat16, device="meta")
+        dd = SA.make_prefill_desc(q, k, k, q, 64)
+        bud = {"min_blocks": [2] * 4, "ratio_q16": [int(x) for x in rng.integers(1000, 40000, 4)],
+               "n_sink": [1] * 4, "n_local": [1] * 4, "granularity": [64] * 4}
+        bb = SA.make_budgets(bud)
+        n_b = -(-S // 64)
+        ld = np.array([O.budget_blocks(m + 1, 2, bud["ratio_q16"][h]) for h in range(4) for m in range(n_b)],
+                      dtype=np.int64)
+        items, off, _ = SA.sa_prefill_schedule(dd, bb, SA.SA_SCHED_QUEUE, queue_group=SA.QUEUE_GROUPS["auto"],
+                                               n_queues=8)
+        if want_parts:
+            kv = (np.arange(ld.size) // n_b // 2).astype(np.int32)
+            w_items, w_off = SA.sa_lpt_queue_partition(ld, kv, 2, 8, 4, 0)
+            assert items.tolist() == w_items.tolist() and off.tolist() == w_off.tolist()
+        else:
+            assert off.tolist() == [0, ld.size]
+            assert items.tolist() == SA.sa_lpt_queue_order(ld, None).tolist()
+
+
 def test_prefill_schedule_validation():
     d, b, *_ = _sched_case(0)
     for kw in (dict(kind=9), dict(kind=SA.SA_SCHED_BINS, n_bins=0), dict(kind=SA.SA_SCHED_BINS_XCD, n_bins=6,

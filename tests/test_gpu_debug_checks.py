@@ -40,7 +40,7 @@ def test_prefill_tables_checked(checks_on):
     print(f"debug checks prefill {spec}", flush=True)
     inp = W.make_prefill(spec, W.seed_of(W.LLAMA_32K), device=DEV)
     plan = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=64, out_f32=True, queue=True,
-                          queues=8)
+                          queues=8, queue_group="kv_tiers")
     o = torch.empty(inp.q.shape, dtype=torch.float32, device=DEV)
     plan.select(inp.q, inp.k)
     SA.sa_set_debug_checks(False)

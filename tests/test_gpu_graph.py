@@ -46,7 +46,7 @@ def test_prefill_graph_replays():
     _say("graph prefill", spec)
     inp = W.make_prefill(spec, 11, device=DEV)
     plan = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=64, out_f32=True, queue=True,
-                          queues=8)
+                          queues=8, queue_group="kv_tiers")
     o = torch.empty(inp.q.shape, dtype=torch.float32, device=DEV)
     lse = torch.empty(inp.q.shape[:3], dtype=torch.float32, device=DEV)
     step = lambda: (plan.select(inp.q, inp.k), plan.attend(inp.q, inp.k, inp.v, o, lse))  # noqa: E731

@@ -86,9 +86,10 @@ def test_prefill_bf16_all_rows(name, over, sched):
     inp = W.make_prefill(spec, 77, device=DEV)
     _say("case:", name, "schedule", sched)
     n_bins = {"natural": 0, "bins37": 37, "queue23": 23, "queue23x1": 23}[sched]
-    # queue23: the queue cut into 8 partitions (the default); queue23x1: one queue
+    # queue23: the tiered queue cut into 8 partitions (the default beyond 256
+    # query blocks); queue23x1: one tiered queue
     idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=n_bins, queue=sched.startswith("queue"),
-                                         queues=1 if sched.endswith("x1") else 8)
+                                         queues=1 if sched.endswith("x1") else 8, queue_group="kv_tiers")
     q, k, v = to_host(inp)
     oidx, ocnt, scores = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, return_scores=True)
     gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
@@ -132,9 +133,13 @@ def test_prefill_schedules_bitwise_equal():
     for kw in (dict(xcd_groups=8, xcd_chunk=4), dict(bin_order="lpt"), dict(queue=True),
                dict(queue=True, n_bins=1), dict(queue=True, n_bins=5000), dict(queue=True, queue_group="kv"),
                dict(queue=True, queue_group="flat"), dict(queue=True, queue_group="head"),
-               dict(queue=True, queues=1), dict(queue=True, queues=1, n_bins=1), dict(queue=True, queue_chunk=3),
-               dict(queue=True, queues=3, n_bins=5), dict(queue=True, queues=16, n_bins=1),
-               dict(queue=True, queues=16, n_bins=5000), dict(queue=True, queues=2, n_bins=2)):
+               dict(queue=True, queue_group="kv_tiers"), dict(queue=True, queue_group="kv_tiers", queues=1),
+               dict(queue=True, queue_group="kv_tiers", queues=1, n_bins=1),
+               dict(queue=True, queue_group="kv_tiers", queue_chunk=3),
+               dict(queue=True, queue_group="kv_tiers", queues=3, n_bins=5),
+               dict(queue=True, queue_group="kv_tiers", queues=16, n_bins=1),
+               dict(queue=True, queue_group="kv_tiers", queues=16, n_bins=5000),
+               dict(queue=True, queue_group="kv_tiers", queues=2, n_bins=2)):
         _say("schedule", kw)
         kw = dict(kw)
         nb = kw.pop("n_bins", 64)

@@ -23,8 +23,9 @@ DEV = "cuda:0"
 def test_timed_prefill_stamps(sched, variant):
     spec = W.LLAMA_32K.with_(seq_len=4096 + 128, n_q_heads=8, n_kv_heads=2)
     inp = W.make_prefill(spec, 90, device=DEV)
-    kw = {"natural": dict(n_bins=0), "bins": dict(n_bins=37), "queue": dict(n_bins=23, queue=True, queues=1),
-          "queue_xcd": dict(n_bins=23, queue=True, queues=8)}[sched]
+    kw = {"natural": dict(n_bins=0), "bins": dict(n_bins=37),
+          "queue": dict(n_bins=23, queue=True, queues=1, queue_group="kv_tiers"),
+          "queue_xcd": dict(n_bins=23, queue=True, queues=8, queue_group="kv_tiers")}[sched]
     plan = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, out_f32=True, kernel_variant=variant, **kw)
     plan.select(inp.q, inp.k)
     o1 = torch.empty(inp.q.shape, dtype=torch.float32, device=DEV)
