@@ -296,6 +296,53 @@ sa_status check_lists(const int32_t* block_idx, const int32_t* block_cnt, int64_
 }
 
 // items: a permutation of [0, n); offsets (device, n_bins + 1): 0 .. n, non-decreasing
+// the key-norm table of a prefill launch bounds every key row: for each
+// (sequence, KV head, key block), the largest Euclidean norm of the block's
+// rows, recomputed from k on the host, is at most the table entry (relative
+// slack 1e-5 for the fp32 rounding of the two sums)
+sa_status check_key_norms(const sa_attn_desc* d, const void* k, const float* key_norms, hipStream_t st) {
+  const int64_t nb = cdiv(d->kv_len, d->block_size);
+  const int es = elem_size(d->dtype), D = d->head_dim;
+  std::vector<float> tab;
+  sa_status s = fetch(tab, key_norms, size_t(d->batch) * d->n_kv_heads * nb, st);
+  if (s) return s;
+  std::vector<char> rows(size_t(d->kv_len) * D * es);
+  for (int b = 0; b < d->batch; ++b)
+    for (int h = 0; h < d->n_kv_heads; ++h) {
+      const char* src = static_cast<const char*>(k) + (b * d->k_stride[0] + h * d->k_stride[1]) * int64_t(es);
+      const hipError_t e = hipMemcpy2D(rows.data(), size_t(D) * es, src, size_t(d->k_stride[2]) * es, size_t(D) * es,
+                                       size_t(d->kv_len), hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_fail(e, "debug check copy");
+      for (int64_t n = 0; n < nb; ++n) {
+        double m2 = 0.0;
+        const int64_t t1 = std::min<int64_t>(d->kv_len, (n + 1) * d->block_size);
+        for (int64_t t = n * d->block_size; t < t1; ++t) {
+          double q2 = 0.0;
+          for (int j = 0; j < D; ++j) {
+            float x;
+            if (es == 2) {
+              uint16_t u;
+              std::memcpy(&u, rows.data() + (size_t(t) * D + j) * 2, 2);
+              const uint32_t w = uint32_t(u) << 16;
+              std::memcpy(&x, &w, 4);
+            } else {
+              std::memcpy(&x, rows.data() + (size_t(t) * D + j) * 4, 4);
+            }
+            q2 += double(x) * x;
+          }
+          m2 = std::max(m2, q2);
+        }
+        const double want = std::sqrt(m2);
+        const float got = tab[(size_t(b) * d->n_kv_heads + h) * nb + n];
+        if (!(double(got) >= want * (1.0 - 1e-5)))
+          return fail(SA_ERR_INVALID_ARG,
+                      "prefill: key_norms[%d][%d][%lld] = %g below the largest key norm %g of the block", b, h,
+                      (long long)n, double(got), want);
+      }
+    }
+  return ok();
+}
+
 sa_status check_items(const int32_t* items, const int32_t* offsets, int32_t n_bins, int64_t n, hipStream_t st) {
   std::vector<int32_t> it, off;
   sa_status s = fetch(it, items, size_t(n), st);
@@ -992,6 +1039,7 @@ static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const voi
                          (hipStream_t)stream, "prefill")))
       return s;
     if (items_by_bin && (s = check_items(items_by_bin, bin_offsets, n_bins, n_tiles, (hipStream_t)stream))) return s;
+    if (key_norms && (s = check_key_norms(desc, k, key_norms, (hipStream_t)stream))) return s;
   }
   const int grid = items_by_bin ? n_bins : int(n_tiles);
   hipError_t e = sa::launch_prefill(p, desc->dtype, desc->head_dim, desc->block_size, desc->kernel_variant, grid,

@@ -361,7 +361,9 @@ size_t sa_prefill_workspace_size(const sa_attn_desc* desc, int32_t kmax, int32_t
  *   first step of a tile always takes it); without it, every step takes the
  *   row max.  The normalised result is the same softmax either way (the
  *   running max cancels; only the bf16 rounding of the probabilities moves).
- *   A table that is not an upper bound for k can overflow the accumulators. */
+ *   A table that is not an upper bound for k can overflow the accumulators;
+ *   with sa_set_debug_checks on, the host recomputes the bound from k and
+ *   rejects such a table (SA_ERR_INVALID_ARG) before the launch. */
 sa_status sa_sparse_attn_prefill(const sa_attn_desc* desc, const void* q, const void* k,
                                  const void* v, void* o, float* lse, const int32_t* block_idx,
                                  const int32_t* block_cnt, int32_t kmax, const float* key_norms,

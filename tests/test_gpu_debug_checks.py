@@ -1,6 +1,6 @@
 """The library's debug checks of the index tables (sa_set_debug_checks): with
 them on, a valid call gives the same output as with them off, and a corrupt
-block list, schedule or page table is rejected on the host with
+block list, schedule, key-norm table or page table is rejected on the host with
 SA_ERR_INVALID_ARG before anything is launched (the output buffer keeps its
 fill)."""
 
@@ -69,6 +69,18 @@ def test_prefill_tables_checked(checks_on):
     plan.items_by_bin[1] = plan.items_by_bin[0]
     _rejected(att, o, "twice")
     plan.items_by_bin.copy_(good_items)
+    # a key-norm entry below its block's longest key (the bound would be
+    # wrong); one just above it passes
+    good_norms = plan.key_norms.clone()
+    plan.key_norms[0, 1, 17] *= 0.99
+    _rejected(att, o, "key_norms[0][1][17]")
+    plan.key_norms.copy_(good_norms)
+    plan.key_norms[0, 0, 3] *= 1.01
+    o.zero_()
+    att()
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref)
+    plan.key_norms.copy_(good_norms)
     o.zero_()
     att()
     torch.cuda.synchronize()
