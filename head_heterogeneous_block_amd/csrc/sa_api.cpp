@@ -263,6 +263,17 @@ std::atomic<int> g_debug{[] {
   return (e && *e && std::strcmp(e, "0") != 0) ? 1 : 0;
 }()};
 
+// Whether the checks run for a call on stream st: they are on and st is not
+// being captured into a graph (a capture does not allow the synchronisation
+// and copies the checks need, and trying them would invalidate the caller's
+// capture; the calls made before a capture, such as its warm-up, are checked).
+bool debug_checks(hipStream_t st) {
+  if (!g_debug.load()) return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) return true;  // the checks report their own error
+  return cs == hipStreamCaptureStatusNone;
+}
+
 template <typename T>
 sa_status fetch(std::vector<T>& host, const T* dev, size_t n, hipStream_t st) {
   host.resize(n);
@@ -1033,7 +1044,7 @@ static sa_status prefill_impl(const sa_attn_desc* desc, const void* q, const voi
     return fail(SA_ERR_INVALID_ARG, "wg_times must be 8-byte aligned");
   p.wg_times = wg_times;
   p.key_norms = key_norms;
-  if (g_debug.load()) {
+  if (debug_checks((hipStream_t)stream)) {
     const int NB = int(nb);
     if ((s = check_lists(block_idx, block_cnt, n_tiles, kmax, [NB](int64_t t) { return int32_t(t % NB) + 1; },
                          (hipStream_t)stream, "prefill")))
@@ -1127,7 +1138,7 @@ static sa_status decode_impl(const sa_attn_desc* desc, const sa_head_budget* bud
   }
   if ((s = check_device())) return s;
   hipStream_t st = (hipStream_t)stream;
-  if (g_debug.load()) {
+  if (debug_checks(st)) {
     const int Hq = desc->n_q_heads, L = desc->kv_len;
     if ((s = check_lists(block_idx, block_cnt, int64_t(desc->batch) * Hq, kmax,
                          [&](int64_t r) { return int32_t(cdiv(L, budgets[r % Hq].granularity)); }, st, "decode")))

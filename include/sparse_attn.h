@@ -119,9 +119,12 @@ const char* sa_last_error(void);
  * the pages in use (in [0, pages_per_head)).  A failed check returns
  * SA_ERR_INVALID_ARG with the first bad entry in sa_last_error, and nothing is
  * launched.  The checks copy the tables to the host after synchronising the
- * stream, so they are for debugging, not for the timed path.  Off by default;
- * on when SA_DEBUG_CHECKS is set (and not "0") in the environment when the
- * library loads.  Returns the previous setting; process-wide. */
+ * stream, so they are for debugging, not for the timed path.  A call on a
+ * stream that is being captured into a graph skips them (a capture allows
+ * neither the synchronisation nor the copies); the calls before the capture,
+ * such as its warm-up, are checked.  Off by default; on when SA_DEBUG_CHECKS
+ * is set (and not "0") in the environment when the library loads.  Returns the
+ * previous setting; process-wide. */
 int32_t sa_set_debug_checks(int32_t on);
 
 /* ---------------------------------------------------------------- host-only */

@@ -71,6 +71,33 @@ def test_prefill_graph_replays():
         assert torch.equal(o2, ref[2])
 
 
+def test_graph_capture_with_debug_checks():
+    """With the host-side checks on, the warm-up calls are checked and the
+    captured calls skip them (a capture allows no synchronisation): the capture
+    succeeds and every replay equals the eager result."""
+    spec = W.LLAMA_32K.with_(seq_len=2048 + 5, n_q_heads=4, n_kv_heads=1)
+    _say("graph prefill with debug checks", spec)
+    inp = W.make_prefill(spec, 5, device=DEV)
+    plan = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=32, out_f32=True, queue=True,
+                          queues=2, queue_group="kv_tiers")
+    o = torch.empty(inp.q.shape, dtype=torch.float32, device=DEV)
+    step = lambda: (plan.select(inp.q, inp.k), plan.attend(inp.q, inp.k, inp.v, o))  # noqa: E731
+    was = SA.sa_set_debug_checks(True)
+    try:
+        step()
+        torch.cuda.synchronize()
+        ref = (plan.block_idx.clone(), plan.block_cnt.clone(), o.clone())
+        g = _capture(step)
+        for r in range(REPLAYS):
+            o.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert all(torch.equal(a, b) for a, b in zip((plan.block_idx, plan.block_cnt, o), ref)), f"replay {r}"
+    finally:
+        SA.sa_set_debug_checks(was)
+
+
 @pytest.mark.parametrize("noalloc", [False, True], ids=["workspace", "noalloc"])
 def test_decode_graph_replays(noalloc):
     spec = W.DECODE_128K.with_(batch=3, kv_len=8192 + 40)

@@ -97,7 +97,9 @@ def test_paged_decode_bitwise_and_oracle(page_size, L):
 
 def test_paged_decode_bf16_output_and_table_out_of_range():
     """bf16 output equals the contiguous path's bit for bit; a page-table entry
-    outside the pool reads as zero keys and values instead of faulting."""
+    outside the pool reads as zero keys and values instead of faulting (the
+    unchecked path: the host-side debug checks, which reject such a table, are
+    switched off for it)."""
     spec = W.DECODE_128K.with_(batch=2, kv_len=4096, tok_lo=256, tok_hi=1024, stream_local=8)
     inp = W.make_decode(spec, 43, device=DEV)
     cont, oc, lc, paged, op, lp, pk = _run_both(inp, 128, out_f32=False)
@@ -106,10 +108,14 @@ def test_paged_decode_bf16_output_and_table_out_of_range():
     bad[1, 0, 5] = pk.k_pages.shape[1] + 7  # sequence 1, KV head 0, tokens 640..767
     plan = SA.PagedDecodePlan(inp.q, pk.k_pages, pk.v_pages, bad, spec.kv_len, inp.budget, out_f32=True)
     o = torch.empty(inp.q.shape, dtype=torch.float32, device=DEV)
-    plan.pool(pk.k_pages)
-    plan.select(inp.q, pk.k_pages)
-    plan.attend(inp.q, pk.k_pages, pk.v_pages, o)
-    torch.cuda.synchronize()
+    was = SA.sa_set_debug_checks(False)
+    try:
+        plan.pool(pk.k_pages)
+        plan.select(inp.q, pk.k_pages)
+        plan.attend(inp.q, pk.k_pages, pk.v_pages, o)
+        torch.cuda.synchronize()
+    finally:
+        SA.sa_set_debug_checks(was)
     assert torch.isfinite(o).all()
     kz, vz = inp.k.clone(), inp.v.clone()
     kz[1, 0, 640:768] = 0
