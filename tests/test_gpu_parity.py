@@ -67,6 +67,29 @@ def test_prefill_config0_fp32_all_rows(schedule):
         np.testing.assert_array_equal(plan.items_by_bin.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("schedule", ["natural", "queue"])
+def test_prefill_fp32_batched_ragged(schedule):
+    """The fp32 path over two sequences of a ragged length (not a multiple of
+    the 64-token block): batch strides, the partial last block, and the
+    schedule's (sequence, KV head) groups."""
+    spec = W.TINY_F32.with_(batch=2, seq_len=1000)
+    inp = W.make_prefill(spec, 91, device=DEV)
+    _say("case: fp32 batched ragged", schedule)
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins={"natural": 0, "queue": 5}[schedule],
+                                         queue=schedule == "queue", queue_group="kv_tiers")
+    q, k, v = to_host(inp)
+    oidx, ocnt, scores = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, return_scores=True)
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    pinned, exempt = check_prefill_selection(gidx, gcnt, oidx, ocnt, scores, inp.budget)
+    _say("pinned", pinned, "exempt", exempt)
+    assert pinned >= 0.9 * (pinned + exempt)
+    ro, rl = O.attention_prefill_gather(q, k, v, gidx, gcnt, spec.block)
+    err = max_abs(o.cpu().numpy(), ro)
+    lerr = max_abs(lse.cpu().numpy(), rl)
+    _say("max abs err o", err, "lse", lerr)
+    assert err <= TOL_F32 and lerr <= TOL_F32
+
+
 PREFILL_SHAPES = [
     # name, overrides
     ("llama-2k", dict(seq_len=2048, n_q_heads=8, n_kv_heads=2)),
@@ -76,6 +99,10 @@ PREFILL_SHAPES = [
     ("one-block", dict(seq_len=100, n_q_heads=2, n_kv_heads=1)),
     ("tiny-17", dict(seq_len=17, n_q_heads=2, n_kv_heads=1)),
     ("one-token", dict(seq_len=1, n_q_heads=4, n_kv_heads=2)),
+    # several sequences: the batch strides of Q, K, V and O, the key-norm
+    # table's rows and the schedule's (sequence, KV head) groups
+    ("batch3-ragged", dict(batch=3, seq_len=1000, n_q_heads=4, n_kv_heads=1)),
+    ("batch2-b64", dict(batch=2, seq_len=700, n_q_heads=4, n_kv_heads=2, block=64)),
 ]
 
 
