@@ -159,6 +159,50 @@ def _stream(t: torch.Tensor):
     return None
 
 
+def _match(name: str, t: Optional[torch.Tensor], shape, strides=None, dtype=None, contiguous: bool = False) -> None:
+    """Raise ValueError unless t has this shape (and dtype, contiguity, and
+    these strides on every axis longer than one).  The kernels address their
+    tensors from the descriptor's sizes and strides alone, so a tensor laid out
+    otherwise would be read or written outside its storage."""
+    if t is None:
+        raise ValueError(f"{name} is None")
+    # fast path: everything as expected (plain tuples compare in one step)
+    if (t.shape == shape and (dtype is None or t.dtype == dtype) and (strides is None or t.stride() == strides)
+            and (not contiguous or t.is_contiguous())):
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(x) for x in shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if strides is not None:
+        for n, got, want in zip(t.shape, t.stride(), strides):
+            if n > 1 and got != int(want):
+                raise ValueError(f"{name}: strides {tuple(t.stride())} differ from the descriptor's "
+                                 f"{tuple(int(x) for x in strides)}")
+
+
+def _check_outputs_prefill(desc: "sa_attn_desc", q, o, lse, out_f32: bool) -> None:
+    """o and lse of a prefill call against the descriptor (what the kernels write)."""
+    B, Hq, S, D = desc.batch, desc.n_q_heads, desc.q_len, desc.head_dim
+    if _dtype_code(q) != desc.dtype:
+        raise ValueError(f"q: dtype {q.dtype} does not match the descriptor")
+    _match("o", o, (B, Hq, S, D), (*desc.o_stride, 1), torch.float32 if out_f32 else q.dtype)
+    if lse is not None:
+        _match("lse", lse, (B, Hq, S), dtype=torch.float32, contiguous=True)
+
+
+def _check_outputs_decode(desc: "sa_attn_desc", q, o, lse, out_f32: bool) -> None:
+    """o and lse of a decode call against the descriptor (what the kernels write)."""
+    B, Hq, D = desc.batch, desc.n_q_heads, desc.head_dim
+    if _dtype_code(q) != desc.dtype:
+        raise ValueError(f"q: dtype {q.dtype} does not match the descriptor")
+    _match("o", o, (B, Hq, D), (desc.o_stride[0], desc.o_stride[1], 1), torch.float32 if out_f32 else q.dtype)
+    if lse is not None:
+        _match("lse", lse, (B, Hq), dtype=torch.float32, contiguous=True)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return SA_BF16
@@ -409,7 +453,18 @@ def sa_pool_keys_decode(desc: sa_attn_desc, budgets, k: torch.Tensor, k_pooled: 
 
 def sa_select_blocks(desc: sa_attn_desc, budgets, q: torch.Tensor, k: torch.Tensor,
                      k_pooled: Optional[torch.Tensor], block_idx: torch.Tensor, block_cnt: torch.Tensor,
-                     kmax: int, workspace: torch.Tensor, key_norms: Optional[torch.Tensor] = None) -> None:
+                     kmax: int, workspace: torch.Tensor, key_norms: Optional[torch.Tensor] = None,
+                     check: bool = True) -> None:
+    if check:  # (the plans validate their own tables once and pass check=False)
+        B, Hq = desc.batch, desc.n_q_heads
+        if desc.block_size == 0:  # decode
+            rows = (B, Hq)
+        else:
+            rows = (B, Hq, -(-desc.q_len // desc.block_size))
+            if key_norms is not None:
+                _match("key_norms", key_norms, (B, desc.n_kv_heads, rows[2]), dtype=torch.float32, contiguous=True)
+        _match("block_idx", block_idx, (*rows, kmax), dtype=torch.int32, contiguous=True)
+        _match("block_cnt", block_cnt, rows, dtype=torch.int32, contiguous=True)
     _check(_lib.sa_select_blocks(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(k_pooled), _ptr(block_idx),
                                  _ptr(block_cnt), kmax, _ptr(key_norms), _ptr(workspace), workspace.numel(),
                                  _stream(q)))
@@ -417,7 +472,10 @@ def sa_select_blocks(desc: sa_attn_desc, budgets, q: torch.Tensor, k: torch.Tens
 
 def sa_sparse_attn_prefill(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
                            bin_offsets=None, items_by_bin=None, n_bins: int = 0, out_f32: bool = False,
-                           workspace: Optional[torch.Tensor] = None, key_norms: Optional[torch.Tensor] = None) -> None:
+                           workspace: Optional[torch.Tensor] = None, key_norms: Optional[torch.Tensor] = None,
+                           check: bool = True) -> None:
+    if check:
+        _check_outputs_prefill(desc, q, o, lse, out_f32)
     ws = workspace
     _check(_lib.sa_sparse_attn_prefill(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                        _ptr(block_idx), _ptr(block_cnt), kmax, _ptr(key_norms), _ptr(bin_offsets),
@@ -428,7 +486,9 @@ def sa_sparse_attn_prefill(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block
 def sa_sparse_attn_prefill_queues(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
                                   queue_offsets: np.ndarray, order, n_workgroups: int, out_f32: bool = False,
                                   workspace: Optional[torch.Tensor] = None,
-                                  key_norms: Optional[torch.Tensor] = None) -> None:
+                                  key_norms: Optional[torch.Tensor] = None, check: bool = True) -> None:
+    if check:
+        _check_outputs_prefill(desc, q, o, lse, out_f32)
     off = np.ascontiguousarray(queue_offsets, dtype=np.int32)
     ws = workspace
     _check(_lib.sa_sparse_attn_prefill_queues(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -441,9 +501,11 @@ def sa_sparse_attn_prefill_queues(desc: sa_attn_desc, q, k, v, o, lse, block_idx
 def sa_sparse_attn_prefill_timed(desc: sa_attn_desc, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
                                  bin_offsets, items_by_bin, n_bins: int, queue_offsets: Optional[np.ndarray],
                                  out_f32: bool, wg_times: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-                                 key_norms: Optional[torch.Tensor] = None) -> None:
+                                 key_norms: Optional[torch.Tensor] = None, check: bool = True) -> None:
     """A prefill launch recording each workgroup's start and end on the constant
     clock into wg_times (int64 [2 * grid])."""
+    if check:
+        _check_outputs_prefill(desc, q, o, lse, out_f32)
     off = None if queue_offsets is None else np.ascontiguousarray(queue_offsets, dtype=np.int32)
     ws = workspace
     _check(_lib.sa_sparse_attn_prefill_timed(
@@ -454,7 +516,9 @@ def sa_sparse_attn_prefill_timed(desc: sa_attn_desc, q, k, v, o, lse, block_idx,
 
 
 def sa_sparse_attn_decode(desc: sa_attn_desc, budgets, q, k, v, o, lse, block_idx, block_cnt, kmax: int,
-                          workspace: torch.Tensor, out_f32: bool = False) -> None:
+                          workspace: torch.Tensor, out_f32: bool = False, check: bool = True) -> None:
+    if check:
+        _check_outputs_decode(desc, q, o, lse, out_f32)
     _check(_lib.sa_sparse_attn_decode(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                       _ptr(block_idx), _ptr(block_cnt), kmax, 1 if out_f32 else 0, _ptr(workspace),
                                       workspace.numel(), _stream(q)))
@@ -464,6 +528,7 @@ def sa_sparse_attn_decode_noalloc(desc: sa_attn_desc, budgets, q, k, v, o, lse, 
                                   out_f32: bool = False) -> None:
     """sa_sparse_attn_decode with the library's fixed per-GPU scratch array
     instead of a workspace (no allocation; calls on one GPU must not overlap)."""
+    _check_outputs_decode(desc, q, o, lse, out_f32)
     _check(_lib.sa_sparse_attn_decode_noalloc(ctypes.byref(desc), budgets, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                               _ptr(lse), _ptr(block_idx), _ptr(block_cnt), kmax,
                                               1 if out_f32 else 0, _stream(q)))
@@ -477,7 +542,9 @@ def sa_pool_keys_decode_paged(desc: sa_attn_desc, budgets, k_pages: torch.Tensor
 
 def sa_sparse_attn_decode_paged(desc: sa_attn_desc, budgets, q, k_pages, v_pages, pages: sa_kv_pages, o, lse,
                                 block_idx, block_cnt, kmax: int, workspace: torch.Tensor,
-                                out_f32: bool = False) -> None:
+                                out_f32: bool = False, check: bool = True) -> None:
+    if check:
+        _check_outputs_decode(desc, q, o, lse, out_f32)
     _check(_lib.sa_sparse_attn_decode_paged(ctypes.byref(desc), budgets, _ptr(q), _ptr(k_pages), _ptr(v_pages),
                                             ctypes.byref(pages), _ptr(o), _ptr(lse), _ptr(block_idx),
                                             _ptr(block_cnt), kmax, 1 if out_f32 else 0, _ptr(workspace),
@@ -611,6 +678,11 @@ class PrefillPlan:
         self.attn_ws = _workspace(sa_prefill_workspace_size(self.desc, self.kmax, n_bins), dev)
         self.key_norms = (torch.empty((q.shape[0], k.shape[1], self.nb), dtype=torch.float32, device=dev)
                           if key_norms else None)
+        # the layouts the descriptor was built for (every later q, k, v must
+        # have them); o may differ from q, and the descriptor follows it
+        self._lay = {n: (tuple(t.shape), tuple(t.stride()), q.dtype) for n, t in (("q", q), ("k", k), ("v", v))}
+        self._o_dtype = torch.float32 if out_f32 else q.dtype
+        self._o_stride = tuple(q.stride())
         self.queue = queue
         self.queue_offsets = None
         self.bin_load = None
@@ -639,18 +711,38 @@ class PrefillPlan:
             self.items_by_bin = torch.from_numpy(items).to(dev)
 
     def select(self, q, k) -> None:
+        _match("q", q, *self._lay["q"])
+        _match("k", k, *self._lay["k"])
         sa_select_blocks(self.desc, self.budgets, q, k, None, self.block_idx, self.block_cnt, self.kmax,
-                         self.select_ws, self.key_norms)
+                         self.select_ws, self.key_norms, check=False)
+
+    def _set_out(self, q, k, v, o, lse) -> None:
+        """Check q, k and v against the plan's layouts and o and lse against its
+        shapes, and take o's strides (o may be laid out differently from q)."""
+        for n, t in (("q", q), ("k", k), ("v", v)):
+            _match(n, t, *self._lay[n])
+        if o is None or o.dim() != 4:
+            raise ValueError("o must be a [b, Hq, S, D] tensor")
+        _match("o", o, self._lay["q"][0], dtype=self._o_dtype)
+        if lse is not None:
+            _match("lse", lse, self._lay["q"][0][:3], dtype=torch.float32, contiguous=True)
+        st = o.stride()
+        if st != self._o_stride:
+            if st[3] != 1:
+                raise ValueError("o: last axis must be contiguous")
+            self.desc.o_stride[:] = [st[0], st[1], st[2]]
+            self._o_stride = st
 
     def attend(self, q, k, v, o, lse=None) -> None:
+        self._set_out(q, k, v, o, lse)
         if self.queue and self.queue_offsets is not None:
             sa_sparse_attn_prefill_queues(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
                                           self.queue_offsets, self.items_by_bin, self.n_bins, self.out_f32,
-                                          self.attn_ws, self.key_norms)
+                                          self.attn_ws, self.key_norms, check=False)
             return
         sa_sparse_attn_prefill(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
                                self.bin_offsets, self.items_by_bin, self.n_bins, self.out_f32, self.attn_ws,
-                               self.key_norms)
+                               self.key_norms, check=False)
 
     def share_tables(self, other: "PrefillPlan") -> None:
         """Use the selection outputs of another plan of the same shape and
@@ -670,13 +762,14 @@ class PrefillPlan:
         """attend(), also recording each workgroup's start and end on the GPU's
         constant clock into ``stamps`` (int64 [grid, 2], allocated if None);
         returns it."""
+        self._set_out(q, k, v, o, lse)
         t = stamps if stamps is not None else torch.zeros((self.grid(), 2), dtype=torch.int64, device=q.device)
         if t.dtype != torch.int64 or t.numel() < 2 * self.grid():
             raise ValueError("stamps must be int64 with 2 * grid entries")
         sa_sparse_attn_prefill_timed(self.desc, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
                                      self.bin_offsets, self.items_by_bin, self.n_bins if self.items_by_bin is not None
                                      else 0, self.queue_offsets if self.queue else None, self.out_f32, t,
-                                     self.attn_ws, self.key_norms)
+                                     self.attn_ws, self.key_norms, check=False)
         return t
 
 
@@ -696,17 +789,44 @@ class DecodePlan:
                                     dtype=torch.float32, device=dev)
         self.select_ws = _workspace(sa_select_workspace_size(self.desc, self.budgets, self.kmax), dev)
         self.attn_ws = _workspace(sa_decode_workspace_size(self.desc, self.budgets, self.kmax), dev)
+        # the layouts the descriptor was built for (k and v: the cache, or the
+        # page pools of a paged plan); o may differ from q
+        self._lay = {n: (tuple(t.shape), tuple(t.stride()), q.dtype) for n, t in (("q", q), ("k", k), ("v", v))}
+        self._o_dtype = torch.float32 if out_f32 else q.dtype
+        self._o_stride = (int(self.desc.o_stride[0]), int(self.desc.o_stride[1]), 1)
 
     def pool(self, k) -> None:
+        _match("k", k, *self._lay["k"])
+        self._pool(k)
+
+    def _pool(self, k) -> None:
         sa_pool_keys_decode(self.desc, self.budgets, k, self.k_pooled)
 
     def select(self, q, k) -> None:
+        # (the selection reads the pooled-key cache, not k)
+        _match("q", q, *self._lay["q"])
         sa_select_blocks(self.desc, self.budgets, q, k, self.k_pooled, self.block_idx, self.block_cnt, self.kmax,
-                         self.select_ws)
+                         self.select_ws, check=False)
+
+    def _set_out(self, q, k, v, o, lse) -> None:
+        for n, t in (("q", q), ("k", k), ("v", v)):
+            _match(n, t, *self._lay[n])
+        if o is None or o.dim() != 3:
+            raise ValueError("o must be a [b, Hq, D] tensor")
+        _match("o", o, self._lay["q"][0], dtype=self._o_dtype)
+        if lse is not None:
+            _match("lse", lse, self._lay["q"][0][:2], dtype=torch.float32, contiguous=True)
+        st = o.stride()
+        if st != self._o_stride:
+            if st[2] != 1:
+                raise ValueError("o: last axis must be contiguous")
+            self.desc.o_stride[:] = [st[0], st[1], 0]
+            self._o_stride = st
 
     def attend(self, q, k, v, o, lse=None) -> None:
+        self._set_out(q, k, v, o, lse)
         sa_sparse_attn_decode(self.desc, self.budgets, q, k, v, o, lse, self.block_idx, self.block_cnt, self.kmax,
-                              self.attn_ws, self.out_f32)
+                              self.attn_ws, self.out_f32, check=False)
 
 
 class PagedDecodePlan(DecodePlan):
@@ -720,9 +840,11 @@ class PagedDecodePlan(DecodePlan):
         self.pages = make_pages(table, k_pages.shape[2], k_pages.shape[1])
         self.table = table  # keeps the table alive while the plan holds its address
 
-    def pool(self, k_pages) -> None:
+    def _pool(self, k_pages) -> None:
         sa_pool_keys_decode_paged(self.desc, self.budgets, k_pages, self.pages, self.k_pooled)
 
     def attend(self, q, k_pages, v_pages, o, lse=None) -> None:
+        self._set_out(q, k_pages, v_pages, o, lse)
         sa_sparse_attn_decode_paged(self.desc, self.budgets, q, k_pages, v_pages, self.pages, o, lse,
-                                    self.block_idx, self.block_cnt, self.kmax, self.attn_ws, self.out_f32)
+                                    self.block_idx, self.block_cnt, self.kmax, self.attn_ws, self.out_f32,
+                                    check=False)
