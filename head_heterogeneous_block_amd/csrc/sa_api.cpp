@@ -928,7 +928,11 @@ sa_status sa_select_blocks(const sa_attn_desc* desc, const sa_head_budget* budge
   dp.nc_max = w.nc_max;
   dp.Hq = desc->n_q_heads;
   dp.Hkv = desc->n_kv_heads;
-  dp.rows_per_wg = 64;  // short streams: many waves balance better than long ones
+  // short streams: many waves balance better than long ones; 32 rows are the
+  // four 8-row stages of a wave's ring, three of them issued at once (a sweep
+  // of the 128K decode step: 32 rows 212.5-214.4 us, 48 214.9-216.1, 64
+  // 215.3-219.5, 40 215.7-217.3, 24 219.6-220.2, 128 218.8-220.4, 16 226.9-229.0)
+  dp.rows_per_wg = 32;
   dp.scale = scale;
   // jobs: (KV head, granularity) -> the scoring heads, at most 8 per job
   std::vector<sa::DecodeScoreJob> jobs;
