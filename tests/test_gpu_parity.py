@@ -226,6 +226,35 @@ def test_prefill_full_size_sampled(spec):
     assert torch.isfinite(o).all()
 
 
+def test_prefill_long_rows_sampled():
+    """Rows longer than 1024 blocks (131072 + 37 tokens in 64-token blocks: 2049
+    candidates in the last row, ragged): the selection keeps fewer rows per
+    workgroup there, and the attention reads block ids and key-norm rows beyond
+    1024.  Every row's selection against the oracle; attention on tiles on
+    both sides of 1024 and at the ragged end, on the benchmark's launch (the
+    work queue in XCD partitions)."""
+    spec = W.LLAMA_32K.with_(seq_len=2048 * 64 + 37, block=64, n_q_heads=2, n_kv_heads=1)
+    _say("case: long rows", spec)
+    inp = W.make_prefill(spec, 61, device=DEV)
+    idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins=512, queue=True)
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    q, k, v = to_host(inp)
+    oidx, ocnt, sc = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, return_scores=True)
+    pinned, exempt = check_prefill_selection(gidx, gcnt, oidx, ocnt, sc, inp.budget)
+    _say("pinned", pinned, "exempt", exempt)
+    assert pinned >= 0.9 * (pinned + exempt)
+    tiles = [(0, h, m) for h in range(2) for m in (0, 1, 1023, 1024, 1025, 2047, 2048)]
+    ro, rl = O.attention_prefill_gather(q, k, v, gidx, gcnt, spec.block, tiles=tiles)
+    og, lg = o.cpu().numpy(), lse.cpu().numpy()
+    worst = 0.0
+    for (bi, h, m) in tiles:
+        rows = slice(m * spec.block, min(spec.seq_len, (m + 1) * spec.block))
+        worst = max(worst, max_abs(og[bi, h, rows], ro[bi, h, rows]), max_abs(lg[bi, h, rows], rl[bi, h, rows]))
+    _say("max abs err over", len(tiles), "tiles:", worst)
+    assert worst <= TOL_BF16
+    assert torch.isfinite(o).all()
+
+
 # ---------------------------------------------------------------- decode
 
 
