@@ -307,6 +307,19 @@ def test_decode_reduced_all(L):
     _check_decode(inp, plan, o, lse, list(range(spec.batch)))
 
 
+def test_decode_long_cache():
+    """A cache longer than the 131072-token workload (200003 tokens): the heads
+    at granularity 16 score 12501 pooled keys instead of at most 8192, so the
+    top-k runs its widest shape (1024 threads, 16 keys each); every row against
+    the oracle, outputs within the bound."""
+    spec = W.DECODE_128K.with_(batch=1, kv_len=200003)
+    _say("case: decode long cache", spec.kv_len)
+    inp = W.make_decode(spec, 47, device=DEV)
+    assert 16 in {int(g) for g in inp.budget["granularity"]}
+    plan, o, lse = _decode_gpu(inp)
+    _check_decode(inp, plan, o, lse, [0])
+
+
 @pytest.mark.parametrize("name,over", [
     ("d64", dict(head_dim=64)),
     ("gqa8", dict(n_q_heads=16, n_kv_heads=2, n_streaming=4)),
