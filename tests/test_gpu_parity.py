@@ -67,14 +67,15 @@ def test_prefill_config0_fp32_all_rows(schedule):
         np.testing.assert_array_equal(plan.items_by_bin.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("schedule", ["natural", "queue"])
-def test_prefill_fp32_batched_ragged(schedule):
-    """The fp32 path over two sequences of a ragged length (not a multiple of
-    the 64-token block): batch strides, the partial last block, and the
-    schedule's (sequence, KV head) groups."""
-    spec = W.TINY_F32.with_(batch=2, seq_len=1000)
+def test_prefill_fp32_batched_ragged(schedule, D):
+    """The fp32 path (both head sizes) over two sequences of a ragged length
+    (not a multiple of the 64-token block): batch strides, the partial last
+    block, and the schedule's (sequence, KV head) groups."""
+    spec = W.TINY_F32.with_(batch=2, seq_len=1000, head_dim=D)
     inp = W.make_prefill(spec, 91, device=DEV)
-    _say("case: fp32 batched ragged", schedule)
+    _say("case: fp32 batched ragged", schedule, "D", D)
     idx, cnt, o, lse, plan = prefill_gpu(inp, n_bins={"natural": 0, "queue": 5}[schedule],
                                          queue=schedule == "queue", queue_group="kv_tiers")
     q, k, v = to_host(inp)
@@ -96,6 +97,7 @@ PREFILL_SHAPES = [
     ("llama-ragged", dict(seq_len=2000, n_q_heads=8, n_kv_heads=2)),
     ("d64-b128", dict(seq_len=1536, n_q_heads=4, n_kv_heads=1, head_dim=64)),
     ("b64", dict(seq_len=1500, n_q_heads=4, n_kv_heads=2, block=64)),
+    ("d64-b64", dict(seq_len=1300, n_q_heads=4, n_kv_heads=1, head_dim=64, block=64)),
     ("one-block", dict(seq_len=100, n_q_heads=2, n_kv_heads=1)),
     ("tiny-17", dict(seq_len=17, n_q_heads=2, n_kv_heads=1)),
     ("one-token", dict(seq_len=1, n_q_heads=4, n_kv_heads=2)),
