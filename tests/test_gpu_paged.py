@@ -95,6 +95,21 @@ def test_paged_decode_bitwise_and_oracle(page_size, L):
     assert err <= TOL_BF16 and lerr <= TOL_BF16
 
 
+@pytest.mark.parametrize("over", [dict(head_dim=64), dict(n_q_heads=16, n_kv_heads=2, n_streaming=4)],
+                         ids=["d64", "gqa8"])
+def test_paged_decode_other_shapes(over):
+    """64-dim heads and eight query heads per KV head through pages: bitwise the
+    contiguous path's pooled keys, selections and outputs (that path is checked
+    against the oracle on the same shapes)."""
+    spec = W.DECODE_128K.with_(batch=2, kv_len=4096 + 24, tok_lo=256, tok_hi=1024, stream_local=8, **over)
+    _say("case: paged decode", over)
+    inp = W.make_decode(spec, 53, device=DEV)
+    cont, oc, lc, paged, op, lp, pk = _run_both(inp, 128)
+    assert torch.equal(_pooled(paged), _pooled(cont))
+    assert torch.equal(paged.block_idx, cont.block_idx) and torch.equal(paged.block_cnt, cont.block_cnt)
+    assert torch.equal(op, oc) and torch.equal(lp, lc)
+
+
 def test_paged_decode_bf16_output_and_table_out_of_range():
     """bf16 output equals the contiguous path's bit for bit; a page-table entry
     outside the pool reads as zero keys and values instead of faulting (the
