@@ -98,6 +98,7 @@ PREFILL_SHAPES = [
     ("d64-b128", dict(seq_len=1536, n_q_heads=4, n_kv_heads=1, head_dim=64)),
     ("b64", dict(seq_len=1500, n_q_heads=4, n_kv_heads=2, block=64)),
     ("d64-b64", dict(seq_len=1300, n_q_heads=4, n_kv_heads=1, head_dim=64, block=64)),
+    ("mha-3heads", dict(seq_len=1100, n_q_heads=3, n_kv_heads=3)),  # one query head per KV head
     ("one-block", dict(seq_len=100, n_q_heads=2, n_kv_heads=1)),
     ("tiny-17", dict(seq_len=17, n_q_heads=2, n_kv_heads=1)),
     ("one-token", dict(seq_len=1, n_q_heads=4, n_kv_heads=2)),
@@ -325,8 +326,9 @@ def test_decode_long_cache():
 @pytest.mark.parametrize("name,over", [
     ("d64", dict(head_dim=64)),
     ("gqa8", dict(n_q_heads=16, n_kv_heads=2, n_streaming=4)),
+    ("mha", dict(n_q_heads=6, n_kv_heads=6, n_streaming=2)),
     ("tiny-L", dict(kv_len=40, tok_lo=16, tok_hi=64, stream_local=4)),
-], ids=["d64", "gqa8", "tiny-L"])
+], ids=["d64", "gqa8", "mha", "tiny-L"])
 def test_decode_bf16_shapes(name, over):
     """The bf16 MFMA decode path at other head sizes and group sizes, and a
     cache shorter than one 64-token block (every head keeps all its blocks)."""
