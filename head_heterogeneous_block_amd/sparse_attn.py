@@ -658,13 +658,14 @@ class PrefillPlan:
     partition in the tiered order; other ``queue_group`` orders use one queue.
     ``key_norms``: the selection also writes each key block's largest key-row
     norm, and the attention uses it to skip the per-step row max where the
-    scores cannot overflow (False: every step takes the row max)."""
+    scores cannot overflow (False: every step takes the row max).  ``scale``:
+    the softmax scale (0: 1/sqrt(D))."""
 
     def __init__(self, q, k, v, budget: dict, block: int, n_bins: int = 0, out_f32: bool = False,
                  kernel_variant: int = 0, bin_order: str = "index", xcd_groups: int = 0, xcd_chunk: int = 64,
                  queue: bool = False, queue_group: str = "auto", queues: int = 8, queue_chunk: int = 0,
-                 key_norms: bool = True):
-        self.desc = make_prefill_desc(q, k, v, q, block, kernel_variant=kernel_variant)
+                 key_norms: bool = True, scale: float = 0.0):
+        self.desc = make_prefill_desc(q, k, v, q, block, scale=scale, kernel_variant=kernel_variant)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_prefill_block_counts(self.desc, self.budgets)
         self.block = block
@@ -777,8 +778,10 @@ class DecodePlan:
     """Descriptor, budgets, kmax, index buffers and workspaces for one decode
     shape; ``pool`` builds the pooled-key cache once per KV cache."""
 
-    def __init__(self, q, k, v, budget: dict, out_f32: bool = False, desc: Optional[sa_attn_desc] = None):
-        self.desc = desc if desc is not None else make_decode_desc(q, k, v, q)
+    def __init__(self, q, k, v, budget: dict, out_f32: bool = False, desc: Optional[sa_attn_desc] = None,
+                 scale: float = 0.0):
+        # scale: the softmax scale (0: 1/sqrt(D)); ignored when desc is given
+        self.desc = desc if desc is not None else make_decode_desc(q, k, v, q, scale=scale)
         self.budgets = make_budgets(budget)
         self.counts, self.kmax = sa_decode_block_counts(self.desc, self.budgets)
         self.out_f32 = out_f32

@@ -310,6 +310,51 @@ def test_decode_reduced_all(L):
     _check_decode(inp, plan, o, lse, list(range(spec.batch)))
 
 
+def test_custom_softmax_scale():
+    """A softmax scale other than 1/sqrt(D) (0.05; 1/sqrt(128) = 0.088), prefill
+    and decode: selections and outputs against the oracle run with the same
+    scale.  (The top-k order does not depend on a positive scale; the
+    attention's exponent does.)"""
+    scale = 0.05
+    spec = W.LLAMA_32K.with_(seq_len=1500, n_q_heads=4, n_kv_heads=2)
+    _say("case: scale", scale, "prefill")
+    inp = W.make_prefill(spec, 83, device=DEV)
+    plan = SA.PrefillPlan(inp.q, inp.k, inp.v, inp.budget, spec.block, n_bins=16, out_f32=True, queue=True,
+                          queue_group="kv_tiers", scale=scale)
+    o = torch.empty(inp.q.shape, dtype=torch.float32, device=DEV)
+    lse = torch.empty(inp.q.shape[:3], dtype=torch.float32, device=DEV)
+    plan.select(inp.q, inp.k)
+    plan.attend(inp.q, inp.k, inp.v, o, lse)
+    torch.cuda.synchronize()
+    q, k, v = to_host(inp)
+    gidx, gcnt = plan.block_idx.cpu().numpy(), plan.block_cnt.cpu().numpy()
+    oidx, ocnt, sc = O.select_blocks_prefill(q, k, inp.budget, spec.block, kmax=plan.kmax, scale=scale,
+                                             return_scores=True)
+    pinned, exempt = check_prefill_selection(gidx, gcnt, oidx, ocnt, sc, inp.budget)
+    assert pinned >= 0.9 * (pinned + exempt)
+    ro, rl = O.attention_prefill_gather(q, k, v, gidx, gcnt, spec.block, scale=scale)
+    err, lerr = max_abs(o.cpu().numpy(), ro), max_abs(lse.cpu().numpy(), rl)
+    _say("prefill max abs err o", err, "lse", lerr)
+    assert err <= TOL_BF16 and lerr <= TOL_BF16
+    # decode
+    dspec = W.DECODE_128K.with_(batch=2, kv_len=4096 + 24, tok_lo=256, tok_hi=1024, stream_local=8)
+    _say("case: scale", scale, "decode")
+    dinp = W.make_decode(dspec, 84, device=DEV)
+    dplan = SA.DecodePlan(dinp.q, dinp.k, dinp.v, dinp.budget, out_f32=True, scale=scale)
+    do = torch.empty(dinp.q.shape, dtype=torch.float32, device=DEV)
+    dl = torch.empty(dinp.q.shape[:2], dtype=torch.float32, device=DEV)
+    dplan.pool(dinp.k)
+    dplan.select(dinp.q, dinp.k)
+    dplan.attend(dinp.q, dinp.k, dinp.v, do, dl)
+    torch.cuda.synchronize()
+    dq, dk, dv = W.to_numpy(dinp.q), W.to_numpy(dinp.k), W.to_numpy(dinp.v)
+    dgidx, dgcnt = dplan.block_idx.cpu().numpy(), dplan.block_cnt.cpu().numpy()
+    ro, rl = O.decode_attention(dq, dk, dv, dgidx, dgcnt, dinp.budget["granularity"], scale=scale)
+    err, lerr = max_abs(do.cpu().numpy(), ro), max_abs(dl.cpu().numpy(), rl)
+    _say("decode max abs err o", err, "lse", lerr)
+    assert err <= TOL_BF16 and lerr <= TOL_BF16
+
+
 def test_decode_long_cache():
     """A cache longer than the 131072-token workload (200003 tokens): the heads
     at granularity 16 score 12501 pooled keys instead of at most 8192, so the
