@@ -609,6 +609,23 @@ def main():
     }
     dgbps = dbytes["total"] / (res["dstep_ms"] * 1e-3) / 1e9 if "dstep_ms" in res else None
     kv_gbps = dbytes["kv"] / (res["datt_ms"] * 1e-3) / 1e9 if "datt_ms" in res else None
+    if args.only == "decode":
+        # no prefill ran: the line's roofline is the decode step's (HBM-bound),
+        # and there is no prefill time to report as the value
+        pk_hbm = peaks["hbm_read_gbps"] if peaks and "hbm_read_gbps" in peaks else None
+        roofline = {
+            "bound": "hbm",
+            "achieved": dgbps,
+            "peak": M.PEAK_HBM_BYTES / 1e9,
+            "unit": "GB/s",
+            "frac": dgbps / (M.PEAK_HBM_BYTES / 1e9) if dgbps else None,
+            "peak_measured": pk_hbm,
+            "frac_measured": dgbps / pk_hbm if dgbps and pk_hbm else None,
+            "traffic": None,
+            "kernel": "decode step (sa_select_blocks + sa_sparse_attn_decode)",
+            "bytes_per_step": dbytes["total"],
+            "avg_step_ms": res.get("dstep_ms"),
+        }
 
     ablation = {}
     if not args.no_ablation and args.only in ("prefill", "all"):
@@ -693,7 +710,7 @@ def main():
 
     out = {
         "metric": "128K prefill ms/layer + attended TFLOP/s (%MFMA peak); decode KV GB/s (%HBM)",
-        "value": prefill_ms,
+        "value": prefill_ms if args.only in ("prefill", "all") else None,
         "unit": "ms/layer",
         "n_gpus": 1,
         "steps": args.steps,
